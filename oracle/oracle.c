@@ -1,0 +1,244 @@
+/*
+ * oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, obviously correct CPU implementation, in fp64, of what the
+ * fused feed-forward path computes.  Only the test suite, the package smoke
+ * check and the benchmark's CPU-baseline leg may load or call this library.
+ * The product path never does: it shares no code, header, table or helper
+ * with the HIP kernels, and the HIP side never calls into it.
+ *
+ * Sources (cited by page title and section; no code appears on the pages):
+ *  - the kernel-fusion / tensor-parallelism post (brunomaga.github.io),
+ *    section "Megatron-LM tensor parallelism", the equations for H and Y:
+ *    H = act(X W1 + b1), Y = act2(H W2 + b2), X: MxN, W1: NxO, b1: O,
+ *    W2: OxP, b2: P; the second activation is optional.
+ *  - Same page, same section, the tensor-parallel equation: the per-shard
+ *    partial H^(g) W2^(g) carries no b2; b2 (and act2) are applied once after
+ *    the sum over shards.  oracle_ffn() with b2 == NULL computes that partial.
+ *  - "Fine-Grained Compute-Communication Overlap for MoE" review
+ *    (zhongzhuzhou.org), section 2.1 (Mixture-of-Experts, briefly) and 2.2
+ *    (five steps): the router picks the top-k experts per token and the
+ *    output is the gate-weighted sum of those experts' FFN outputs.
+ *
+ * Readings where the pages are silent (each also listed in the design doc):
+ *  - act1 is ReLU or the tanh form of GELU; GELU-tanh is
+ *    0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) (Hendrycks & Gimpel).
+ *  - top-k ties go to the smaller expert index; slot 0 holds the largest logit.
+ *  - gate weights are a softmax over the k selected logits only.
+ *  - per-expert token lists hold entries t*k+s in ascending t.
+ *
+ * Everything is computed in double from the exact input values (bf16 bits are
+ * widened exactly; fp32 is widened exactly).  Nothing is rounded to bf16.
+ * Each sum runs in ascending index order; the bias is added after the sum.
+ *
+ * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -o liboracle.so -lm
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { OR_F32 = 0, OR_BF16 = 1 };
+enum { OR_ACT_NONE = 0, OR_ACT_RELU = 1, OR_ACT_GELU_TANH = 2 };
+
+/* bf16 is the upper half of an IEEE binary32; widening is exact. */
+static double bf16_bits_to_double(uint16_t b) {
+    uint32_t u = ((uint32_t)b) << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+static double load(int dtype, const void* base, int64_t idx) {
+    if (dtype == OR_BF16) return bf16_bits_to_double(((const uint16_t*)base)[idx]);
+    return (double)((const float*)base)[idx];
+}
+
+double oracle_act(int act, double x) {
+    if (act == OR_ACT_RELU) return x > 0.0 ? x : 0.0;
+    if (act == OR_ACT_GELU_TANH) {
+        const double c = sqrt(2.0 / M_PI);
+        return 0.5 * x * (1.0 + tanh(c * (x + 0.044715 * x * x * x)));
+    }
+    return x;
+}
+
+/* One output row of the two-layer FFN, straight from the definition.
+ * h[o] = act1( sum_n X[m,n] W1[n,o]  + b1[o] )
+ * y[p] = act2( sum_o h[o]   W2[o,p]  + b2[p] )
+ * Work arrays h (O) and acc (max(O,P)) are supplied by the caller. */
+static void ffn_row(int dtype, const void* X, const void* W1, const void* b1,
+                    const void* W2, const void* b2, int64_t m, int64_t N,
+                    int64_t O, int64_t P, int act1, int act2,
+                    double* h, double* acc, double* yrow) {
+    /* layer 1: each acc[o] accumulates over n in ascending order */
+    for (int64_t o = 0; o < O; ++o) acc[o] = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        double x = load(dtype, X, m * N + n);
+        for (int64_t o = 0; o < O; ++o) acc[o] += x * load(dtype, W1, n * O + o);
+    }
+    for (int64_t o = 0; o < O; ++o) {
+        double a = acc[o] + (b1 ? load(dtype, b1, o) : 0.0);
+        h[o] = oracle_act(act1, a);
+    }
+    /* layer 2: each acc[p] accumulates over o in ascending order */
+    for (int64_t p = 0; p < P; ++p) acc[p] = 0.0;
+    for (int64_t o = 0; o < O; ++o) {
+        double hv = h[o];
+        for (int64_t p = 0; p < P; ++p) acc[p] += hv * load(dtype, W2, o * P + p);
+    }
+    for (int64_t p = 0; p < P; ++p) {
+        double a = acc[p] + (b2 ? load(dtype, b2, p) : 0.0);
+        yrow[p] = oracle_act(act2, a);
+    }
+}
+
+/* Y[r, :] for r in rows[0..nrows) (all M rows when rows == NULL, nrows = M).
+ * Y is nrows x P doubles.  b1/b2 may be NULL (zero bias): b2 == NULL with
+ * act2 == NONE gives one tensor-parallel shard's partial output.
+ * Returns 0, or -1 on bad arguments. */
+int oracle_ffn(int dtype, const void* X, const void* W1, const void* b1,
+               const void* W2, const void* b2, const int64_t* rows, int64_t nrows,
+               int64_t M, int64_t N, int64_t O, int64_t P, int act1, int act2,
+               double* Y) {
+    if (!X || !W1 || !W2 || !Y || M < 0 || N < 1 || O < 1 || P < 1) return -1;
+    if (dtype != OR_F32 && dtype != OR_BF16) return -1;
+    if (!rows) nrows = M;
+    int bad = 0;
+#pragma omp parallel
+    {
+        int64_t wn = O > P ? O : P;
+        double* h = (double*)malloc(sizeof(double) * (size_t)O);
+        double* acc = (double*)malloc(sizeof(double) * (size_t)wn);
+        if (!h || !acc) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < nrows; ++r) {
+                int64_t m = rows ? rows[r] : r;
+                if (m < 0 || m >= M) {
+#pragma omp atomic write
+                    bad = 1;
+                    continue;
+                }
+                ffn_row(dtype, X, W1, b1, W2, b2, m, N, O, P, act1, act2, h, acc,
+                        Y + r * P);
+            }
+        }
+        free(h);
+        free(acc);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Top-k routing from fp32 gate logits (M x E).
+ * ids[t*k+s]: s-th largest logit's expert (ties -> smaller index).
+ * w[t*k+s]  : softmax over the k selected logits, in fp64.
+ * counts[e], offsets[e] (exclusive prefix sum, offsets[E] = M*k),
+ * sorted[offsets[e] + j]: the j-th entry t*k+s routed to e, ascending t.
+ * Any output pointer may be NULL except ids and w. */
+int oracle_moe_route(const float* logits, int64_t M, int64_t E, int k,
+                     int32_t* ids, double* w, int32_t* counts, int32_t* offsets,
+                     int32_t* sorted) {
+    if (!logits || !ids || !w || M < 0 || E < 1 || k < 1 || k > E) return -1;
+    for (int64_t t = 0; t < M; ++t) {
+        const float* l = logits + t * E;
+        for (int s = 0; s < k; ++s) {
+            int64_t best = -1;
+            for (int64_t e = 0; e < E; ++e) {
+                int taken = 0;
+                for (int q = 0; q < s; ++q) taken |= (ids[t * k + q] == e);
+                if (taken) continue;
+                if (best < 0 || l[e] > l[best]) best = e; /* strict: first max wins */
+            }
+            ids[t * k + s] = (int32_t)best;
+        }
+        double l0 = (double)l[ids[t * k]];
+        double denom = 0.0;
+        for (int s = 0; s < k; ++s) denom += exp((double)l[ids[t * k + s]] - l0);
+        for (int s = 0; s < k; ++s) w[t * k + s] = exp((double)l[ids[t * k + s]] - l0) / denom;
+    }
+    if (counts || offsets || sorted) {
+        int32_t* cnt = (int32_t*)calloc((size_t)E, sizeof(int32_t));
+        if (!cnt) return -1;
+        for (int64_t i = 0; i < M * k; ++i) cnt[ids[i]]++;
+        int32_t run = 0;
+        for (int64_t e = 0; e < E; ++e) {
+            if (counts) counts[e] = cnt[e];
+            if (offsets) offsets[e] = run;
+            if (sorted) {
+                int32_t pos = run;
+                for (int64_t t = 0; t < M; ++t)
+                    for (int s = 0; s < k; ++s)
+                        if (ids[t * k + s] == e) sorted[pos++] = (int32_t)(t * k + s);
+            }
+            run += cnt[e];
+        }
+        if (offsets) offsets[E] = run;
+        free(cnt);
+    }
+    return 0;
+}
+
+/* Mixture-of-Experts layer output for tokens rows[0..nrows) (all when NULL):
+ * Y[r] = sum_s w[t,s] * FFN_{ids[t,s]}(X[t]), each expert with its own
+ * W1_e (NxO), b1_e (O), W2_e (OxP), b2_e (P); experts stacked along the
+ * leading axis.  Y is nrows x P doubles. */
+int oracle_moe_ffn(int dtype, const void* X, const float* logits, int64_t M,
+                   int64_t E, int k, const void* W1, const void* b1,
+                   const void* W2, const void* b2, int64_t N, int64_t O,
+                   int64_t P, int act1, int act2, const int64_t* rows,
+                   int64_t nrows, double* Y) {
+    if (!X || !logits || !W1 || !W2 || !Y || M < 0 || E < 1 || k < 1 || k > E ||
+        N < 1 || O < 1 || P < 1)
+        return -1;
+    if (dtype != OR_F32 && dtype != OR_BF16) return -1;
+    if (!rows) nrows = M;
+    int32_t* ids = (int32_t*)malloc(sizeof(int32_t) * (size_t)(M * k + 1));
+    double* w = (double*)malloc(sizeof(double) * (size_t)(M * k + 1));
+    if (!ids || !w) { free(ids); free(w); return -1; }
+    if (oracle_moe_route(logits, M, E, k, ids, w, NULL, NULL, NULL)) {
+        free(ids); free(w); return -1;
+    }
+    size_t esz = dtype == OR_BF16 ? 2 : 4;
+    int bad = 0;
+#pragma omp parallel
+    {
+        int64_t wn = O > P ? O : P;
+        double* h = (double*)malloc(sizeof(double) * (size_t)O);
+        double* acc = (double*)malloc(sizeof(double) * (size_t)wn);
+        double* z = (double*)malloc(sizeof(double) * (size_t)P);
+        if (!h || !acc || !z) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < nrows; ++r) {
+                int64_t t = rows ? rows[r] : r;
+                if (t < 0 || t >= M) {
+#pragma omp atomic write
+                    bad = 1;
+                    continue;
+                }
+                double* y = Y + r * P;
+                for (int64_t p = 0; p < P; ++p) y[p] = 0.0;
+                for (int s = 0; s < k; ++s) {
+                    int64_t e = ids[t * k + s];
+                    const char* w1 = (const char*)W1 + (size_t)(e * N * O) * esz;
+                    const char* w2 = (const char*)W2 + (size_t)(e * O * P) * esz;
+                    const char* bb1 = b1 ? (const char*)b1 + (size_t)(e * O) * esz : NULL;
+                    const char* bb2 = b2 ? (const char*)b2 + (size_t)(e * P) * esz : NULL;
+                    ffn_row(dtype, X, w1, bb1, w2, bb2, t, N, O, P, act1, act2, h, acc, z);
+                    for (int64_t p = 0; p < P; ++p) y[p] += w[t * k + s] * z[p];
+                }
+            }
+        }
+        free(h);
+        free(acc);
+        free(z);
+    }
+    free(ids);
+    free(w);
+    return bad ? -1 : 0;
+}

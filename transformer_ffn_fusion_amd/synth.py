@@ -1,0 +1,90 @@
+"""Seeded synthetic inputs shared by the tests, the bench and the smoke check.
+
+This module generates inputs only.  It holds none of the feed-forward
+arithmetic: no activation, no bias addition, no FFN product and no routing.
+Both sides of every parity check (the HIP library and the fp64 oracle) receive
+the arrays produced here, bit for bit.
+
+Recipe (the reading is recorded in the design doc):
+* ``numpy.random.default_rng(seed)`` (PCG64), ``standard_normal(dtype=float32)``
+  scaled by the standard deviation, in the order X, W1, b1, W2, b2
+  (MoE: X, Wr, then per expert W1_e, b1_e, W2_e, b2_e);
+* standard deviations: X 1, W1 1/sqrt(N), W2 1/sqrt(O), Wr 1/sqrt(N), biases
+  sqrt(v) with v read as a variance (0.1 for the tiny fp32 case, 0.02 else);
+* bf16 tensors are the fp32 draws rounded once to nearest, ties to even;
+* MoE gate logits are an input of the layer: ``fp32(sum_n X[t,n] Wr[n,e] + off[e])``
+  accumulated in float64 from the bf16 values of X and the fp32 Wr.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+# Per-expert logit offsets that skew the expert load (from the MoE workload spec).
+MOE_SKEW_OFFSETS = (0.8, 0.4, 0.2, 0.0, 0.0, -0.2, -0.4, -0.8)
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round float32 values to bf16 (nearest, ties to even); return uint16 bit patterns."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 exactly."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def _draw(rng, shape, std):
+    return rng.standard_normal(shape, dtype=np.float32) * np.float32(std)
+
+
+def dense_inputs(M, N, O, P, *, dtype="bf16", bias_var=0.02, seed=0, with_bias=True):
+    """X (MxN), W1 (NxO), b1 (O), W2 (OxP), b2 (P).
+
+    ``dtype="bf16"`` returns uint16 bf16 bit patterns, ``"f32"`` float32 arrays."""
+    rng = np.random.default_rng(seed)
+    X = _draw(rng, (M, N), 1.0)
+    W1 = _draw(rng, (N, O), 1.0 / np.sqrt(N))
+    b1 = _draw(rng, (O,), np.sqrt(bias_var))
+    W2 = _draw(rng, (O, P), 1.0 / np.sqrt(O))
+    b2 = _draw(rng, (P,), np.sqrt(bias_var))
+    if not with_bias:
+        b1 = b2 = None
+    out = (X, W1, b1, W2, b2)
+    if dtype == "bf16":
+        out = tuple(None if a is None else f32_to_bf16_bits(a) for a in out)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    return out
+
+
+def moe_inputs(M, E, N, O, P, *, offsets=MOE_SKEW_OFFSETS, bias_var=0.02, seed=0):
+    """bf16 MoE inputs: X (MxN), logits (MxE, fp32), W1 (ExNxO), b1 (ExO), W2 (ExOxP), b2 (ExP)."""
+    rng = np.random.default_rng(seed)
+    X = f32_to_bf16_bits(_draw(rng, (M, N), 1.0))
+    Wr = _draw(rng, (N, E), 1.0 / np.sqrt(N))
+    W1 = np.empty((E, N, O), np.uint16)
+    b1 = np.empty((E, O), np.uint16)
+    W2 = np.empty((E, O, P), np.uint16)
+    b2 = np.empty((E, P), np.uint16)
+    for e in range(E):
+        W1[e] = f32_to_bf16_bits(_draw(rng, (N, O), 1.0 / np.sqrt(N)))
+        b1[e] = f32_to_bf16_bits(_draw(rng, (O,), np.sqrt(bias_var)))
+        W2[e] = f32_to_bf16_bits(_draw(rng, (O, P), 1.0 / np.sqrt(O)))
+        b2[e] = f32_to_bf16_bits(_draw(rng, (P,), np.sqrt(bias_var)))
+    off = np.asarray(offsets[:E] if len(offsets) >= E else list(offsets) + [0.0] * (E - len(offsets)),
+                     dtype=np.float64)
+    logits = (bf16_bits_to_f32(X).astype(np.float64) @ Wr.astype(np.float64) + off).astype(np.float32)
+    return X, logits, W1, b1, W2, b2
+
+
+def check_rows(M, block=64, n_random=249, seed=1):
+    """Rows checked at full size: tile edges, the middle, the tail, plus random rows."""
+    fixed = {0, 1, block - 1, block, M // 2, M - 2, M - 1}
+    fixed = {r for r in fixed if 0 <= r < M}
+    rng = np.random.default_rng(seed)
+    pool = np.setdiff1d(np.arange(M), np.fromiter(fixed, dtype=np.int64))
+    extra = rng.choice(pool, size=min(n_random, pool.size), replace=False) if pool.size else []
+    return np.array(sorted(fixed | set(int(r) for r in extra)), dtype=np.int64)
