@@ -1,0 +1,328 @@
+#!/usr/bin/env python3
+"""Benchmark of the fused FFN on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload prefill|decode|large|moe|tiny] [--all]
+
+A step is one call of the whole path on one batch of synthetic input that is
+already resident in HBM: for the dense workloads the fused FFN kernel and the
+ordered split reduction (or the two skinny layers at M <= 16); for the MoE
+workload routing, the grouped fused FFN and the combine.  W untimed warm-up
+steps, then K timed steps bracketed by a device synchronisation on both sides.
+
+Inputs are rotated over R identical copies (R * bytes >= 512 MB) so that the
+256 MB Infinity Cache cannot serve the weights from one call to the next.
+
+One JSON line goes to stdout:
+  value      whole-path throughput of the headline workload (TFLOP/s at M=4096);
+  roofline   the dominant kernel's algorithmic FLOPs (or bytes) per launch over its
+             average duration, timed live with HIP events recorded on the launch
+             stream around each kernel, against MI355X's published peak;
+  cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload;
+  secondary  the decode shape (M=16: us/call, HBM GB/s) and, with --all, the others.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+METRIC = ("fused FFN TFLOP/s and % bf16 MFMA peak at M=4096; "
+          "µs/call + HBM GB/s at M=16")
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA (AMD published, no sparsity)
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+MALL_DEFEAT_BYTES = 512 << 20
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+class Hip:
+    """The few HIP runtime calls the bench makes itself (events)."""
+
+    def __init__(self):
+        self.h = ctypes.CDLL("libamdhip64.so")
+        self.h.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.h.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.h.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                               ctypes.c_void_p]
+        self.h.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def event(self):
+        e = ctypes.c_void_p()
+        assert self.h.hipEventCreate(ctypes.byref(e)) == 0
+        return e.value
+
+    def record(self, e, stream):
+        assert self.h.hipEventRecord(e, stream) == 0
+
+    def ms(self, a, b):
+        f = ctypes.c_float()
+        assert self.h.hipEventSynchronize(b) == 0
+        assert self.h.hipEventElapsedTime(ctypes.byref(f), a, b) == 0
+        return f.value
+
+    def destroy(self, evs):
+        for e in evs:
+            self.h.hipEventDestroy(e)
+
+
+def to_dev(a, torch):
+    if a is None:
+        return None
+    if a.dtype == np.uint16:
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).cuda()
+    return torch.from_numpy(np.ascontiguousarray(a)).cuda()
+
+
+# ---------------------------------------------------------------- dense
+
+def run_dense(cfg, steps, warmup, hip, torch, ffn, synth, workload):
+    dt = cfg.dtype
+    X, W1, b1, W2, b2 = synth.dense_inputs(cfg.M, cfg.N, cfg.O, cfg.P, dtype=dt,
+                                           bias_var=cfg.bias_var, seed=0)
+    es = workload.esize(dt)
+    set_bytes = workload.dense_bytes(cfg.M, cfg.N, cfg.O, cfg.P, es)
+    R = max(1, min(64, math.ceil(MALL_DEFEAT_BYTES / set_bytes)))
+    tdt = torch.bfloat16 if dt == "bf16" else torch.float32
+    base = [to_dev(a, torch) for a in (X, W1, b1, W2, b2)]
+    sets = [[t.clone() for t in base] + [torch.empty((cfg.M, cfg.P), dtype=tdt, device="cuda")]
+            for _ in range(R)]
+    del base
+    code = ffn.BF16 if dt == "bf16" else ffn.F32
+    ws = ffn.workspace(ffn.ffn_workspace_size(cfg.M, cfg.N, cfg.O, cfg.P, code))
+    L = ffn.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    act1 = ffn.ACTS[cfg.act1]
+    nev = 3
+    evs = [hip.event() for _ in range(nev * steps)]
+    arr_t = ctypes.c_void_p * nev
+
+    def call(i, ev=None):
+        x, w1, c1, w2, c2, y = sets[i % R]
+        p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
+        if ev is None:
+            rc = L.ffn_forward(p(x), p(w1), p(c1), p(w2), p(c2), p(y), cfg.M, cfg.N, cfg.O, cfg.P,
+                               code, act1, 0, p(ws), ws.numel(), stream)
+        else:
+            rc = L.ffn_forward_traced(p(x), p(w1), p(c1), p(w2), p(c2), p(y), cfg.M, cfg.N, cfg.O,
+                                      cfg.P, code, act1, 0, 0, p(ws), ws.numel(), stream, ev, nev)
+        if rc != 0:
+            raise RuntimeError(ffn.ffn_last_error())
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0, t1 = hip.event(), hip.event()
+    ev_arrays = [arr_t(*evs[nev * s: nev * (s + 1)]) for s in range(steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    hip.record(t0, stream)
+    for s in range(steps):
+        call(s, ev_arrays[s])
+    hip.record(t1, stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    total_ms = hip.ms(t0, t1)
+    k1 = [hip.ms(evs[nev * s], evs[nev * s + 1]) for s in range(steps)]
+    k2 = [hip.ms(evs[nev * s + 1], evs[nev * s + 2]) for s in range(steps)]
+    hip.destroy(evs + [t0, t1])
+    flops = workload.dense_flops(cfg.M, cfg.N, cfg.O, cfg.P)
+    nbytes = set_bytes
+    ms = total_ms / steps
+    return dict(ms_per_step=ms, wall_ms_per_step=1e3 * wall / steps, k1_ms=float(np.mean(k1)),
+                k1_std_ms=float(np.std(k1)), k2_ms=float(np.mean(k2)), flops=flops, bytes=nbytes,
+                rotate=R, inputs=(X, W1, b1, W2, b2))
+
+
+def run_moe(cfg, steps, warmup, hip, torch, ffn, synth, workload):
+    X, logits, W1, b1, W2, b2 = synth.moe_inputs(cfg.M, cfg.E, cfg.N, cfg.O, cfg.P, seed=0)
+    set_bytes = workload.moe_bytes(cfg.M, cfg.E, cfg.N, cfg.O, cfg.P)
+    R = max(1, min(8, math.ceil(MALL_DEFEAT_BYTES / set_bytes)))
+    base = [to_dev(a, torch) for a in (X, logits, W1, b1, W2, b2)]
+    sets = [[t.clone() for t in base] +
+            [torch.empty((cfg.M, cfg.P), dtype=torch.bfloat16, device="cuda")] for _ in range(R)]
+    del base
+    ws = ffn.workspace(ffn.moe_workspace_size(cfg.M, cfg.E, cfg.k, cfg.N, cfg.O, cfg.P))
+    L = ffn.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    nev = 4
+    evs = [hip.event() for _ in range(nev * steps)]
+    arr_t = ctypes.c_void_p * nev
+
+    def call(i, ev=None):
+        x, lg, w1, c1, w2, c2, y = sets[i % R]
+        p = lambda t: t.data_ptr()  # noqa: E731
+        if ev is None:
+            rc = L.moe_ffn_forward(p(x), p(lg), cfg.M, cfg.E, cfg.k, p(w1), p(c1), p(w2), p(c2),
+                                   p(y), cfg.N, cfg.O, cfg.P, ffn.BF16, 2, 0, None, None, None,
+                                   None, p(ws), ws.numel(), stream)
+        else:
+            rc = L.moe_ffn_forward_traced(p(x), p(lg), cfg.M, cfg.E, cfg.k, p(w1), p(c1), p(w2),
+                                          p(c2), p(y), cfg.N, cfg.O, cfg.P, ffn.BF16, 2, 0,
+                                          p(ws), ws.numel(), stream, ev, nev)
+        if rc != 0:
+            raise RuntimeError(ffn.ffn_last_error())
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0, t1 = hip.event(), hip.event()
+    ev_arrays = [arr_t(*evs[nev * s: nev * (s + 1)]) for s in range(steps)]
+    hip.record(t0, stream)
+    for s in range(steps):
+        call(s, ev_arrays[s])
+    hip.record(t1, stream)
+    torch.cuda.synchronize()
+    total_ms = hip.ms(t0, t1)
+    ks = [[hip.ms(evs[nev * s + j], evs[nev * s + j + 1]) for s in range(steps)] for j in range(3)]
+    hip.destroy(evs + [t0, t1])
+    flops = workload.moe_flops(cfg.M * cfg.k, cfg.N, cfg.O, cfg.P)
+    return dict(ms_per_step=total_ms / steps, route_ms=float(np.mean(ks[0])),
+                k1_ms=float(np.mean(ks[1])), combine_ms=float(np.mean(ks[2])), flops=flops,
+                bytes=set_bytes, rotate=R)
+
+
+# ---------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(cfg, inputs, rows, synth, workload):
+    import oracle  # the reported CPU baseline is the oracle as it stands
+    X, W1, b1, W2, b2 = inputs
+    sel = np.arange(rows, dtype=np.int64)
+    t0 = time.perf_counter()
+    oracle.ffn(X, W1, b1, W2, b2, act1=oracle.ACT_GELU_TANH, rows=sel)
+    dt = time.perf_counter() - t0
+    flops = workload.dense_flops(rows, cfg.N, cfg.O, cfg.P)
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
+            "kind": "oracle",
+            "sample": f"{rows} of {cfg.M} rows of {cfg.name} (fp64, {dt:.2f} s); "
+                      f"extrapolated full call {dt * cfg.M / rows:.1f} s"}
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "large", "moe", "tiny"])
+    ap.add_argument("--all", action="store_true", help="also time the large and MoE workloads")
+    ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle sample rows (0: skip)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported "
+              f"(the path runs on a single MI355X, no cross-GPU step is built).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import transformer_ffn_fusion_amd as ffn
+    from transformer_ffn_fusion_amd import synth, workload
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    ffn.lib()  # fail loudly when the library is missing
+    hip = Hip()
+    cfgs = {"prefill": workload.PREFILL, "decode": workload.DECODE, "large": workload.LARGE,
+            "tiny": workload.TINY_F32, "moe": workload.MOE}
+    head = cfgs[args.workload]
+    log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {head.name}")
+
+    secondary = {}
+    if args.workload == "moe":
+        r = run_moe(head, args.steps, args.warmup, hip, torch, ffn, synth, workload)
+        value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
+        kern_tflops = r["flops"] / (r["k1_ms"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": "grouped fused FFN", "achieved": kern_tflops,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": kern_tflops / PEAK_BF16_TFLOPS,
+                "traffic": None, "kernel_us": 1e3 * r["k1_ms"]}
+        unit = "TFLOP/s"
+        dense = None
+    else:
+        r = run_dense(head, args.steps, args.warmup, hip, torch, ffn, synth, workload)
+        dense = r
+        if head.M <= 16 and head.dtype == "bf16":
+            value = r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
+            unit = "GB/s"
+            # layer 1 and layer 2 each stream one weight matrix: count each layer's own bytes
+            k1_bytes = 2 * (head.M * head.N + head.N * head.O + head.O + head.M * head.O)
+            ach = k1_bytes / (r["k1_ms"] * 1e-3) / 1e9
+            roof = {"bound": "hbm", "kernel": "skinny layer 1", "achieved": ach, "peak": PEAK_HBM_GBS,
+                    "unit": "GB/s", "frac": ach / PEAK_HBM_GBS, "traffic": None,
+                    "kernel_us": 1e3 * r["k1_ms"]}
+        else:
+            value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
+            unit = "TFLOP/s"
+            ach = r["flops"] / (r["k1_ms"] * 1e-3) / 1e12
+            peak = PEAK_BF16_TFLOPS if head.dtype == "bf16" else 157.3
+            roof = {"bound": "mfma", "kernel": "fused FFN (H in LDS)", "achieved": ach, "peak": peak,
+                    "unit": "TFLOP/s", "frac": ach / peak, "traffic": None,
+                    "kernel_us": 1e3 * r["k1_ms"], "reduce_us": 1e3 * r["k2_ms"]}
+
+    if args.workload == "prefill":
+        d = run_dense(workload.DECODE, max(args.steps, 200), args.warmup, hip, torch, ffn, synth,
+                      workload)
+        secondary[workload.DECODE.name] = {
+            "us_per_call": 1e3 * d["ms_per_step"],
+            "GB_per_s": d["bytes"] / (d["ms_per_step"] * 1e-3) / 1e9,
+            "frac_hbm_peak": d["bytes"] / (d["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "layer1_us": 1e3 * d["k1_ms"], "layer2_us": 1e3 * d["k2_ms"],
+            "kernels_GB_per_s": d["bytes"] / ((d["k1_ms"] + d["k2_ms"]) * 1e-3) / 1e9,
+            "rotate": d["rotate"]}
+    if args.all:
+        for name in ("large", "moe", "tiny"):
+            c = cfgs[name]
+            if c is head:
+                continue
+            if name == "moe":
+                m = run_moe(c, args.steps, args.warmup, hip, torch, ffn, synth, workload)
+                secondary[c.name] = {"TFLOP_per_s": m["flops"] / (m["ms_per_step"] * 1e-3) / 1e12,
+                                     "us_per_call": 1e3 * m["ms_per_step"],
+                                     "route_us": 1e3 * m["route_ms"],
+                                     "grouped_us": 1e3 * m["k1_ms"],
+                                     "combine_us": 1e3 * m["combine_ms"]}
+            else:
+                m = run_dense(c, args.steps, args.warmup, hip, torch, ffn, synth, workload)
+                secondary[c.name] = {"TFLOP_per_s": m["flops"] / (m["ms_per_step"] * 1e-3) / 1e12,
+                                     "us_per_call": 1e3 * m["ms_per_step"],
+                                     "kernel1_us": 1e3 * m["k1_ms"], "kernel2_us": 1e3 * m["k2_ms"]}
+
+    cpu = None
+    if dense is not None and args.cpu_rows > 0 and head.dtype == "bf16":
+        rows = min(args.cpu_rows, head.M)
+        log(f"[bench] CPU oracle baseline on {rows} rows ...")
+        cpu = cpu_baseline(head, dense["inputs"], rows, synth, workload)
+
+    out = {
+        "metric": METRIC,
+        "value": value,
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": head.dtype,
+        "data": "synthetic (seeded normal inputs, random-init weights of the workload's shape)",
+        "config": {"workload": head.name, **{k: getattr(head, k) for k in ("M", "N", "O", "P")},
+                   "act1": head.act1, "rotate_input_sets": r["rotate"]},
+        "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS if unit == "TFLOP/s" else None,
+        "roofline": roof,
+        "cpu_baseline": cpu,
+        "secondary": secondary,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

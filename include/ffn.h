@@ -1,0 +1,160 @@
+/*
+ * ffn.h -- C ABI of libffn.so: the fused two-layer feed-forward network on one
+ * AMD Instinct MI355X (gfx950), and its grouped Mixture-of-Experts form.
+ *
+ * Operation (the kernel-fusion / tensor-parallelism post, brunomaga.github.io,
+ * section "Megatron-LM tensor parallelism", equations for H and Y):
+ *
+ *     H = act1(X W1 + b1)          X: M x N, W1: N x O, b1: O
+ *     Y = act2(H W2 + b2)          W2: O x P, b2: P, Y: M x P
+ *
+ * computed for one GPU's tensor-parallel shard: O is the shard's share of the
+ * hidden width.  H never goes to global memory on the bf16 path with M > 16:
+ * it is produced tile by tile into LDS and consumed there by the second
+ * product (same page, section "Step 1: fusing the two linear layers").  For a
+ * shard's partial output in a tensor-parallel layer pass b2 = NULL and
+ * act2 = NONE on every shard but one (the bias is added once, after the sum).
+ *
+ * Conventions for every entry point:
+ *  - Memory.  All array arguments are DEVICE pointers on the current HIP
+ *    device, row-major and contiguous, and must be 16-byte aligned; the
+ *    workspace must be 256-byte aligned.  The caller allocates and owns every
+ *    buffer, the workspace included; the library never allocates, frees or
+ *    keeps a pointer after the call returns.
+ *  - Workspace.  Query the size with the matching *_workspace_size call and
+ *    zero-fill the workspace ONCE after allocating it.  Every call leaves its
+ *    counters at zero again, so no per-call clearing is needed.  Calls that
+ *    share a workspace must be ordered (same stream).
+ *  - Asynchrony.  Calls only enqueue work on `stream` (a hipStream_t; NULL is
+ *    the default stream) and return without synchronising.
+ *  - Errors.  Every argument check runs on the host before anything is
+ *    enqueued.  A failed check returns a negative FFN_E* code, sets the text
+ *    returned by ffn_last_error() (per host thread) and leaves every output
+ *    untouched.  A failed launch returns FFN_ELAUNCH.
+ *  - Shapes.  M >= 1 (M == 0 is a no-op); N, O, P >= 8 and multiples of 8.
+ *    Any M works (partial row tiles are handled).
+ *  - Numerics.  bf16 storage, fp32 accumulation; H is rounded to bf16 once,
+ *    Y once (round to nearest even).  No floating-point atomics: repeated
+ *    calls with the same inputs give bitwise-identical outputs.
+ *  - Aliasing.  Outputs must not overlap any input or the workspace.
+ */
+#ifndef FFN_MI355X_H
+#define FFN_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum { FFN_F32 = 0, FFN_BF16 = 1 } ffn_dtype_t;
+
+/* act1 / act2.  GELU_TANH is 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))). */
+typedef enum { FFN_ACT_NONE = 0, FFN_ACT_RELU = 1, FFN_ACT_GELU_TANH = 2 } ffn_act_t;
+
+/* Kernel family.  AUTO picks SKINNY for bf16 with M <= 16, FUSED for other
+ * bf16 shapes and F32 for fp32 data; the others force a family (tests). */
+typedef enum {
+    FFN_VARIANT_AUTO = 0,
+    FFN_VARIANT_FUSED = 1,   /* bf16, H in LDS, split-O partials + ordered reduce */
+    FFN_VARIANT_SKINNY = 2,  /* bf16, M <= 16: two weight-streaming layers        */
+    FFN_VARIANT_F32 = 3      /* fp32 data, fp32 arithmetic                       */
+} ffn_variant_t;
+
+enum {
+    FFN_OK = 0,
+    FFN_EINVAL = -1,       /* null pointer, size out of range, unknown enum      */
+    FFN_EWORKSPACE = -2,   /* workspace smaller than *_workspace_size()          */
+    FFN_EUNSUPPORTED = -3, /* shape or combination the kernels do not implement  */
+    FFN_EALIGN = -4,       /* pointer not 16-byte (workspace: 256-byte) aligned  */
+    FFN_ELAUNCH = -5       /* the HIP runtime refused a launch                   */
+};
+
+/* Workspace bytes ffn_forward needs for this shape (0 if the shape is invalid). */
+size_t ffn_workspace_size(int64_t M, int64_t N, int64_t O, int64_t P, int dtype);
+size_t ffn_workspace_size_ex(int64_t M, int64_t N, int64_t O, int64_t P, int dtype, int variant);
+
+/* Y = act2(act1(X W1 + b1) W2 + b2).
+ *   X  : M x N  (dtype)          W1 : N x O (dtype)     b1 : O (dtype) or NULL
+ *   W2 : O x P  (dtype)          b2 : P (dtype) or NULL Y  : M x P (dtype), written
+ *   dtype: ffn_dtype_t; act1, act2: ffn_act_t.
+ * Returns FFN_OK or a negative FFN_E* code (see the conventions above). */
+int ffn_forward(const void* X, const void* W1, const void* b1, const void* W2, const void* b2,
+                void* Y, int64_t M, int64_t N, int64_t O, int64_t P, int dtype, int act1,
+                int act2, void* workspace, size_t workspace_bytes, void* stream);
+
+/* As ffn_forward, with the kernel family forced (FFN_VARIANT_*). */
+int ffn_forward_ex(const void* X, const void* W1, const void* b1, const void* W2,
+                   const void* b2, void* Y, int64_t M, int64_t N, int64_t O, int64_t P,
+                   int dtype, int act1, int act2, int variant, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* As ffn_forward_ex, and records caller-created HIP events (hipEvent_t cast
+ * to void*) on `stream` around the path's kernels, for per-kernel timing:
+ * events[0] before the first kernel, events[1] between the first (the fused
+ * FFN, the fp32 FFN or skinny layer 1) and the second (the split reduction or
+ * skinny layer 2), events[2] after the second.  n_events >= 3. */
+int ffn_forward_traced(const void* X, const void* W1, const void* b1, const void* W2,
+                       const void* b2, void* Y, int64_t M, int64_t N, int64_t O, int64_t P,
+                       int dtype, int act1, int act2, int variant, void* workspace,
+                       size_t workspace_bytes, void* stream, void** events, int n_events);
+
+/* ---------------------------------------------------------------- MoE
+ * Grouped form over the per-expert token lists of a top-k Mixture-of-Experts
+ * layer (the MoE tile-signalling review, zhongzhuzhou.org, sections 2.1-2.2:
+ * route, expert computation, gate-weighted sum).  bf16 only; 1 <= E <= 256,
+ * 1 <= k <= min(E, 8).
+ *
+ * Routing (from the fp32 gate logits, M x E): per token the k largest logits
+ * (ties: smaller expert index first; slot 0 = largest), gate weights =
+ * softmax over those k logits (fp32).  Entry t*k+s is token t's s-th choice;
+ * each expert's list holds its entries in ascending token order, lists
+ * concatenated by expert index. */
+size_t moe_workspace_size(int64_t M, int64_t E, int k, int64_t N, int64_t O, int64_t P,
+                          int dtype);
+
+/* Routing alone.  Outputs (device, caller-owned; each may be NULL):
+ *   topk_ids M x k int32, topk_w M x k float, expert_offsets E+1 int32
+ *   (exclusive prefix of the per-expert counts; [E] = M*k),
+ *   sorted_entries M*k int32 (the concatenated per-expert lists).
+ * workspace: at least moe_workspace_size(M, E, k, 8, 8, 8, FFN_BF16) bytes. */
+int moe_route(const float* logits, int64_t M, int64_t E, int k, int32_t* topk_ids,
+              float* topk_w, int32_t* expert_offsets, int32_t* sorted_entries,
+              void* workspace, size_t workspace_bytes, void* stream);
+
+/* Y[t] = sum_s w[t,s] * act2( act1(X[t] W1_e + b1_e) W2_e + b2_e ), e = topk_ids[t,s].
+ *   X: M x N bf16; logits: M x E fp32; W1: E x N x O; b1: E x O or NULL;
+ *   W2: E x O x P; b2: E x P or NULL; Y: M x P bf16.
+ *   The routing outputs are optional copies, as in moe_route. */
+int moe_ffn_forward(const void* X, const float* logits, int64_t M, int64_t E, int k,
+                    const void* W1, const void* b1, const void* W2, const void* b2, void* Y,
+                    int64_t N, int64_t O, int64_t P, int dtype, int act1, int act2,
+                    int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                    int32_t* sorted_entries, void* workspace, size_t workspace_bytes,
+                    void* stream);
+
+/* As moe_ffn_forward without the routing copies, recording events[0..3]
+ * around the routing, grouped-FFN and combine kernels.  n_events >= 4. */
+int moe_ffn_forward_traced(const void* X, const float* logits, int64_t M, int64_t E, int k,
+                           const void* W1, const void* b1, const void* W2, const void* b2,
+                           void* Y, int64_t N, int64_t O, int64_t P, int dtype, int act1,
+                           int act2, void* workspace, size_t workspace_bytes, void* stream,
+                           void** events, int n_events);
+
+/* Text describing the last non-zero return on this host thread ("" if none). */
+const char* ffn_last_error(void);
+
+/* Library version (major * 10000 + minor * 100 + patch). */
+int ffn_version(void);
+
+/* Host-only self-check of the LDS operand swizzle: 0 when every fragment read
+ * and every transposing tile write is a bijection onto distinct bank slots.
+ * Makes no HIP call. */
+int ffn_selftest_layout(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FFN_MI355X_H */

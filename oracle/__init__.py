@@ -66,6 +66,8 @@ def _bind(lib):
     lib.oracle_moe_ffn.argtypes = [i32, vp, vp, i64, i64, i32, vp, vp, vp, vp, i64, i64, i64,
                                    i32, i32, vp, i64, dp]
     lib.oracle_moe_ffn.restype = ctypes.c_int
+    lib.oracle_threads.argtypes = []
+    lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_act.argtypes = [i32, ctypes.c_double]
     lib.oracle_act.restype = ctypes.c_double
     return lib
@@ -88,6 +90,11 @@ def _as_input(a, dtype_code):
 
 def _dtype_of(X):
     return BF16 if np.asarray(X).dtype == np.uint16 else F32
+
+
+def threads(lib=None) -> int:
+    """OpenMP threads the oracle's row loops use."""
+    return (lib or load()).oracle_threads()
 
 
 def act(kind: int, x: float, lib=None) -> float:

@@ -34,12 +34,16 @@
  * Build: gcc -O2 -fopenmp -shared -fPIC oracle.c -o liboracle.so -lm
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
 
 enum { OR_F32 = 0, OR_BF16 = 1 };
 enum { OR_ACT_NONE = 0, OR_ACT_RELU = 1, OR_ACT_GELU_TANH = 2 };
+
+/* Threads the OpenMP loops below use (reported with the CPU baseline). */
+int oracle_threads(void) { return omp_get_max_threads(); }
 
 /* bf16 is the upper half of an IEEE binary32; widening is exact. */
 static double bf16_bits_to_double(uint16_t b) {

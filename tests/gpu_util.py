@@ -1,0 +1,42 @@
+"""Helpers for the GPU parity tests: moving the seeded inputs to the device and
+comparing the library's outputs with the fp64 oracle."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+
+BF16_TOL = 2e-2   # max |Y - Yref| <= BF16_TOL * rms(Yref): bf16 data, fp32 accumulation
+F32_TOL = 1e-5    # same rule for fp32 data
+
+
+def log(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bf16(bits):
+    import torch
+    a = np.ascontiguousarray(bits, dtype=np.uint16)
+    return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).cuda()
+
+
+def dev_f32(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+def host_f64(t):
+    return t.float().cpu().numpy().astype(np.float64)
+
+
+def compare(y_gpu, y_ref, tol, what=""):
+    """Max-abs error against tol * rms of the reference; returns (max_err, rms)."""
+    assert y_gpu.shape == y_ref.shape, (y_gpu.shape, y_ref.shape)
+    assert np.all(np.isfinite(y_gpu)), f"{what}: non-finite output"
+    rms = float(np.sqrt(np.mean(y_ref ** 2)))
+    err = float(np.max(np.abs(y_gpu - y_ref))) if y_ref.size else 0.0
+    log(f"  {what}: max|err| = {err:.3e}, rms(ref) = {rms:.3e}, ratio = {err / max(rms, 1e-30):.3e}"
+        f" (tol {tol:.0e})")
+    assert err <= tol * rms, f"{what}: max|err| {err:.4e} > {tol} * rms {rms:.4e}"
+    return err, rms

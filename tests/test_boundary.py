@@ -1,0 +1,128 @@
+"""The C-ABI boundary on the CPU: the library loads, exports every symbol the
+header declares, and rejects bad arguments on the host before any HIP call
+(so these run without a GPU: no call here reaches a kernel launch)."""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+
+import pytest
+
+import transformer_ffn_fusion_amd as ffn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ffn.h")
+
+E_INVAL, E_WS, E_UNSUP, E_ALIGN = -1, -2, -3, -4
+FAKE = 0x10000      # 256-byte aligned, never dereferenced: every call below fails a check first
+FAKE2 = 0x20000
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\**\s*([a-z_0-9]+)\s*\(", text,
+                                 flags=re.M)))
+
+
+def test_library_loads_and_exports_every_declared_symbol():
+    L = ffn.lib()
+    names = declared_functions()
+    assert {"ffn_forward", "ffn_forward_ex", "ffn_workspace_size", "moe_ffn_forward",
+            "moe_route", "moe_workspace_size", "ffn_last_error"} <= set(names)
+    for n in names:
+        assert hasattr(L, n), f"libffn.so does not export {n}"
+    assert L.ffn_version() >= 100
+
+
+def test_layout_selfcheck():
+    assert ffn.lib().ffn_selftest_layout() == 0
+
+
+def _fwd(X=FAKE, W1=FAKE, b1=None, W2=FAKE, b2=None, Y=FAKE2, M=64, N=64, O=448, P=64,
+         dtype=ffn.BF16, act1=2, act2=0, variant=0, ws=FAKE, wsb=None):
+    if wsb is None:
+        wsb = 0  # too small unless a test says otherwise
+    return ffn.lib().ffn_forward_ex(X, W1, b1, W2, b2, Y, M, N, O, P, dtype, act1, act2, variant,
+                                    ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=None), E_INVAL),
+    (dict(W1=None), E_INVAL),
+    (dict(Y=None), E_INVAL),
+    (dict(ws=None), E_INVAL),
+    (dict(M=-1), E_INVAL),
+    (dict(N=0), E_INVAL),
+    (dict(O=12), E_UNSUP),
+    (dict(P=100), E_UNSUP),
+    (dict(dtype=7), E_INVAL),
+    (dict(act1=5), E_INVAL),
+    (dict(act2=-1), E_INVAL),
+    (dict(variant=9), E_INVAL),
+    (dict(X=FAKE + 8), E_ALIGN),
+    (dict(b1=FAKE + 4), E_ALIGN),
+    (dict(ws=FAKE + 16), E_ALIGN),
+    (dict(variant=ffn.VARIANT_SKINNY, M=17), E_UNSUP),
+    (dict(variant=ffn.VARIANT_F32), E_UNSUP),
+    (dict(dtype=ffn.F32, variant=ffn.VARIANT_FUSED), E_UNSUP),
+    (dict(), E_WS),
+])
+def test_forward_rejects(kw, code):
+    rc = _fwd(**kw)
+    assert rc == code, (rc, ffn.ffn_last_error())
+    assert ffn.ffn_last_error() != ""
+
+
+def test_workspace_one_byte_short_is_rejected():
+    need = ffn.ffn_workspace_size(4096, 4096, 1792, 4096)
+    assert need >= 4 * 4096 * 4096 * 4          # four fp32 split partials of Y
+    assert _fwd(M=4096, N=4096, O=1792, P=4096, wsb=need - 1) == E_WS
+    skinny = ffn.ffn_workspace_size(16, 4096, 1792, 4096)
+    assert 0 < skinny < need
+    assert _fwd(M=16, N=4096, O=1792, P=4096, wsb=skinny - 1) == E_WS
+
+
+def test_workspace_size_invalid_shapes():
+    assert ffn.ffn_workspace_size(4, 4, 448, 64) == 0
+    assert ffn.ffn_workspace_size(4, 64, 448, 64, dtype=5) == 0
+    assert ffn.moe_workspace_size(64, 300, 2, 64, 448, 64) == 0
+    assert ffn.moe_workspace_size(64, 8, 9, 64, 448, 64) == 0
+    assert ffn.moe_workspace_size(64, 2, 3, 64, 448, 64) == 0
+
+
+def _moe(**kw):
+    a = dict(X=FAKE, logits=FAKE, M=64, E=8, k=2, W1=FAKE, b1=None, W2=FAKE, b2=None, Y=FAKE2,
+             N=64, O=448, P=64, dtype=ffn.BF16, act1=2, act2=0, ws=FAKE, wsb=0)
+    a.update(kw)
+    return ffn.lib().moe_ffn_forward(a["X"], a["logits"], a["M"], a["E"], a["k"], a["W1"], a["b1"],
+                                     a["W2"], a["b2"], a["Y"], a["N"], a["O"], a["P"], a["dtype"],
+                                     a["act1"], a["act2"], None, None, None, None, a["ws"],
+                                     a["wsb"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(E=0), E_UNSUP),
+    (dict(E=257), E_UNSUP),
+    (dict(k=0), E_UNSUP),
+    (dict(k=3, E=2), E_UNSUP),
+    (dict(k=9, E=16), E_UNSUP),
+    (dict(logits=None), E_INVAL),
+    (dict(logits=FAKE + 2), E_ALIGN),
+    (dict(dtype=ffn.F32), E_UNSUP),
+    (dict(O=20), E_UNSUP),
+    (dict(act1=3), E_INVAL),
+    (dict(W2=FAKE + 4), E_ALIGN),
+    (dict(), E_WS),
+])
+def test_moe_rejects(kw, code):
+    rc = _moe(**kw)
+    assert rc == code, (rc, ffn.ffn_last_error())
+
+
+def test_route_rejects():
+    L = ffn.lib()
+    assert L.moe_route(None, 8, 8, 2, None, None, None, None, FAKE, 1 << 20, None) == E_INVAL
+    assert L.moe_route(FAKE, 8, 8, 2, None, None, None, None, FAKE, 0, None) == E_WS
+    assert L.moe_route(FAKE, 8, 8, 2, None, None, None, None, FAKE + 8, 1 << 20, None) == E_ALIGN

@@ -1,0 +1,174 @@
+"""Fused two-layer FFN (and its grouped MoE form) on AMD Instinct MI355X.
+
+Thin Python binding over ``libffn.so`` (C ABI in ``include/ffn.h``).  The
+functions here only marshal torch tensors into pointers, sizes and the
+current HIP stream; every step of the computation runs in the library's HIP
+kernels.  There is no CPU or PyTorch fallback: if the library is missing, or a
+call fails, an exception is raised.
+
+Names mirror the C entry points: ``ffn_forward``, ``ffn_forward_ex``,
+``ffn_workspace_size``, ``moe_route``, ``moe_ffn_forward``,
+``moe_workspace_size``, ``ffn_last_error``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "F32", "BF16", "ACT_NONE", "ACT_RELU", "ACT_GELU_TANH",
+    "VARIANT_AUTO", "VARIANT_FUSED", "VARIANT_SKINNY", "VARIANT_F32",
+    "FFNError", "lib", "lib_path", "ffn_workspace_size", "ffn_forward", "ffn_forward_ex",
+    "moe_workspace_size", "moe_route", "moe_ffn_forward", "ffn_last_error", "workspace",
+]
+
+F32, BF16 = 0, 1
+ACT_NONE, ACT_RELU, ACT_GELU_TANH = 0, 1, 2
+VARIANT_AUTO, VARIANT_FUSED, VARIANT_SKINNY, VARIANT_F32 = 0, 1, 2, 3
+ACTS = {"none": ACT_NONE, "relu": ACT_RELU, "gelu_tanh": ACT_GELU_TANH}
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+lib_path = os.path.join(_PKG, "libffn.so")
+_lib = None
+
+
+class FFNError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"libffn error {code}: {msg}")
+        self.code = code
+
+
+def lib():
+    """The loaded libffn.so (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(lib_path):
+            raise FFNError(-100, f"{lib_path} is missing; run `python -m transformer_ffn_fusion_amd.build`")
+        L = ctypes.CDLL(lib_path)
+        vp, i64, i32, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+        L.ffn_workspace_size.argtypes = [i64, i64, i64, i64, i32]
+        L.ffn_workspace_size.restype = sz
+        L.ffn_workspace_size_ex.argtypes = [i64, i64, i64, i64, i32, i32]
+        L.ffn_workspace_size_ex.restype = sz
+        L.ffn_forward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp, sz, vp]
+        L.ffn_forward.restype = i32
+        L.ffn_forward_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, i32,
+                                     vp, sz, vp]
+        L.ffn_forward_ex.restype = i32
+        L.moe_workspace_size.argtypes = [i64, i64, i32, i64, i64, i64, i32]
+        L.moe_workspace_size.restype = sz
+        L.moe_route.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_route.restype = i32
+        L.moe_ffn_forward.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, i64, i64, i64, i32,
+                                      i32, i32, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_ffn_forward.restype = i32
+        evp = ctypes.POINTER(ctypes.c_void_p)
+        L.ffn_forward_traced.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32,
+                                         i32, vp, sz, vp, evp, i32]
+        L.ffn_forward_traced.restype = i32
+        L.moe_ffn_forward_traced.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, i64, i64,
+                                             i64, i32, i32, i32, vp, sz, vp, evp, i32]
+        L.moe_ffn_forward_traced.restype = i32
+        L.ffn_last_error.argtypes = []
+        L.ffn_last_error.restype = ctypes.c_char_p
+        L.ffn_version.restype = i32
+        L.ffn_selftest_layout.restype = i32
+        _lib = L
+    return _lib
+
+
+def ffn_last_error() -> str:
+    return lib().ffn_last_error().decode()
+
+
+def _check(rc: int):
+    if rc != 0:
+        raise FFNError(rc, ffn_last_error())
+
+
+def _ptr(t):
+    return None if t is None else t.data_ptr()
+
+
+def _stream(stream):
+    if stream is not None:
+        return stream
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _act(a):
+    return ACTS[a] if isinstance(a, str) else int(a)
+
+
+def ffn_workspace_size(M, N, O, P, dtype=BF16, variant=VARIANT_AUTO) -> int:
+    return lib().ffn_workspace_size_ex(M, N, O, P, dtype, variant)
+
+
+def moe_workspace_size(M, E, k, N, O, P, dtype=BF16) -> int:
+    return lib().moe_workspace_size(M, E, k, N, O, P, dtype)
+
+
+def workspace(nbytes: int, device="cuda"):
+    """A zero-filled device workspace of ``nbytes`` (torch allocations are 256-byte aligned)."""
+    import torch
+    return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+def ffn_forward_ex(X, W1, b1, W2, b2, Y, act1="gelu_tanh", act2="none", variant=VARIANT_AUTO,
+                   ws=None, stream=None):
+    """``Y = act2(act1(X W1 + b1) W2 + b2)`` on the GPU; ``Y`` is written in place.
+
+    ``ws`` is a zero-initialised uint8 device tensor of at least
+    ``ffn_workspace_size(...)`` bytes (allocated here when None)."""
+    M, N = X.shape
+    O = W1.shape[1]
+    P = W2.shape[1]
+    dt = _dtype_code(X)
+    if ws is None:
+        ws = workspace(ffn_workspace_size(M, N, O, P, dt, variant), X.device)
+    _check(lib().ffn_forward_ex(_ptr(X), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), _ptr(Y),
+                                M, N, O, P, dt, _act(act1), _act(act2), int(variant),
+                                _ptr(ws), ws.numel(), _stream(stream)))
+    return Y
+
+
+def ffn_forward(X, W1, b1, W2, b2, Y, act1="gelu_tanh", act2="none", ws=None, stream=None):
+    return ffn_forward_ex(X, W1, b1, W2, b2, Y, act1, act2, VARIANT_AUTO, ws, stream)
+
+
+def moe_route(logits, k, topk_ids=None, topk_w=None, expert_offsets=None, sorted_entries=None,
+              ws=None, stream=None):
+    """Top-k routing on the GPU; fills whichever output tensors are given."""
+    M, E = logits.shape
+    if ws is None:
+        ws = workspace(moe_workspace_size(M, E, k, 8, 8, 8), logits.device)
+    _check(lib().moe_route(_ptr(logits), M, E, k, _ptr(topk_ids), _ptr(topk_w),
+                           _ptr(expert_offsets), _ptr(sorted_entries), _ptr(ws), ws.numel(),
+                           _stream(stream)))
+
+
+def moe_ffn_forward(X, logits, k, W1, b1, W2, b2, Y, act1="gelu_tanh", act2="none",
+                    topk_ids=None, topk_w=None, expert_offsets=None, sorted_entries=None,
+                    ws=None, stream=None):
+    """Grouped FFN over the top-k experts of each token; ``Y`` written in place."""
+    M, N = X.shape
+    E, _, O = W1.shape
+    P = W2.shape[2]
+    dt = _dtype_code(X)
+    if ws is None:
+        ws = workspace(moe_workspace_size(M, E, k, N, O, P, dt), X.device)
+    _check(lib().moe_ffn_forward(_ptr(X), _ptr(logits), M, E, k, _ptr(W1), _ptr(b1), _ptr(W2),
+                                 _ptr(b2), _ptr(Y), N, O, P, dt, _act(act1), _act(act2),
+                                 _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets),
+                                 _ptr(sorted_entries), _ptr(ws), ws.numel(), _stream(stream)))
+    return Y

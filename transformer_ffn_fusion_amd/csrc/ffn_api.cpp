@@ -1,0 +1,476 @@
+// ffn_api.cpp -- the C ABI of libffn.so (declared in include/ffn.h): argument
+// checks, workspace carving and dispatch to the gfx950 kernels.
+//
+// Every check that can fail runs on the host before the first launch, so a
+// rejected call leaves all outputs untouched.  The library keeps no state
+// between calls other than the error text of the calling host thread.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+
+#include "ffn.h"
+#include "ffn_device.h"
+#include "ffn_internal.h"
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+int fail(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+
+int ok() {
+    g_err[0] = '\0';
+    return FFN_OK;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_act(int a) { return a == FFN_ACT_NONE || a == FFN_ACT_RELU || a == FFN_ACT_GELU_TANH; }
+
+int check_dims(int64_t M, int64_t N, int64_t O, int64_t P) {
+    if (M < 0) return fail(FFN_EINVAL, "M must be >= 0 (got %lld)", (long long)M);
+    if (N < 1 || O < 1 || P < 1)
+        return fail(FFN_EINVAL, "N, O, P must be >= 1 (got %lld, %lld, %lld)", (long long)N,
+                    (long long)O, (long long)P);
+    if (N % 8 || O % 8 || P % 8)
+        return fail(FFN_EUNSUPPORTED, "N, O, P must be multiples of 8 (got %lld, %lld, %lld)",
+                    (long long)N, (long long)O, (long long)P);
+    const int64_t lim = (int64_t)1 << 31;
+    if (M >= lim || N >= lim || O >= lim || P >= lim)
+        return fail(FFN_EUNSUPPORTED, "dimensions must be below 2^31");
+    return FFN_OK;
+}
+
+int resolve_variant(int variant, int dtype, int64_t M) {
+    if (variant == FFN_VARIANT_AUTO) {
+        if (dtype == FFN_F32) return FFN_VARIANT_F32;
+        return M <= ffn::kSkinnyMaxM ? FFN_VARIANT_SKINNY : FFN_VARIANT_FUSED;
+    }
+    return variant;
+}
+
+// ---- dense workspace layouts (byte offsets, each region 256-byte aligned)
+struct DenseLayout {
+    size_t part = 0;       // fused / f32: fp32 partials
+    size_t counters = 0;   // skinny: int32 counters (layer 1 then layer 2)
+    size_t part1 = 0, h = 0, part2 = 0;
+    size_t total = 0;
+};
+
+DenseLayout dense_layout(int64_t M, int64_t N, int64_t O, int64_t P, int variant) {
+    DenseLayout L;
+    if (variant == FFN_VARIANT_FUSED) {
+        const int chunk = ffn::fused_pick_chunk(O);
+        const int S = ffn::fused_num_splits(O, chunk);
+        L.part = 0;
+        L.total = align_up((size_t)S * M * P * sizeof(float));
+    } else if (variant == FFN_VARIANT_F32) {
+        const int64_t S = (O + ffn::kF32Chunk - 1) / ffn::kF32Chunk;
+        L.total = align_up((size_t)S * M * P * sizeof(float));
+    } else {  // skinny
+        size_t off = 0;
+        L.counters = off;
+        off += align_up(sizeof(int32_t) * (ffn::skinny_counters(O) + ffn::skinny_counters(P)));
+        L.part1 = off;
+        off += align_up(sizeof(float) * ffn::skinny_partial_floats(N, O));
+        L.h = off;
+        off += align_up(sizeof(uint16_t) * ffn::kSkinnyMaxM * O);
+        L.part2 = off;
+        off += align_up(sizeof(float) * ffn::skinny_partial_floats(O, P));
+        L.total = off;
+    }
+    if (L.total == 0) L.total = kAlign;
+    return L;
+}
+
+// ---- MoE workspace layout
+struct MoeLayout {
+    size_t ids, w, counts, offsets, sorted, pos, tiles, tile_count, part, total;
+    int splits, chunk;
+    int64_t max_tiles;
+};
+
+MoeLayout moe_layout(int64_t M, int64_t E, int k, int64_t O, int64_t P) {
+    MoeLayout L{};
+    const int64_t mk = M * k;
+    L.chunk = ffn::fused_pick_chunk(O);
+    L.splits = ffn::fused_num_splits(O, L.chunk);
+    L.max_tiles = ffn::moe_max_tiles(M, E, k);
+    size_t off = 0;
+    L.ids = off;        off += align_up(sizeof(int32_t) * mk);
+    L.w = off;          off += align_up(sizeof(float) * mk);
+    L.counts = off;     off += align_up(sizeof(int32_t) * E);
+    L.offsets = off;    off += align_up(sizeof(int32_t) * (E + 1));
+    L.sorted = off;     off += align_up(sizeof(int32_t) * mk);
+    L.pos = off;        off += align_up(sizeof(int32_t) * mk);
+    L.tiles = off;      off += align_up(sizeof(int32_t) * 3 * (L.max_tiles + 1));
+    L.tile_count = off; off += kAlign;
+    L.part = off;       off += align_up(sizeof(float) * (size_t)L.splits * mk * P);
+    L.total = off;
+    return L;
+}
+
+int check_common_ptrs(const void* X, const void* W1, const void* b1, const void* W2,
+                      const void* b2, const void* Y, void* ws) {
+    if (!X || !W1 || !W2 || !Y) return fail(FFN_EINVAL, "X, W1, W2 and Y must not be NULL");
+    if (!ws) return fail(FFN_EINVAL, "workspace must not be NULL");
+    const void* ps[] = {X, W1, b1, W2, b2, Y};
+    const char* nm[] = {"X", "W1", "b1", "W2", "b2", "Y"};
+    for (int i = 0; i < 6; ++i)
+        if (ps[i] && !aligned16(ps[i])) return fail(FFN_EALIGN, "%s is not 16-byte aligned", nm[i]);
+    if ((reinterpret_cast<uintptr_t>(ws) & (kAlign - 1)) != 0)
+        return fail(FFN_EALIGN, "workspace is not 256-byte aligned");
+    return FFN_OK;
+}
+
+int launched(hipError_t e, const char* what) {
+    if (e != hipSuccess) return fail(FFN_ELAUNCH, "%s: %s", what, hipGetErrorString(e));
+    return FFN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ffn_version(void) { return 100; }
+
+const char* ffn_last_error(void) { return g_err; }
+
+size_t ffn_workspace_size_ex(int64_t M, int64_t N, int64_t O, int64_t P, int dtype,
+                             int variant) {
+    if (check_dims(M, N, O, P) != FFN_OK) return 0;
+    if (dtype != FFN_F32 && dtype != FFN_BF16) return 0;
+    const int v = resolve_variant(variant, dtype, M);
+    if (v < FFN_VARIANT_FUSED || v > FFN_VARIANT_F32) return 0;
+    return dense_layout(M, N, O, P, v).total;
+}
+
+size_t ffn_workspace_size(int64_t M, int64_t N, int64_t O, int64_t P, int dtype) {
+    return ffn_workspace_size_ex(M, N, O, P, dtype, FFN_VARIANT_AUTO);
+}
+
+static int mark(void** events, int n_events, int i, hipStream_t st) {
+    if (!events || i >= n_events) return FFN_OK;
+    hipError_t e = hipEventRecord(reinterpret_cast<hipEvent_t>(events[i]), st);
+    if (e != hipSuccess) return fail(FFN_ELAUNCH, "event record: %s", hipGetErrorString(e));
+    return FFN_OK;
+}
+
+static int dense_forward(const void* X, const void* W1, const void* b1, const void* W2,
+                         const void* b2, void* Y, int64_t M, int64_t N, int64_t O, int64_t P,
+                         int dtype, int act1, int act2, int variant, void* workspace,
+                         size_t workspace_bytes, void* stream, void** events, int n_events) {
+    if (events && n_events < 3) return fail(FFN_EINVAL, "traced calls take at least 3 events");
+    int rc = check_dims(M, N, O, P);
+    if (rc) return rc;
+    if (dtype != FFN_F32 && dtype != FFN_BF16) return fail(FFN_EINVAL, "unknown dtype %d", dtype);
+    if (!valid_act(act1) || !valid_act(act2))
+        return fail(FFN_EINVAL, "unknown activation (act1=%d, act2=%d)", act1, act2);
+    if (variant < FFN_VARIANT_AUTO || variant > FFN_VARIANT_F32)
+        return fail(FFN_EINVAL, "unknown variant %d", variant);
+    rc = check_common_ptrs(X, W1, b1, W2, b2, Y, workspace);
+    if (rc) return rc;
+    const int v = resolve_variant(variant, dtype, M);
+    if ((v == FFN_VARIANT_F32) != (dtype == FFN_F32))
+        return fail(FFN_EUNSUPPORTED, "variant %d does not take dtype %d", v, dtype);
+    if (v == FFN_VARIANT_SKINNY && M > ffn::kSkinnyMaxM)
+        return fail(FFN_EUNSUPPORTED, "the skinny variant takes M <= %d (got %lld)",
+                    ffn::kSkinnyMaxM, (long long)M);
+    const DenseLayout L = dense_layout(M, N, O, P, v);
+    if (workspace_bytes < L.total)
+        return fail(FFN_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+    if (M == 0) return ok();
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    if ((rc = mark(events, n_events, 0, st))) return rc;
+    if (v == FFN_VARIANT_FUSED) {
+        const int chunk = ffn::fused_pick_chunk(O);
+        const int S = ffn::fused_num_splits(O, chunk);
+        float* part = reinterpret_cast<float*>(ws + L.part);
+        const int64_t rbs = (M + ffn::kBM - 1) / ffn::kBM;
+        rc = launched(ffn::launch_fused_bf16((const uint16_t*)X, (const uint16_t*)W1,
+                                             (const uint16_t*)b1, (const uint16_t*)W2, part, M,
+                                             N, O, P, act1, chunk, rbs, M, nullptr, st),
+                      "fused FFN kernel");
+        if (rc) return rc;
+        if ((rc = mark(events, n_events, 1, st))) return rc;
+        rc = launched(ffn::launch_reduce_splits(part, S, b2, 0, Y, 0, M, P, act2, st),
+                      "split reduction kernel");
+        if (rc) return rc;
+    } else if (v == FFN_VARIANT_F32) {
+        const int S = (int)((O + ffn::kF32Chunk - 1) / ffn::kF32Chunk);
+        float* part = reinterpret_cast<float*>(ws + L.part);
+        rc = launched(ffn::launch_fused_f32((const float*)X, (const float*)W1, (const float*)b1,
+                                            (const float*)W2, part, M, N, O, P, act1, st),
+                      "fp32 FFN kernel");
+        if (rc) return rc;
+        if ((rc = mark(events, n_events, 1, st))) return rc;
+        rc = launched(ffn::launch_reduce_splits(part, S, b2, 1, Y, 1, M, P, act2, st),
+                      "split reduction kernel");
+        if (rc) return rc;
+    } else {
+        int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.counters);
+        uint16_t* H = reinterpret_cast<uint16_t*>(ws + L.h);
+        rc = launched(ffn::launch_skinny_bf16((const uint16_t*)X, (const uint16_t*)W1,
+                                              (const uint16_t*)b1, H,
+                                              reinterpret_cast<float*>(ws + L.part1), cnt, M, N,
+                                              O, act1, st),
+                      "skinny layer-1 kernel");
+        if (rc) return rc;
+        if ((rc = mark(events, n_events, 1, st))) return rc;
+        rc = launched(ffn::launch_skinny_bf16(H, (const uint16_t*)W2, (const uint16_t*)b2,
+                                              (uint16_t*)Y,
+                                              reinterpret_cast<float*>(ws + L.part2),
+                                              cnt + ffn::skinny_counters(O), M, O, P, act2, st),
+                      "skinny layer-2 kernel");
+        if (rc) return rc;
+    }
+    if ((rc = mark(events, n_events, 2, st))) return rc;
+    return ok();
+}
+
+int ffn_forward_ex(const void* X, const void* W1, const void* b1, const void* W2,
+                   const void* b2, void* Y, int64_t M, int64_t N, int64_t O, int64_t P,
+                   int dtype, int act1, int act2, int variant, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+    return dense_forward(X, W1, b1, W2, b2, Y, M, N, O, P, dtype, act1, act2, variant, workspace,
+                         workspace_bytes, stream, nullptr, 0);
+}
+
+int ffn_forward_traced(const void* X, const void* W1, const void* b1, const void* W2,
+                       const void* b2, void* Y, int64_t M, int64_t N, int64_t O, int64_t P,
+                       int dtype, int act1, int act2, int variant, void* workspace,
+                       size_t workspace_bytes, void* stream, void** events, int n_events) {
+    if (!events) return fail(FFN_EINVAL, "events must not be NULL");
+    return dense_forward(X, W1, b1, W2, b2, Y, M, N, O, P, dtype, act1, act2, variant, workspace,
+                         workspace_bytes, stream, events, n_events);
+}
+
+int ffn_forward(const void* X, const void* W1, const void* b1, const void* W2, const void* b2,
+                void* Y, int64_t M, int64_t N, int64_t O, int64_t P, int dtype, int act1,
+                int act2, void* workspace, size_t workspace_bytes, void* stream) {
+    return ffn_forward_ex(X, W1, b1, W2, b2, Y, M, N, O, P, dtype, act1, act2,
+                          FFN_VARIANT_AUTO, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- MoE
+
+static int check_moe_dims(int64_t M, int64_t E, int k) {
+    if (M < 0) return fail(FFN_EINVAL, "M must be >= 0");
+    if (E < 1 || E > 256) return fail(FFN_EUNSUPPORTED, "E must be in [1, 256] (got %lld)", (long long)E);
+    if (k < 1 || k > 8 || k > E)
+        return fail(FFN_EUNSUPPORTED, "k must be in [1, min(E, 8)] (got %d)", k);
+    if (M * k >= ((int64_t)1 << 31)) return fail(FFN_EUNSUPPORTED, "M*k must be below 2^31");
+    return FFN_OK;
+}
+
+size_t moe_workspace_size(int64_t M, int64_t E, int k, int64_t N, int64_t O, int64_t P,
+                          int dtype) {
+    if (dtype != FFN_BF16) return 0;
+    if (check_moe_dims(M, E, k) != FFN_OK) return 0;
+    if (check_dims(M, N, O, P) != FFN_OK) return 0;
+    return moe_layout(M, E, k, O, P).total;
+}
+
+static int route_into(const float* logits, int64_t M, int64_t E, int k, const MoeLayout& L,
+                      char* ws, int32_t** ids, float** w, hipStream_t st) {
+    *ids = reinterpret_cast<int32_t*>(ws + L.ids);
+    *w = reinterpret_cast<float*>(ws + L.w);
+    return launched(ffn::launch_moe_route(logits, M, E, k, *ids, *w,
+                                          reinterpret_cast<int32_t*>(ws + L.counts),
+                                          reinterpret_cast<int32_t*>(ws + L.offsets),
+                                          reinterpret_cast<int32_t*>(ws + L.sorted),
+                                          reinterpret_cast<int32_t*>(ws + L.pos),
+                                          reinterpret_cast<int32_t*>(ws + L.tiles),
+                                          reinterpret_cast<int32_t*>(ws + L.tile_count), st),
+                    "routing kernel");
+}
+
+static int copy_route_outputs(int64_t M, int64_t E, int k, const MoeLayout& L, const char* ws,
+                              int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                              int32_t* sorted_entries, hipStream_t st) {
+    struct Cp { void* dst; size_t off, bytes; } cps[] = {
+        {topk_ids, L.ids, sizeof(int32_t) * M * k},
+        {topk_w, L.w, sizeof(float) * M * k},
+        {expert_offsets, L.offsets, sizeof(int32_t) * (E + 1)},
+        {sorted_entries, L.sorted, sizeof(int32_t) * M * k},
+    };
+    for (const Cp& c : cps) {
+        if (!c.dst || c.bytes == 0) continue;
+        hipError_t e = hipMemcpyAsync(c.dst, ws + c.off, c.bytes, hipMemcpyDeviceToDevice, st);
+        if (e != hipSuccess) return fail(FFN_ELAUNCH, "routing output copy: %s", hipGetErrorString(e));
+    }
+    return FFN_OK;
+}
+
+int moe_route(const float* logits, int64_t M, int64_t E, int k, int32_t* topk_ids,
+              float* topk_w, int32_t* expert_offsets, int32_t* sorted_entries,
+              void* workspace, size_t workspace_bytes, void* stream) {
+    int rc = check_moe_dims(M, E, k);
+    if (rc) return rc;
+    if (!logits || !workspace) return fail(FFN_EINVAL, "logits and workspace must not be NULL");
+    if (reinterpret_cast<uintptr_t>(logits) & 3u) return fail(FFN_EALIGN, "logits not 4-byte aligned");
+    if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))
+        return fail(FFN_EALIGN, "workspace is not 256-byte aligned");
+    const MoeLayout L = moe_layout(M, E, k, 8, 8);
+    if (workspace_bytes < L.part) return fail(FFN_EWORKSPACE, "workspace has %zu bytes, needs %zu",
+                                              workspace_bytes, L.part);
+    if (M == 0) return ok();
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    int32_t* ids;
+    float* w;
+    rc = route_into(logits, M, E, k, L, ws, &ids, &w, st);
+    if (rc) return rc;
+    rc = copy_route_outputs(M, E, k, L, ws, topk_ids, topk_w, expert_offsets, sorted_entries, st);
+    if (rc) return rc;
+    return ok();
+}
+
+static int moe_forward(const void* X, const float* logits, int64_t M, int64_t E, int k,
+                       const void* W1, const void* b1, const void* W2, const void* b2, void* Y,
+                       int64_t N, int64_t O, int64_t P, int dtype, int act1, int act2,
+                       int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                       int32_t* sorted_entries, void* workspace, size_t workspace_bytes,
+                       void* stream, void** events, int n_events) {
+    if (events && n_events < 4) return fail(FFN_EINVAL, "traced MoE calls take at least 4 events");
+    int rc = check_moe_dims(M, E, k);
+    if (rc) return rc;
+    rc = check_dims(M, N, O, P);
+    if (rc) return rc;
+    if (dtype != FFN_BF16) return fail(FFN_EUNSUPPORTED, "the grouped form takes bf16 only");
+    if (!valid_act(act1) || !valid_act(act2))
+        return fail(FFN_EINVAL, "unknown activation (act1=%d, act2=%d)", act1, act2);
+    if (!logits) return fail(FFN_EINVAL, "logits must not be NULL");
+    if (reinterpret_cast<uintptr_t>(logits) & 3u) return fail(FFN_EALIGN, "logits not 4-byte aligned");
+    rc = check_common_ptrs(X, W1, b1, W2, b2, Y, workspace);
+    if (rc) return rc;
+    const MoeLayout L = moe_layout(M, E, k, O, P);
+    if (workspace_bytes < L.total)
+        return fail(FFN_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+    if (M == 0) return ok();
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    int32_t* ids;
+    float* w;
+    if ((rc = mark(events, n_events, 0, st))) return rc;
+    rc = route_into(logits, M, E, k, L, ws, &ids, &w, st);
+    if (rc) return rc;
+    if ((rc = mark(events, n_events, 1, st))) return rc;
+
+    ffn::GroupedRows g;
+    g.tiles = reinterpret_cast<const int32_t*>(ws + L.tiles);
+    g.tile_count = reinterpret_cast<const int32_t*>(ws + L.tile_count);
+    g.sorted = reinterpret_cast<const int32_t*>(ws + L.sorted);
+    g.k = k;
+    g.w1_stride = N * O;
+    g.w2_stride = O * P;
+    g.b1_stride = O;
+    const int64_t row_blocks = (L.max_tiles + 7) / 8 * 8;
+    float* part = reinterpret_cast<float*>(ws + L.part);
+    rc = launched(ffn::launch_fused_bf16((const uint16_t*)X, (const uint16_t*)W1,
+                                         (const uint16_t*)b1, (const uint16_t*)W2, part, M, N, O,
+                                         P, act1, L.chunk, row_blocks, M * k, &g, st),
+                  "grouped FFN kernel");
+    if (rc) return rc;
+    if ((rc = mark(events, n_events, 2, st))) return rc;
+    rc = launched(ffn::launch_moe_combine(part, L.splits, M * k,
+                                          reinterpret_cast<const int32_t*>(ws + L.pos), ids, w,
+                                          (const uint16_t*)b2, (uint16_t*)Y, M, k, P, act2, st),
+                  "combine kernel");
+    if (rc) return rc;
+    if ((rc = mark(events, n_events, 3, st))) return rc;
+    rc = copy_route_outputs(M, E, k, L, ws, topk_ids, topk_w, expert_offsets, sorted_entries, st);
+    if (rc) return rc;
+    return ok();
+}
+
+int moe_ffn_forward(const void* X, const float* logits, int64_t M, int64_t E, int k,
+                    const void* W1, const void* b1, const void* W2, const void* b2, void* Y,
+                    int64_t N, int64_t O, int64_t P, int dtype, int act1, int act2,
+                    int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
+                    int32_t* sorted_entries, void* workspace, size_t workspace_bytes,
+                    void* stream) {
+    return moe_forward(X, logits, M, E, k, W1, b1, W2, b2, Y, N, O, P, dtype, act1, act2,
+                       topk_ids, topk_w, expert_offsets, sorted_entries, workspace,
+                       workspace_bytes, stream, nullptr, 0);
+}
+
+int moe_ffn_forward_traced(const void* X, const float* logits, int64_t M, int64_t E, int k,
+                           const void* W1, const void* b1, const void* W2, const void* b2,
+                           void* Y, int64_t N, int64_t O, int64_t P, int dtype, int act1,
+                           int act2, void* workspace, size_t workspace_bytes, void* stream,
+                           void** events, int n_events) {
+    if (!events) return fail(FFN_EINVAL, "events must not be NULL");
+    return moe_forward(X, logits, M, E, k, W1, b1, W2, b2, Y, N, O, P, dtype, act1, act2,
+                       nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream,
+                       events, n_events);
+}
+
+// ---------------------------------------------------------------- self-check
+
+int ffn_selftest_layout(void) {
+    // Fragment reads: for each 16-index fragment and k-group, the 16 lanes hit
+    // 16 distinct 16-byte slots of one 256-byte line (and 8 distinct slots in
+    // each half-wave group of 8 lanes, for 32-bank hardware).
+    for (uint32_t f = 0; f < 64; ++f) {
+        for (uint32_t g = 0; g < 4; ++g) {
+            uint32_t seen16 = 0, line = ~0u;
+            for (uint32_t i = 0; i < 16; ++i) {
+                uint32_t off = ffn::frag_off(16 * f + i, g);
+                if (line == ~0u) line = off >> 8;
+                if ((off >> 8) != line) return 1;
+                seen16 |= 1u << ((off >> 4) & 15);
+            }
+            if (seen16 != 0xffffu) return 2;
+            for (uint32_t h = 0; h < 2; ++h) {
+                uint32_t seen8 = 0;
+                for (uint32_t i = 0; i < 8; ++i)
+                    seen8 |= 1u << ((ffn::frag_off(16 * f + 8 * h + i, g) >> 4) & 7);
+                if (seen8 != 0xffu) return 3;
+            }
+        }
+    }
+    // Transposing writes: thread t owns k-group t%4 and 8-column group t/4 and
+    // writes column 8*(t/4)+j in step j.  Each 16-thread (and 8-thread) group
+    // must hit distinct slots.
+    for (uint32_t j = 0; j < 8; ++j) {
+        for (uint32_t t0 = 0; t0 < 256; t0 += 16) {
+            uint32_t seen16 = 0;
+            for (uint32_t t = t0; t < t0 + 16; ++t)
+                seen16 |= 1u << ((ffn::frag_off(8 * (t / 4) + j, t % 4) >> 4) & 15);
+            if (seen16 != 0xffffu) return 4;
+        }
+        for (uint32_t t0 = 0; t0 < 256; t0 += 8) {
+            uint32_t seen8 = 0;
+            for (uint32_t t = t0; t < t0 + 8; ++t)
+                seen8 |= 1u << ((ffn::frag_off(8 * (t / 4) + j, t % 4) >> 4) & 7);
+            if (seen8 != 0xffu) return 5;
+        }
+    }
+    // The offsets of one tile are a bijection onto [0, 64 * idx_count).
+    static unsigned char hit[64 * 512];
+    std::memset(hit, 0, sizeof hit);
+    for (uint32_t idx = 0; idx < 512; ++idx)
+        for (uint32_t g = 0; g < 4; ++g) {
+            uint32_t off = ffn::frag_off(idx, g);
+            if (off % 16 || off / 16 >= 4 * 512 || hit[off / 16]) return 6;
+            hit[off / 16] = 1;
+        }
+    return 0;
+}
+
+}  // extern "C"

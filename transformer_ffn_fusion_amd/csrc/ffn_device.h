@@ -1,0 +1,112 @@
+// ffn_device.h -- device-side building blocks shared by the gfx950 kernels.
+//
+// Fragment conventions for the CDNA4 bf16 matrix instruction
+// v_mfma_f32_16x16x32_bf16 (wave64):
+//   operand fragment: lane l supplies 8 bf16 values of row/column (l % 16) for
+//     the k-values 8*(l/16) + 0..7 of a 32-deep k-step (A and B use the same
+//     lane <-> (index, k) convention, so the dot product is over matching k);
+//   result: lane l holds D[4*(l/16) + r][l % 16] for r = 0..3.
+//
+// LDS operand tiles are stored "fragment-major": for every group of 16
+// indices (rows of A, columns of B) and every 8-wide k-group g there is one
+// 256-byte line holding the 16 indices' 16-byte k-chunks.  Inside the line the
+// chunk slot is XOR-swizzled so that
+//   * the MFMA fragment read (16 lanes = 16 consecutive indices, fixed g) and
+//   * the transposing writes of weight tiles (lanes spread over k-groups and
+//     8-column groups, fixed column offset within the group)
+// each touch 16 distinct 16-byte slots of the line: no bank conflicts with
+// either 32 or 64 four-byte banks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ffn {
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+enum Act { ACT_NONE = 0, ACT_RELU = 1, ACT_GELU_TANH = 2 };
+
+// ---------------------------------------------------------------- numerics
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+    return __uint_as_float(bits16 << 16);
+}
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Two floats -> packed bf16 pair (round to nearest even, hardware convert).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    __bf16 a = (__bf16)lo;
+    __bf16 b = (__bf16)hi;
+    return (uint32_t)__builtin_bit_cast(uint16_t, a) |
+           ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// GELU, tanh form: 0.5 x (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3),
+// evaluated as x * sigmoid(2u) = x / (1 + exp(-2u)), which is the same
+// function (0.5 (1 + tanh u) = 1 / (1 + e^{-2u})) and saturates cleanly:
+// exp(-2u) -> inf gives -0, exp(-2u) -> 0 gives x.  The reciprocal is the
+// hardware approximation (about 1 ulp), far below the bf16 rounding of H.
+__device__ __forceinline__ float gelu_tanh(float x) {
+    const float k2 = -2.0f * 0.7978845608028654f;  // -2 sqrt(2/pi)
+    float u = x * (1.0f + 0.044715f * x * x);
+    float e = __expf(k2 * u);
+    return x * __builtin_amdgcn_rcpf(1.0f + e);
+}
+
+__device__ __forceinline__ float apply_act(int act, float x) {
+    if (act == ACT_RELU) return x > 0.0f ? x : 0.0f;
+    if (act == ACT_GELU_TANH) return gelu_tanh(x);
+    return x;
+}
+
+// ---------------------------------------------------------------- MFMA
+
+__device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b, floatx4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a),
+                                                   __builtin_bit_cast(bf16x8_t, b), c, 0, 0, 0);
+}
+
+// ---------------------------------------------------------------- LDS layout
+
+// Byte offset of the 16-byte k-chunk (index idx, k-group g) inside a
+// fragment-major operand tile (see the file comment).
+__host__ __device__ __forceinline__ uint32_t frag_off(uint32_t idx, uint32_t g) {
+    uint32_t flip = ((idx >> 3) ^ (idx >> 4)) & 1u;
+    uint32_t unit = (idx & 15u) ^ (g | (flip << 2));
+    return (((idx >> 4) * 4u + g) << 8) + (unit << 4);
+}
+
+// ---------------------------------------------------------------- 8x8 transpose
+
+// rows[i] holds 8 bf16 of row i (dword d = elements 2d, 2d+1).  On return
+// cols[j] holds the 8 row-values of column j (dword q = rows 2q, 2q+1).
+// v_perm_b32 picks bytes from {S0:S1}; selector 0x05040100 yields
+// S1.lo16 | S0.lo16 << 16 and 0x07060302 yields S1.hi16 | S0.hi16 << 16.
+__device__ __forceinline__ void transpose8x8(const uint4 (&rows)[8], uint4 (&cols)[8]) {
+    const uint32_t LO = 0x05040100u;
+    const uint32_t HI = 0x07060302u;
+    uint32_t c[8][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint4 a = rows[2 * q];
+        const uint4 b = rows[2 * q + 1];
+        c[0][q] = __builtin_amdgcn_perm(b.x, a.x, LO);
+        c[1][q] = __builtin_amdgcn_perm(b.x, a.x, HI);
+        c[2][q] = __builtin_amdgcn_perm(b.y, a.y, LO);
+        c[3][q] = __builtin_amdgcn_perm(b.y, a.y, HI);
+        c[4][q] = __builtin_amdgcn_perm(b.z, a.z, LO);
+        c[5][q] = __builtin_amdgcn_perm(b.z, a.z, HI);
+        c[6][q] = __builtin_amdgcn_perm(b.w, a.w, LO);
+        c[7][q] = __builtin_amdgcn_perm(b.w, a.w, HI);
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) cols[j] = make_uint4(c[j][0], c[j][1], c[j][2], c[j][3]);
+}
+
+__device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+__device__ __forceinline__ uint4 zero16() { return make_uint4(0u, 0u, 0u, 0u); }
+
+}  // namespace ffn

@@ -1,0 +1,72 @@
+// ffn_internal.h -- host-side launch interfaces between the C-ABI layer and
+// the kernel translation units.  Not installed; the public interface is
+// include/ffn.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ffn {
+
+// ---- fused bf16 FFN with H kept in LDS (prefill shapes and the MoE groups)
+
+constexpr int kBM = 64;     // token rows per workgroup tile
+constexpr int kBN2 = 512;   // output columns per second-layer pass
+
+// Hidden-chunk widths the fused kernel is instantiated for.
+int fused_pick_chunk(int64_t O);                 // 448 or 512
+int fused_num_splits(int64_t O, int chunk);      // ceil(O / chunk)
+
+struct GroupedRows {
+    const int32_t* tiles = nullptr;       // [max_tiles][3]: expert, first row, valid rows
+    const int32_t* tile_count = nullptr;  // number of valid tiles (device)
+    const int32_t* sorted = nullptr;      // sorted entries t*k+s; token = entry / k
+    int k = 1;
+    int64_t w1_stride = 0, w2_stride = 0, b1_stride = 0;  // per expert, in elements
+};
+
+// Writes fp32 partial outputs part[s][row][p] (s < splits) for rows < rows_out.
+hipError_t launch_fused_bf16(const uint16_t* X, const uint16_t* W1, const uint16_t* b1,
+                             const uint16_t* W2, float* part, int64_t M, int64_t N,
+                             int64_t O, int64_t P, int act1, int chunk, int64_t row_blocks,
+                             int64_t rows_out, const GroupedRows* grouped, hipStream_t stream);
+
+// Y[m][p] = act2(sum_s part[s][m][p] + b2[p]) in ascending s; bf16 or fp32 out.
+hipError_t launch_reduce_splits(const float* part, int splits, const void* b2, int b2_f32,
+                                void* Y, int y_f32, int64_t M, int64_t P, int act2,
+                                hipStream_t stream);
+
+// ---- skinny (M <= 16) bf16 layer with a fixed-order split-K reduction
+
+constexpr int kSkinnyCols = 128;   // output columns per workgroup
+constexpr int kSkinnyMaxM = 16;
+int64_t skinny_kblock(int64_t K, int64_t Ncol);                 // rows of K per workgroup
+size_t skinny_partial_floats(int64_t K, int64_t Ncol);          // workspace floats
+int64_t skinny_counters(int64_t Ncol);                          // workspace counters
+
+// out[m][c] = act(sum_k A[m][k] W[k][c] + bias[c]) as bf16, m < M <= 16.
+hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* W, const uint16_t* bias,
+                              uint16_t* out, float* part, int32_t* counters, int64_t M,
+                              int64_t K, int64_t Ncol, int act, hipStream_t stream);
+
+// ---- fp32 path
+
+constexpr int kF32Chunk = 512;
+hipError_t launch_fused_f32(const float* X, const float* W1, const float* b1, const float* W2,
+                            float* part, int64_t M, int64_t N, int64_t O, int64_t P, int act1,
+                            hipStream_t stream);
+
+// ---- Mixture-of-Experts
+
+int64_t moe_max_tiles(int64_t M, int64_t E, int k);
+hipError_t launch_moe_route(const float* logits, int64_t M, int64_t E, int k, int32_t* ids,
+                            float* w, int32_t* counts, int32_t* offsets, int32_t* sorted,
+                            int32_t* pos, int32_t* tiles, int32_t* tile_count,
+                            hipStream_t stream);
+hipError_t launch_moe_combine(const float* part, int splits, int64_t rows_total,
+                              const int32_t* pos, const int32_t* ids, const float* w,
+                              const uint16_t* b2, uint16_t* Y, int64_t M, int k, int64_t P,
+                              int act2, hipStream_t stream);
+
+}  // namespace ffn

@@ -1,0 +1,183 @@
+// ffn_skinny.hip -- one FFN layer for decode-sized batches (M <= 16 rows).
+//
+// out[m][c] = act( sum_k A[m][k] W[k][c] + bias[c] ), bf16 in and out, fp32
+// accumulation.  Called twice per FFN: layer 1 (A = X, W = W1, bias = b1,
+// act = act1 -> H) and layer 2 (A = H, W = W2, bias = b2, act = act2 -> Y),
+// following the two equations of the kernel-fusion / tensor-parallelism post
+// (brunomaga.github.io), section "Megatron-LM tensor parallelism".
+//
+// At M = 16 the layer is a weight stream: every byte of W is used for 16 rows
+// only, so the time is the HBM time of W.  The design is built for that:
+//  * one workgroup owns 128 output columns x a block of K rows of W; every
+//    lane issues all of its 16-byte weight loads before any math, so the whole
+//    weight matrix is in flight at once across the grid;
+//  * the 16 rows map exactly onto the 16-row side of v_mfma_f32_16x16x32_bf16;
+//    the weight block is transposed in registers (8x8 per lane) straight into
+//    the MFMA operand layout -- no LDS round trip for the weights;
+//  * the K blocks are reduced in a fixed order: each workgroup writes its
+//    fp32 partial, and the last workgroup to finish a column block (one
+//    integer counter per block) sums all partials in ascending K-block order,
+//    adds the bias once, applies the activation and rounds once to bf16.  The
+//    last arriver resets its counter, so the workspace needs zeroing only once.
+#include "ffn_device.h"
+#include "ffn_internal.h"
+
+namespace ffn {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+struct SkinnyArgs {
+    const uint16_t* A;
+    const uint16_t* W;
+    const uint16_t* bias;
+    uint16_t* out;
+    float* part;        // [nkb][16][Ncol]
+    int32_t* counters;  // [ncb]
+    int64_t M, K, Ncol;
+    int64_t kblock;
+    int nkb;
+    int act;
+};
+
+template <int KSTEPS>
+__global__ __launch_bounds__(kThreads) void skinny_bf16_kernel(SkinnyArgs a) {
+    __shared__ __attribute__((aligned(16))) float red[4][kSkinnyMaxM][kSkinnyCols];
+    __shared__ int s_last;
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int g = lane >> 4;
+    const int c = lane & 15;
+    const int64_t cb = blockIdx.x;
+    const int kb = blockIdx.y;
+    const int64_t K = a.K, Ncol = a.Ncol;
+    const int64_t col = cb * kSkinnyCols + 8 * c;
+    const bool colok = col < Ncol;
+    const int64_t kw = (int64_t)kb * a.kblock + (int64_t)wave * 32 * KSTEPS;
+
+    // ---- issue every load of this lane first
+    uint4 af[KSTEPS];
+    uint4 wr[KSTEPS][8];
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+        const int64_t k0 = kw + 32 * t + 8 * g;
+        af[t] = (c < a.M && k0 < K) ? ld16(a.A + c * K + k0) : zero16();
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int64_t n = k0 + i;
+            wr[t][i] = (colok && n < K) ? ld16(a.W + n * Ncol + col) : zero16();
+        }
+    }
+
+    floatx4_t acc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) acc[j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < KSTEPS; ++t) {
+        uint4 cv[8];
+        transpose8x8(wr[t], cv);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[j] = mfma16x16x32(af[t], cv[j], acc[j]);
+    }
+
+    // acc[j][r] = partial out[m = 4g + r][col + j]; sum the four waves in order
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        float* dst = &red[wave][4 * g + r][8 * c];
+        *reinterpret_cast<float4*>(dst) = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+        *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4][r], acc[5][r], acc[6][r], acc[7][r]);
+    }
+    __syncthreads();
+    const int m = tid >> 4;           // 16 rows x 16 threads, 8 columns each
+    const int cl = (tid & 15) * 8;
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+        v[i] = ((red[0][m][cl + i] + red[1][m][cl + i]) + red[2][m][cl + i]) + red[3][m][cl + i];
+    const int64_t gc = cb * kSkinnyCols + cl;
+    const bool outok = (m < a.M) && (gc < Ncol);
+
+    if (a.nkb > 1) {
+        float* mine = a.part + ((int64_t)kb * kSkinnyMaxM + m) * Ncol + gc;
+        if (gc < Ncol) {
+            *reinterpret_cast<float4*>(mine) = make_float4(v[0], v[1], v[2], v[3]);
+            *reinterpret_cast<float4*>(mine + 4) = make_float4(v[4], v[5], v[6], v[7]);
+        }
+        __threadfence();  // release this block's partial
+        __syncthreads();
+        if (tid == 0) s_last = (atomicAdd(&a.counters[cb], 1) == a.nkb - 1);
+        __syncthreads();
+        if (!s_last) return;
+        __threadfence();  // acquire the other blocks' partials
+        if (gc < Ncol) {
+            const float* src = a.part + (int64_t)m * Ncol + gc;
+            float4 lo = *reinterpret_cast<const float4*>(src);
+            float4 hi = *reinterpret_cast<const float4*>(src + 4);
+            v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
+            v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
+            for (int q = 1; q < a.nkb; ++q) {
+                const float* s2 = src + (int64_t)q * kSkinnyMaxM * Ncol;
+                lo = *reinterpret_cast<const float4*>(s2);
+                hi = *reinterpret_cast<const float4*>(s2 + 4);
+                v[0] += lo.x; v[1] += lo.y; v[2] += lo.z; v[3] += lo.w;
+                v[4] += hi.x; v[5] += hi.y; v[6] += hi.z; v[7] += hi.w;
+            }
+        }
+        if (tid == 0) a.counters[cb] = 0;  // ready for the next call
+    }
+    if (!outok) return;
+    if (a.bias) {
+        uint4 bb = ld16(a.bias + gc);
+        uint32_t bw[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            v[2 * i] += bf16_lo(bw[i]);
+            v[2 * i + 1] += bf16_hi(bw[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = apply_act(a.act, v[i]);
+    uint4 o = make_uint4(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]), pack_bf16x2(v[4], v[5]),
+                         pack_bf16x2(v[6], v[7]));
+    *reinterpret_cast<uint4*>(a.out + (int64_t)m * Ncol + gc) = o;
+}
+
+constexpr int kKSteps = 2;   // 32-deep MFMA steps per wave
+constexpr int64_t kKBlock = 4 * 32 * kKSteps;
+
+}  // namespace
+
+int64_t skinny_kblock(int64_t, int64_t) { return kKBlock; }
+
+size_t skinny_partial_floats(int64_t K, int64_t Ncol) {
+    int64_t nkb = (K + kKBlock - 1) / kKBlock;
+    return nkb > 1 ? (size_t)(nkb * kSkinnyMaxM * Ncol) : 0;
+}
+
+int64_t skinny_counters(int64_t Ncol) { return (Ncol + kSkinnyCols - 1) / kSkinnyCols; }
+
+hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* W, const uint16_t* bias,
+                              uint16_t* out, float* part, int32_t* counters, int64_t M,
+                              int64_t K, int64_t Ncol, int act, hipStream_t stream) {
+    SkinnyArgs a;
+    a.A = A;
+    a.W = W;
+    a.bias = bias;
+    a.out = out;
+    a.part = part;
+    a.counters = counters;
+    a.M = M;
+    a.K = K;
+    a.Ncol = Ncol;
+    a.kblock = kKBlock;
+    a.nkb = (int)((K + kKBlock - 1) / kKBlock);
+    a.act = act;
+    dim3 grid((unsigned)skinny_counters(Ncol), (unsigned)a.nkb);
+    hipLaunchKernelGGL(skinny_bf16_kernel<kKSteps>, grid, dim3(kThreads), 0, stream, a);
+    return hipGetLastError();
+}
+
+}  // namespace ffn

@@ -24,11 +24,15 @@ MOE_SKEW_OFFSETS = (0.8, 0.4, 0.2, 0.0, 0.0, -0.2, -0.4, -0.8)
 
 
 def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
-    """Round float32 values to bf16 (nearest, ties to even); return uint16 bit patterns."""
-    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
-    return r.astype(np.uint16)
+    """Round finite float32 values to bf16 (nearest, ties to even); return uint16 bits.
+
+    Adding 0x7FFF plus the lowest kept bit and truncating is round-to-nearest-even
+    on the 16 dropped bits; it cannot overflow 32 bits for finite inputs."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32)
+    if not np.all(np.isfinite(x)):
+        raise ValueError("only finite values are generated")
+    lsb = (u >> np.uint32(16)) & np.uint32(1)
+    return ((u + np.uint32(0x7FFF) + lsb) >> np.uint32(16)).astype(np.uint16)
 
 
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
