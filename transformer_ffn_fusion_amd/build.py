@@ -27,6 +27,9 @@ FLAGS = [
     "-Wall",
     # keep the compiler from forming packed fp32 instructions
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # keep MFMA accumulators in arch VGPRs: with the AGPR form the register
+    # allocator rotates accumulators through copies inside the k-loops
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-I", INCLUDE,
     "-I", CSRC,
 ]

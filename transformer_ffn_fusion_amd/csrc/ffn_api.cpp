@@ -49,6 +49,10 @@ int check_dims(int64_t M, int64_t N, int64_t O, int64_t P) {
     const int64_t lim = (int64_t)1 << 31;
     if (M >= lim || N >= lim || O >= lim || P >= lim)
         return fail(FFN_EUNSUPPORTED, "dimensions must be below 2^31");
+    // the kernels address each weight matrix and each 64-row tile of X with
+    // 32-bit byte offsets below 2^31
+    if (N * O >= ((int64_t)1 << 30) || O * P >= ((int64_t)1 << 30))
+        return fail(FFN_EUNSUPPORTED, "each weight matrix must hold fewer than 2^30 elements");
     return FFN_OK;
 }
 
@@ -122,8 +126,10 @@ MoeLayout moe_layout(int64_t M, int64_t E, int k, int64_t O, int64_t P) {
 }
 
 int check_common_ptrs(const void* X, const void* W1, const void* b1, const void* W2,
-                      const void* b2, const void* Y, void* ws) {
-    if (!X || !W1 || !W2 || !Y) return fail(FFN_EINVAL, "X, W1, W2 and Y must not be NULL");
+                      const void* b2, const void* Y, void* ws, int64_t M) {
+    // with M == 0 there are no rows: X and Y may be NULL (an empty tensor's pointer)
+    if ((M > 0 && (!X || !Y)) || !W1 || !W2)
+        return fail(FFN_EINVAL, "X, W1, W2 and Y must not be NULL");
     if (!ws) return fail(FFN_EINVAL, "workspace must not be NULL");
     const void* ps[] = {X, W1, b1, W2, b2, Y};
     const char* nm[] = {"X", "W1", "b1", "W2", "b2", "Y"};
@@ -179,7 +185,7 @@ static int dense_forward(const void* X, const void* W1, const void* b1, const vo
         return fail(FFN_EINVAL, "unknown activation (act1=%d, act2=%d)", act1, act2);
     if (variant < FFN_VARIANT_AUTO || variant > FFN_VARIANT_F32)
         return fail(FFN_EINVAL, "unknown variant %d", variant);
-    rc = check_common_ptrs(X, W1, b1, W2, b2, Y, workspace);
+    rc = check_common_ptrs(X, W1, b1, W2, b2, Y, workspace, M);
     if (rc) return rc;
     const int v = resolve_variant(variant, dtype, M);
     if ((v == FFN_VARIANT_F32) != (dtype == FFN_F32))
@@ -355,8 +361,10 @@ static int moe_forward(const void* X, const float* logits, int64_t M, int64_t E,
         return fail(FFN_EINVAL, "unknown activation (act1=%d, act2=%d)", act1, act2);
     if (!logits) return fail(FFN_EINVAL, "logits must not be NULL");
     if (reinterpret_cast<uintptr_t>(logits) & 3u) return fail(FFN_EALIGN, "logits not 4-byte aligned");
-    rc = check_common_ptrs(X, W1, b1, W2, b2, Y, workspace);
+    rc = check_common_ptrs(X, W1, b1, W2, b2, Y, workspace, M);
     if (rc) return rc;
+    if (M * N >= ((int64_t)1 << 30))
+        return fail(FFN_EUNSUPPORTED, "the grouped form gathers from X with 32-bit offsets: M*N < 2^30");
     const MoeLayout L = moe_layout(M, E, k, O, P);
     if (workspace_bytes < L.total)
         return fail(FFN_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);

@@ -107,6 +107,81 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&rows)[8], uint4 (&col
 }
 
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
+
+// ---------------------------------------------------------------- LDS transposing read
+//
+// ds_read_b64_tr_b16 (gfx950): within each group of 16 lanes, output lane i,
+// element j (of 4 bf16) is element (i % 4) of the 8-byte chunk addressed by
+// lane 4*j + i/4 of the same group.  Pointing lane s = 4*j + q at the four
+// consecutive columns 4q..4q+3 of k-row j turns a row-major [k][col] tile into
+// the k-contiguous operand fragment: lane i receives column i, rows 0..3.
+typedef short shortx4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) shortx4_t lds_shortx4_t;
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+__device__ __forceinline__ uint2 lds_read_tr16(const char* p) {
+    shortx4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4_t*)(p));
+    return __builtin_bit_cast(uint2, v);
+}
+
+// ---------------------------------------------------------------- buffer loads
+//
+// Raw buffer loads with the hardware range check: a load whose byte offset is
+// at or beyond the resource's size returns zeros and touches no memory.
+// Tails (rows past M or N, columns past O or P) are loaded through an offset
+// of kOOB, so the load sequence needs no branches.  Callers keep every
+// resource below 2^31 bytes, so kOOB plus any row offset stays out of range.
+constexpr uint32_t kOOB = 0x80000000u;
+constexpr int kRsrcWord3 = 0x00020000;  // gfx9 descriptor word 3 (32-bit data format)
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t nbytes) {
+    const int n = nbytes > 0x7fffffff ? 0x7fffffff : (nbytes < 0 ? 0 : (int)nbytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, n, kRsrcWord3);
+}
+
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+
+// Direct global -> LDS load: lane l's 16 bytes land at lds_base + 16*l
+// (lds_base must be the same for the whole wave; it goes to M0).  The load
+// counts in vmcnt.  It is issued through inline assembly on purpose: the
+// compiler cannot prove these LDS writes disjoint from the LDS reads of other
+// stages and would otherwise wait for every outstanding load before each LDS
+// read, which defeats the multi-stage ring.  Ordering is explicit instead:
+// wait_vmcnt<n>() plus a workgroup barrier before a stage is read, and
+// wait_vmcnt<0>() before the LDS is reused for anything else or the
+// workgroup ends.
+typedef int int32x4_t __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int32x4_t make_srd(const void* base, int64_t nbytes) {
+    const uint64_t a = reinterpret_cast<uint64_t>(base);
+    const int n = nbytes > 0x7fffffff ? 0x7fffffff : (nbytes < 0 ? 0 : (int)nbytes);
+    int32x4_t r;
+    r.x = __builtin_amdgcn_readfirstlane((int)(uint32_t)a);
+    r.y = __builtin_amdgcn_readfirstlane((int)((a >> 32) & 0xffffu));  // stride 0
+    r.z = __builtin_amdgcn_readfirstlane(n);
+    r.w = kRsrcWord3;
+    return r;
+}
+
+__device__ __forceinline__ void dma16(const int32x4_t& srd, uint32_t byte_off, char* lds_base) {
+    const uint32_t m0 = (uint32_t)(uintptr_t)((lds_void_t*)lds_base);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "buffer_load_dwordx4 %1, %2, 0 offen lds"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane((int)m0)), "v"(byte_off), "s"(srd)
+        : "m0");
+}
+
+// s_waitcnt vmcnt(n) with the other counters left alone (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+    static_assert(n >= 0 && n < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
 __device__ __forceinline__ uint4 zero16() { return make_uint4(0u, 0u, 0u, 0u); }
 
 }  // namespace ffn

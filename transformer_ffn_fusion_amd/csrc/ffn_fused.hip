@@ -33,22 +33,50 @@ namespace ffn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBK = 32;
-constexpr int kXStage = kBM * kBK * 2;  // bytes of one X k-slab in LDS
-constexpr int kW2Stage = kBN2 * kBK * 2;
+constexpr int kBK = 32;                // k-stage depth of both products (one MFMA k-step)
+constexpr int kFrag = 1024;            // bytes of one 16-index x 32-deep operand fragment
+constexpr int kSub = kBM * kBK * 2;    // one 32-deep slab of X or H in LDS: 4 KiB
+
+// LDS layout of a row-major weight stage (32 k-rows x `cols` columns), filled by
+// direct global->LDS loads and read back through the transposing LDS read.
+// The stage is cut into 1 KiB blocks of 8 k-rows x 64 columns, block
+// (r, c) at (r * cols/64 + c) KiB.  Inside a block the 16-byte unit holding
+// row kk (0..7) and 8-column group u (0..7) sits at slot 8u + (kk ^ 4(u&1)):
+// the loading lane l writes slot l, and the 16 lanes of one transposing read
+// (4 rows x 2 neighbouring 8-column groups) hit 8 distinct 16-byte slots of a
+// 128-byte window -- no bank conflicts on either side.
+__device__ __forceinline__ uint32_t wtile_dma_row(int l) { return (l & 7) ^ (((l >> 3) & 1) << 2); }
+
+// Byte offset, inside a weight stage with `nb` 64-column blocks per row group,
+// of the 8-byte chunk that lane l of a transposing read supplies for operand
+// fragment f (columns 16f..16f+15), half t (k-rows 8g+4t..8g+4t+3).
+__device__ __forceinline__ uint32_t wtile_tr_off(int l, int nb, int f, int t) {
+    const int g = l >> 4, s = l & 15, j = s >> 2, q = s & 3;
+    const int c8 = 2 * f + (q >> 1);
+    const int slot = 8 * (c8 & 7) + ((j + 4 * t) ^ ((c8 & 1) << 2));
+    return (uint32_t)((g * nb + (c8 >> 3)) * kFrag + 16 * slot + 8 * (q & 1));
+}
 
 template <int C>
 struct FusedCfg {
-    static constexpr int kFO = C / 64;               // 16-wide hidden fragments per wave
-    static constexpr int kW1Stage = C * kBK * 2;
-    static constexpr int kStage1 = kXStage + kW1Stage;
-    static constexpr int kStageBytes = (kStage1 > kW2Stage) ? kStage1 : kW2Stage;
-    static constexpr int kHOff = 2 * kStageBytes;
-    static constexpr int kHSlab = kBM * kBK * 2;     // one 32-deep slab of H
-    static constexpr int kLds = kHOff + (C / kBK) * kHSlab;
-    static constexpr int kW1Threads = (C / 8) * 4;   // threads owning an 8x8 W1 block
-    static_assert(C % 64 == 0, "chunk must split evenly over four waves");
-    static_assert(kW1Threads <= kThreads, "one W1 block per thread at most");
+    static constexpr int kFO = C / 64;                 // hidden fragments per wave
+    static constexpr int kNB1 = C / 64;                // W1 stage: 64-column blocks per row group
+    static constexpr int kNB2 = kBN2 / 64;             // W2 stage: 8
+    static constexpr int kKS = C / kBK;                // GEMM2 k-stages per output pass
+    static constexpr int kW1Stage = 4 * kNB1 * kFrag;  // 32 x C bf16
+    static constexpr int kStage1 = kSub + kW1Stage;    // X slab + W1 slab
+    static constexpr int kStage2 = 4 * kNB2 * kFrag;   // 32 x 512 bf16 = 32 KiB
+    static constexpr int kHBytes = kKS * kSub;         // H: C/32 slabs of 64 x 32
+    static constexpr int kNS1 = 4;                     // GEMM1 stages in flight
+    static constexpr int kNS2 = (kHBytes + 3 * kStage2 <= 152 * 1024) ? 3 : 2;
+    static constexpr int kD1 = 1 + kNB1;               // DMA instructions per wave per GEMM1 stage
+    static constexpr int kD2 = kNB2;                   // ... per GEMM2 stage
+    static constexpr int kLds1 = kNS1 * kStage1;
+    static constexpr int kLds2 = kHBytes + kNS2 * kStage2;
+    static constexpr int kLds = kLds1 > kLds2 ? kLds1 : kLds2;
+    static_assert(C % 64 == 0 && (4 * kNB1) % 4 == 0, "chunk must split over four waves");
+    static_assert(kLds <= 160 * 1024, "LDS budget");
+    static_assert(kNB1 <= kFO && kNB2 == 8, "one load slot per fragment");
 };
 
 struct FusedArgs {
@@ -82,6 +110,13 @@ __device__ __forceinline__ void map_unit(int64_t unit, int64_t row_blocks, int s
     }
 }
 
+// Both products run the same pipeline: a ring of LDS stages filled by direct
+// global->LDS loads issued NS-1 stages ahead.  At the top of every iteration
+// each wave waits until its loads of the current stage have landed (the
+// newer stages stay in flight), a barrier publishes the stage to all waves,
+// the buffer freed by the previous stage is refilled, and the stage is
+// multiplied out.  Loads past the end read zeros through out-of-range
+// offsets, so every stage issues the same number of loads.
 template <int C, bool kGrouped>
 __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a) {
     using Cfg = FusedCfg<C>;
@@ -119,51 +154,40 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     const int64_t o0 = (int64_t)s * C;
     const int64_t oc = (O - o0) < C ? (O - o0) : C;  // valid hidden columns of this chunk
 
-    // ---- per-thread load roles
-    // X slab: thread -> (row xr, k-group xg); 16 consecutive threads share xg.
-    const int xr = (tid & 15) + 16 * (tid >> 6);
-    const int xg = (tid >> 4) & 3;
-    const uint16_t* xrow = nullptr;
-    if (xr < valid) {
-        int64_t token;
-        if constexpr (kGrouped) token = a.g.sorted[row0 + xr] / a.g.k;
-        else token = row0 + xr;
-        xrow = a.X + token * N;
+    // ---- X slab loads: wave w fills fragment w (rows 16w..16w+15); lane l
+    // brings row 16w + l%16, k-group l/16, straight into fragment slot l.
+    const int xr = 16 * wave + li;
+    int32x4_t rx;
+    uint32_t xrow_off = kOOB;
+    if constexpr (kGrouped) {
+        rx = make_srd(a.X, a.M * N * 2);
+        if (xr < valid) xrow_off = (uint32_t)((a.g.sorted[row0 + xr] / a.g.k) * N * 2);
+    } else {
+        rx = make_srd(a.X + row0 * N, (int64_t)valid * N * 2);
+        if (xr < valid) xrow_off = (uint32_t)(xr * N * 2);
     }
-    // weight blocks: thread -> (k-group wg, 8-column group wc)
-    const int wg = tid & 3;
-    const int wc = tid >> 2;
-    const bool w1_role = tid < Cfg::kW1Threads;
-    const bool w1_colok = w1_role && (8 * wc < oc);
-    const uint16_t* w1col = W1 + o0 + 8 * wc;
+    // ---- weight loads: lane l brings k-row wtile_dma_row(l), column group l/8.
+    // The W1 resource ends at the end of W1, so rows past N read zeros; columns
+    // past this chunk's valid width read finite neighbours whose H columns the
+    // epilogue forces to zero.
+    const int32x4_t rw1 = make_srd(W1 + o0, (N * O - o0) * 2);
+    const uint32_t w1_lane = (uint32_t)wtile_dma_row(lane) * (uint32_t)(O * 2) + 16u * (lane >> 3);
 
-    char* const hreg = smem + Cfg::kHOff;
-
-    // =========================== GEMM1: A^T = W1_chunk^T X^T ===============
-    uint4 xv;
-    uint4 wv[8];
-    auto load1 = [&](int64_t k0) {
-        int64_t kx = k0 + 8 * xg;
-        xv = (xrow && kx < N) ? ld16(xrow + kx) : zero16();
-        if (w1_role) {
-#pragma unroll
-            for (int i = 0; i < 8; ++i) {
-                int64_t n = k0 + 8 * wg + i;
-                wv[i] = (w1_colok && n < N) ? ld16(w1col + n * O) : zero16();
-            }
-        }
+    // one W1 block (8 k-rows x 64 columns) of stage kt, block index blk
+    auto dma_w1 = [&](int64_t kt, int buf, int blk) {
+        char* sw = smem + buf * Cfg::kStage1 + kSub;
+        const int r = blk / Cfg::kNB1, c = blk % Cfg::kNB1;
+        const uint32_t base = (uint32_t)(((kt * kBK + 8 * r) * O + 64 * c) * 2);
+        dma16(rw1, base + w1_lane, sw + blk * kFrag);
     };
-    auto store1 = [&](int buf) {
-        char* sx = smem + buf * Cfg::kStageBytes;
-        char* sw = sx + kXStage;
-        *reinterpret_cast<uint4*>(sx + frag_off(xr, xg)) = xv;
-        if (w1_role) {
-            uint4 cv[8];
-            transpose8x8(wv, cv);
+    auto dma_x = [&](int64_t kt, int buf) {
+        const int64_t kx = kt * kBK + 8 * lg;
+        dma16(rx, kx < N ? xrow_off + (uint32_t)(kx * 2) : kOOB, smem + buf * Cfg::kStage1 + wave * kFrag);
+    };
+    auto issue1 = [&](int64_t kt, int buf) {
+        dma_x(kt, buf);
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<uint4*>(sw + frag_off(8 * wc + j, wg)) = cv[j];
-        }
+        for (int i = 0; i < Cfg::kNB1; ++i) dma_w1(kt, buf, wave + 4 * i);
     };
 
     floatx4_t acc[Cfg::kFO][4];
@@ -172,57 +196,76 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    const int64_t nk = (N + kBK - 1) / kBK;
-    load1(0);
-    store1(0);
-    __syncthreads();
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        const int cur = (int)(kt & 1);
-        if (kt + 1 < nk) load1((kt + 1) * kBK);
-        const char* sx = smem + cur * Cfg::kStageBytes;
-        const char* sw = sx + kXStage;
-        uint4 bx[4];
+    const uint32_t trw1_0 = wtile_tr_off(lane, Cfg::kNB1, wave * Cfg::kFO, 0);
+    const uint32_t trw1_1 = wtile_tr_off(lane, Cfg::kNB1, wave * Cfg::kFO, 1);
+    // Multiply stage `buf` out of LDS while issuing the loads of stage kt_next
+    // into buffer `nbuf`: one load after each fragment's four MFMAs, so that a
+    // load waiting for the address unit never holds back a long run of MFMAs.
+    auto step1 = [&](int buf, int64_t kt_next, int nbuf) {
+        const char* st = smem + buf * Cfg::kStage1;
+        const char* sw = st + kSub;
+        uint4 bx[4], aw[Cfg::kFO];
 #pragma unroll
-        for (int fm = 0; fm < 4; ++fm) bx[fm] = ld16(sx + frag_off(16 * fm + li, lg));
+        for (int fm = 0; fm < 4; ++fm) bx[fm] = ld16(st + fm * kFrag + 16 * lane);
 #pragma unroll
         for (int fo = 0; fo < Cfg::kFO; ++fo) {
-            uint4 aw = ld16(sw + frag_off(16 * (wave * Cfg::kFO + fo) + li, lg));
-#pragma unroll
-            for (int fm = 0; fm < 4; ++fm) acc[fo][fm] = mfma16x16x32(aw, bx[fm], acc[fo][fm]);
+            // fragment offsets are linear in f: 256 bytes per 16 columns
+            const uint2 lo = lds_read_tr16(sw + trw1_0 + 256 * fo);
+            const uint2 hi = lds_read_tr16(sw + trw1_1 + 256 * fo);
+            aw[fo] = make_uint4(lo.x, lo.y, hi.x, hi.y);
         }
-        if (kt + 1 < nk) store1(cur ^ 1);
+#pragma unroll
+        for (int fo = 0; fo < Cfg::kFO; ++fo) {
+#pragma unroll
+            for (int fm = 0; fm < 4; ++fm) acc[fo][fm] = mfma16x16x32(aw[fo], bx[fm], acc[fo][fm]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (fo < Cfg::kNB1) dma_w1(kt_next, nbuf, wave + 4 * fo);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        dma_x(kt_next, nbuf);
+    };
+
+    // =========================== GEMM1: A^T = W1_chunk^T X^T ===============
+    const int64_t nk = (N + kBK - 1) / kBK;
+#pragma unroll
+    for (int i = 0; i < Cfg::kNS1 - 1; ++i) issue1(i, i);
+    int cbuf = 0, ibuf = Cfg::kNS1 - 1;
+    for (int64_t kt = 0; kt < nk; ++kt) {
+        wait_vmcnt<Cfg::kD1 * (Cfg::kNS1 - 2)>();
         __syncthreads();
+        step1(cbuf, kt + Cfg::kNS1 - 1, ibuf);
+        cbuf = (cbuf + 1 == Cfg::kNS1) ? 0 : cbuf + 1;
+        ibuf = (ibuf + 1 == Cfg::kNS1) ? 0 : ibuf + 1;
     }
+    wait_vmcnt<0>();   // the stages loaded past the end still write LDS
+    __syncthreads();
 
     // =========================== GEMM2 setup ==============================
+    // W2 stage: 32 hidden rows x 512 output columns.  The W2 resource covers
+    // exactly this chunk's rows, so rows past the chunk read zeros; columns
+    // past P read finite neighbours that reach only unstored partial columns.
+    const int32x4_t rw2 = make_srd(W2 + o0 * P, oc * P * 2);
+    const uint32_t w2_lane = (uint32_t)wtile_dma_row(lane) * (uint32_t)(P * 2) + 16u * (lane >> 3);
     const int64_t np = (P + kBN2 - 1) / kBN2;
-    const int nk2 = (int)((oc + kBK - 1) / kBK);
-    const int64_t nsteps = np * nk2;
-    const uint16_t* w2base = W2 + (o0 + 8 * wg) * P + 8 * wc;
-
-    auto load2 = [&](int64_t step) {
-        int64_t pt = step / nk2;
-        int ks = (int)(step - pt * nk2);
-        int64_t p = pt * kBN2 + 8 * wc;
-        int64_t orow = (int64_t)ks * kBK;   // relative to o0 + 8*wg
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            int64_t o = orow + 8 * wg + i;  // relative to o0
-            wv[i] = (o < oc && p < P) ? ld16(w2base + (orow + i) * P + pt * kBN2) : zero16();
-        }
+    char* const w2reg = smem + Cfg::kHBytes;
+    auto dma_w2 = [&](int64_t step, int blk) {
+        const int64_t pt = step / Cfg::kKS;
+        const int ks = (int)(step - pt * Cfg::kKS);
+        char* st = w2reg + (int)(step % Cfg::kNS2) * Cfg::kStage2;
+        const int r = blk / Cfg::kNB2, c = blk % Cfg::kNB2;
+        const uint32_t base = (uint32_t)(((int64_t)(ks * kBK + 8 * r) * P + pt * kBN2 + 64 * c) * 2);
+        dma16(rw2, base + w2_lane, st + blk * kFrag);
     };
-    auto store2 = [&](int buf) {
-        char* sw = smem + buf * Cfg::kStageBytes;
-        uint4 cv[8];
-        transpose8x8(wv, cv);
+    auto issue2 = [&](int64_t step) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j)
-            *reinterpret_cast<uint4*>(sw + frag_off(8 * wc + j, wg)) = cv[j];
+        for (int i = 0; i < Cfg::kNB2; ++i) dma_w2(step, wave + 4 * i);
     };
-
-    if (nsteps > 0) load2(0);
+    // the first W2 stages do not depend on H: start them before the epilogue
+#pragma unroll
+    for (int i = 0; i < Cfg::kNS2 - 1; ++i) issue2(i);
 
     // ---- epilogue 1: H = act(A + b1) -> bf16 -> LDS (GEMM2 operand layout)
+    char* const hreg = smem;
 #pragma unroll
     for (int fo = 0; fo < Cfg::kFO; ++fo) {
         const int ol = 16 * (wave * Cfg::kFO + fo) + 4 * lg;  // first of 4 hidden cols
@@ -236,8 +279,8 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
             bias[2] = bf16_lo(bb.y);
             bias[3] = bf16_hi(bb.y);
         }
-        const int slab = ol / kBK;
-        const int g = (ol % kBK) / 8;
+        const int slab = ol / 32;
+        const int g = (ol % 32) / 8;
         const int e = ol % 8;
 #pragma unroll
         for (int fm = 0; fm < 4; ++fm) {
@@ -246,8 +289,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
             for (int r = 0; r < 4; ++r)
                 h[r] = colok ? apply_act(a.act1, acc[fo][fm][r] + bias[r]) : 0.f;
             uint2 pk = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-            *reinterpret_cast<uint2*>(hreg + slab * Cfg::kHSlab + frag_off(16 * fm + li, g) +
-                                      2 * e) = pk;
+            *reinterpret_cast<uint2*>(hreg + slab * kSub + frag_off(16 * fm + li, g) + 2 * e) = pk;
         }
     }
 
@@ -258,45 +300,53 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc2[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    if (nsteps > 0) store2(0);
-    __syncthreads();
+    const uint32_t trw2_0 = wtile_tr_off(lane, Cfg::kNB2, 8 * wave, 0);
+    const uint32_t trw2_1 = wtile_tr_off(lane, Cfg::kNB2, 8 * wave, 1);
     float* const part = a.part + (int64_t)s * a.rows_out * P;
-    for (int64_t step = 0; step < nsteps; ++step) {
-        const int cur = (int)(step & 1);
-        const int64_t pt = step / nk2;
-        const int ks = (int)(step - pt * nk2);
-        if (step + 1 < nsteps) load2(step + 1);
-        const char* sw = smem + cur * Cfg::kStageBytes;
-        const char* hs = hreg + ks * Cfg::kHSlab;
-        uint4 bh[4];
+    int64_t step = 0;   // global stage counter; the load ring runs across passes
+    for (int64_t pt = 0; pt < np; ++pt) {
+#pragma unroll 2
+        for (int ks = 0; ks < Cfg::kKS; ++ks, ++step) {
+            wait_vmcnt<Cfg::kD2 * (Cfg::kNS2 - 2)>();
+            __syncthreads();
+            const char* sw = w2reg + (int)(step % Cfg::kNS2) * Cfg::kStage2;
+            const char* hs = hreg + ks * kSub;
+            uint4 bh[4], aw[8];
 #pragma unroll
-        for (int fm = 0; fm < 4; ++fm) bh[fm] = ld16(hs + frag_off(16 * fm + li, lg));
-#pragma unroll
-        for (int fp = 0; fp < 8; ++fp) {
-            uint4 aw = ld16(sw + frag_off(128 * wave + 16 * fp + li, lg));
-#pragma unroll
-            for (int fm = 0; fm < 4; ++fm) acc2[fp][fm] = mfma16x16x32(aw, bh[fm], acc2[fp][fm]);
-        }
-        if (ks == nk2 - 1) {
-            // store this pass's partial: lane holds 4 consecutive columns of row m
+            for (int fm = 0; fm < 4; ++fm) bh[fm] = ld16(hs + frag_off(16 * fm + li, lg));
 #pragma unroll
             for (int fp = 0; fp < 8; ++fp) {
-                const int64_t p = pt * kBN2 + 128 * wave + 16 * fp + 4 * lg;
+                const uint2 lo = lds_read_tr16(sw + trw2_0 + 256 * fp);
+                const uint2 hi = lds_read_tr16(sw + trw2_1 + 256 * fp);
+                aw[fp] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
 #pragma unroll
-                for (int fm = 0; fm < 4; ++fm) {
-                    const int m = 16 * fm + li;
-                    if (m < valid && p < P) {
-                        float4 v = make_float4(acc2[fp][fm][0], acc2[fp][fm][1], acc2[fp][fm][2],
-                                               acc2[fp][fm][3]);
-                        *reinterpret_cast<float4*>(part + (row0 + m) * P + p) = v;
-                    }
-                    acc2[fp][fm] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-                }
+            for (int fp = 0; fp < 8; ++fp) {
+#pragma unroll
+                for (int fm = 0; fm < 4; ++fm)
+                    acc2[fp][fm] = mfma16x16x32(aw[fp], bh[fm], acc2[fp][fm]);
+                __builtin_amdgcn_sched_barrier(0);
+                dma_w2(step + Cfg::kNS2 - 1, wave + 4 * fp);  // kNB2 == 8 loads per stage
+                __builtin_amdgcn_sched_barrier(0);
             }
         }
-        if (step + 1 < nsteps) store2(cur ^ 1);
-        __syncthreads();
+        // this pass's partial: lane holds 4 consecutive columns of row m
+#pragma unroll
+        for (int fp = 0; fp < 8; ++fp) {
+            const int64_t p = pt * kBN2 + 128 * wave + 16 * fp + 4 * lg;
+#pragma unroll
+            for (int fm = 0; fm < 4; ++fm) {
+                const int m = 16 * fm + li;
+                if (m < valid && p < P) {
+                    float4 v = make_float4(acc2[fp][fm][0], acc2[fp][fm][1], acc2[fp][fm][2],
+                                           acc2[fp][fm][3]);
+                    *reinterpret_cast<float4*>(part + (row0 + m) * P + p) = v;
+                }
+                acc2[fp][fm] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+            }
+        }
     }
+    wait_vmcnt<0>();   // no load into LDS may outlive the workgroup
 }
 
 // ---------------------------------------------------------------- reduce

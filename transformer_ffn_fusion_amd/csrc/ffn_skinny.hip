@@ -27,6 +27,7 @@ namespace ffn {
 namespace {
 
 constexpr int kThreads = 256;
+constexpr int kBatch = 8;    // partials the last arriver loads at once
 
 struct SkinnyArgs {
     const uint16_t* A;
@@ -55,20 +56,24 @@ __global__ __launch_bounds__(kThreads) void skinny_bf16_kernel(SkinnyArgs a) {
     const int kb = blockIdx.y;
     const int64_t K = a.K, Ncol = a.Ncol;
     const int64_t col = cb * kSkinnyCols + 8 * c;
-    const bool colok = col < Ncol;
     const int64_t kw = (int64_t)kb * a.kblock + (int64_t)wave * 32 * KSTEPS;
 
-    // ---- issue every load of this lane first
+    // ---- issue every load of this lane first (out-of-range rows/columns read zeros)
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, a.M * K * 2);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.W, K * Ncol * 2);
+    const uint32_t arow = (uint32_t)(c * K * 2);
     uint4 af[KSTEPS];
     uint4 wr[KSTEPS][8];
 #pragma unroll
     for (int t = 0; t < KSTEPS; ++t) {
         const int64_t k0 = kw + 32 * t + 8 * g;
-        af[t] = (c < a.M && k0 < K) ? ld16(a.A + c * K + k0) : zero16();
+        af[t] = bload16(ra, (c < a.M && k0 < K) ? arow + (uint32_t)(k0 * 2) : kOOB);
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int64_t n = k0 + i;
-            wr[t][i] = (colok && n < K) ? ld16(a.W + n * Ncol + col) : zero16();
+            // rows past K fall outside the resource and read zeros; columns past
+            // Ncol read finite neighbours that only reach unstored columns
+            wr[t][i] = bload16(rw, (uint32_t)((n * Ncol + col) * 2));
         }
     }
 
@@ -113,17 +118,27 @@ __global__ __launch_bounds__(kThreads) void skinny_bf16_kernel(SkinnyArgs a) {
         if (!s_last) return;
         __threadfence();  // acquire the other blocks' partials
         if (gc < Ncol) {
+            // load the K-blocks' partials eight at a time (all eight in flight),
+            // adding them in ascending K-block order (fixed, whoever arrives last)
             const float* src = a.part + (int64_t)m * Ncol + gc;
-            float4 lo = *reinterpret_cast<const float4*>(src);
-            float4 hi = *reinterpret_cast<const float4*>(src + 4);
-            v[0] = lo.x; v[1] = lo.y; v[2] = lo.z; v[3] = lo.w;
-            v[4] = hi.x; v[5] = hi.y; v[6] = hi.z; v[7] = hi.w;
-            for (int q = 1; q < a.nkb; ++q) {
-                const float* s2 = src + (int64_t)q * kSkinnyMaxM * Ncol;
-                lo = *reinterpret_cast<const float4*>(s2);
-                hi = *reinterpret_cast<const float4*>(s2 + 4);
-                v[0] += lo.x; v[1] += lo.y; v[2] += lo.z; v[3] += lo.w;
-                v[4] += hi.x; v[5] += hi.y; v[6] += hi.z; v[7] += hi.w;
+            const int64_t kstride = (int64_t)kSkinnyMaxM * Ncol;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = 0.f;
+            for (int q0 = 0; q0 < a.nkb; q0 += kBatch) {
+                float4 lo[kBatch], hi[kBatch];
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    const int q = (q0 + j < a.nkb) ? q0 + j : q0;
+                    lo[j] = *reinterpret_cast<const float4*>(src + q * kstride);
+                    hi[j] = *reinterpret_cast<const float4*>(src + q * kstride + 4);
+                }
+#pragma unroll
+                for (int j = 0; j < kBatch; ++j) {
+                    if (q0 + j < a.nkb) {
+                        v[0] += lo[j].x; v[1] += lo[j].y; v[2] += lo[j].z; v[3] += lo[j].w;
+                        v[4] += hi[j].x; v[5] += hi[j].y; v[6] += hi[j].z; v[7] += hi[j].w;
+                    }
+                }
             }
         }
         if (tid == 0) a.counters[cb] = 0;  // ready for the next call
