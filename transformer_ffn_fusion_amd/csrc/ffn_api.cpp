@@ -67,7 +67,6 @@ int resolve_variant(int variant, int dtype, int64_t M) {
 // ---- dense workspace layouts (byte offsets, each region 256-byte aligned)
 struct DenseLayout {
     size_t part = 0;       // fused / f32: fp32 partials
-    size_t counters = 0;   // skinny: int32 counters (layer 1 then layer 2)
     size_t part1 = 0, h = 0, part2 = 0;
     size_t total = 0;
 };
@@ -84,8 +83,6 @@ DenseLayout dense_layout(int64_t M, int64_t N, int64_t O, int64_t P, int variant
         L.total = align_up((size_t)S * M * P * sizeof(float));
     } else {  // skinny
         size_t off = 0;
-        L.counters = off;
-        off += align_up(sizeof(int32_t) * (ffn::skinny_counters(O) + ffn::skinny_counters(P)));
         L.part1 = off;
         off += align_up(sizeof(float) * ffn::skinny_partial_floats(N, O));
         L.h = off;
@@ -227,19 +224,18 @@ static int dense_forward(const void* X, const void* W1, const void* b1, const vo
                       "split reduction kernel");
         if (rc) return rc;
     } else {
-        int32_t* cnt = reinterpret_cast<int32_t*>(ws + L.counters);
         uint16_t* H = reinterpret_cast<uint16_t*>(ws + L.h);
         rc = launched(ffn::launch_skinny_bf16((const uint16_t*)X, (const uint16_t*)W1,
                                               (const uint16_t*)b1, H,
-                                              reinterpret_cast<float*>(ws + L.part1), cnt, M, N,
-                                              O, act1, st),
+                                              reinterpret_cast<float*>(ws + L.part1), M, N, O,
+                                              act1, st),
                       "skinny layer-1 kernel");
         if (rc) return rc;
         if ((rc = mark(events, n_events, 1, st))) return rc;
         rc = launched(ffn::launch_skinny_bf16(H, (const uint16_t*)W2, (const uint16_t*)b2,
                                               (uint16_t*)Y,
-                                              reinterpret_cast<float*>(ws + L.part2),
-                                              cnt + ffn::skinny_counters(O), M, O, P, act2, st),
+                                              reinterpret_cast<float*>(ws + L.part2), M, O, P,
+                                              act2, st),
                       "skinny layer-2 kernel");
         if (rc) return rc;
     }

@@ -94,16 +94,21 @@ struct FusedArgs {
 };
 
 // Unit -> (row tile, hidden chunk).  Workgroups are dispatched round-robin
-// over the 8 XCDs; when the row tiles divide evenly, all chunks of one row
-// tile are given to the same XCD so they share its L2 (the X rows) and run
-// at the same time.
+// over the 8 XCDs (unit u runs on XCD u % 8), and each XCD has its own L2.
+// When the split count divides 8 and the row tiles divide evenly, every XCD
+// works on ONE hidden chunk (XCD x takes chunk x % splits and every
+// (8/splits)-th row tile): its 32 workgroups then stream the same W1 and W2
+// chunk in step, so each weight byte leaves HBM/MALL once per XCD group
+// instead of once per XCD for every chunk.  Otherwise units are numbered
+// row-major.
 __device__ __forceinline__ void map_unit(int64_t unit, int64_t row_blocks, int splits,
                                          int64_t* rb, int* s) {
-    if ((row_blocks & 7) == 0) {
-        int64_t xcd = unit & 7;
-        int64_t j = unit >> 3;
-        *rb = (j / splits) * 8 + xcd;
-        *s = (int)(j % splits);
+    const int g = (splits > 0 && 8 % splits == 0) ? 8 / splits : 0;
+    if (g > 0 && row_blocks % g == 0) {
+        const int x = (int)(unit & 7);
+        const int64_t j = unit >> 3;
+        *s = x % splits;
+        *rb = (int64_t)(x / splits) + (int64_t)g * j;
     } else {
         *rb = unit / splits;
         *s = (int)(unit % splits);
@@ -338,9 +343,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
             for (int fm = 0; fm < 4; ++fm) {
                 const int m = 16 * fm + li;
                 if (m < valid && p < P) {
-                    float4 v = make_float4(acc2[fp][fm][0], acc2[fp][fm][1], acc2[fp][fm][2],
-                                           acc2[fp][fm][3]);
-                    *reinterpret_cast<float4*>(part + (row0 + m) * P + p) = v;
+                    // streaming store: the partial is read once, by the reduction pass
+                    floatx4_t* dst = reinterpret_cast<floatx4_t*>(part + (row0 + m) * P + p);
+                    __builtin_nontemporal_store(acc2[fp][fm], dst);
                 }
                 acc2[fp][fm] = floatx4_t{0.f, 0.f, 0.f, 0.f};
             }

@@ -43,12 +43,12 @@ constexpr int kSkinnyCols = 128;   // output columns per workgroup
 constexpr int kSkinnyMaxM = 16;
 int64_t skinny_kblock(int64_t K, int64_t Ncol);                 // rows of K per workgroup
 size_t skinny_partial_floats(int64_t K, int64_t Ncol);          // workspace floats
-int64_t skinny_counters(int64_t Ncol);                          // workspace counters
 
-// out[m][c] = act(sum_k A[m][k] W[k][c] + bias[c]) as bf16, m < M <= 16.
+// out[m][c] = act(sum_k A[m][k] W[k][c] + bias[c]) as bf16, m < M <= 16: a
+// split-K weight-stream kernel plus an ordered reduction kernel.
 hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* W, const uint16_t* bias,
-                              uint16_t* out, float* part, int32_t* counters, int64_t M,
-                              int64_t K, int64_t Ncol, int act, hipStream_t stream);
+                              uint16_t* out, float* part, int64_t M, int64_t K, int64_t Ncol,
+                              int act, hipStream_t stream);
 
 // ---- fp32 path
 

@@ -14,11 +14,13 @@
 //  * the 16 rows map exactly onto the 16-row side of v_mfma_f32_16x16x32_bf16;
 //    the weight block is transposed in registers (8x8 per lane) straight into
 //    the MFMA operand layout -- no LDS round trip for the weights;
-//  * the K blocks are reduced in a fixed order: each workgroup writes its
-//    fp32 partial, and the last workgroup to finish a column block (one
-//    integer counter per block) sums all partials in ascending K-block order,
-//    adds the bias once, applies the activation and rounds once to bf16.  The
-//    last arriver resets its counter, so the workspace needs zeroing only once.
+//  * the K blocks are reduced in a fixed order by a second small kernel: each
+//    workgroup writes its fp32 partial; the reduction sums them in ascending
+//    K-block order, adds the bias once, applies the activation and rounds once
+//    to bf16.  (A last-arriver reduction inside the first kernel would need a
+//    device-scope release per workgroup; on this part that fence writes back
+//    the XCD's L2 and the workgroups of an XCD serialise on it -- measured at
+//    ~20 us per layer, against ~1.5 us for the loads and the math.)
 #include "ffn_device.h"
 #include "ffn_internal.h"
 
@@ -35,7 +37,6 @@ struct SkinnyArgs {
     const uint16_t* bias;
     uint16_t* out;
     float* part;        // [nkb][16][Ncol]
-    int32_t* counters;  // [ncb]
     int64_t M, K, Ncol;
     int64_t kblock;
     int nkb;
@@ -45,7 +46,6 @@ struct SkinnyArgs {
 template <int KSTEPS>
 __global__ __launch_bounds__(kThreads) void skinny_bf16_kernel(SkinnyArgs a) {
     __shared__ __attribute__((aligned(16))) float red[4][kSkinnyMaxM][kSkinnyCols];
-    __shared__ int s_last;
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
@@ -106,42 +106,12 @@ __global__ __launch_bounds__(kThreads) void skinny_bf16_kernel(SkinnyArgs a) {
     const bool outok = (m < a.M) && (gc < Ncol);
 
     if (a.nkb > 1) {
-        float* mine = a.part + ((int64_t)kb * kSkinnyMaxM + m) * Ncol + gc;
         if (gc < Ncol) {
+            float* mine = a.part + ((int64_t)kb * kSkinnyMaxM + m) * Ncol + gc;
             *reinterpret_cast<float4*>(mine) = make_float4(v[0], v[1], v[2], v[3]);
             *reinterpret_cast<float4*>(mine + 4) = make_float4(v[4], v[5], v[6], v[7]);
         }
-        __threadfence();  // release this block's partial
-        __syncthreads();
-        if (tid == 0) s_last = (atomicAdd(&a.counters[cb], 1) == a.nkb - 1);
-        __syncthreads();
-        if (!s_last) return;
-        __threadfence();  // acquire the other blocks' partials
-        if (gc < Ncol) {
-            // load the K-blocks' partials eight at a time (all eight in flight),
-            // adding them in ascending K-block order (fixed, whoever arrives last)
-            const float* src = a.part + (int64_t)m * Ncol + gc;
-            const int64_t kstride = (int64_t)kSkinnyMaxM * Ncol;
-#pragma unroll
-            for (int i = 0; i < 8; ++i) v[i] = 0.f;
-            for (int q0 = 0; q0 < a.nkb; q0 += kBatch) {
-                float4 lo[kBatch], hi[kBatch];
-#pragma unroll
-                for (int j = 0; j < kBatch; ++j) {
-                    const int q = (q0 + j < a.nkb) ? q0 + j : q0;
-                    lo[j] = *reinterpret_cast<const float4*>(src + q * kstride);
-                    hi[j] = *reinterpret_cast<const float4*>(src + q * kstride + 4);
-                }
-#pragma unroll
-                for (int j = 0; j < kBatch; ++j) {
-                    if (q0 + j < a.nkb) {
-                        v[0] += lo[j].x; v[1] += lo[j].y; v[2] += lo[j].z; v[3] += lo[j].w;
-                        v[4] += hi[j].x; v[5] += hi[j].y; v[6] += hi[j].z; v[7] += hi[j].w;
-                    }
-                }
-            }
-        }
-        if (tid == 0) a.counters[cb] = 0;  // ready for the next call
+        return;
     }
     if (!outok) return;
     if (a.bias) {
@@ -160,6 +130,51 @@ __global__ __launch_bounds__(kThreads) void skinny_bf16_kernel(SkinnyArgs a) {
     *reinterpret_cast<uint4*>(a.out + (int64_t)m * Ncol + gc) = o;
 }
 
+// out[m][c] = act(sum_kb part[kb][m][c] + bias[c]), K blocks in ascending order.
+__global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ part, int nkb,
+                                                            const uint16_t* __restrict__ bias,
+                                                            uint16_t* __restrict__ out, int64_t M,
+                                                            int64_t Ncol, int act) {
+    const int64_t nvec = M * (Ncol / 8);
+    const int64_t v = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (v >= nvec) return;
+    const int64_t m = v / (Ncol / 8);
+    const int64_t c = (v - m * (Ncol / 8)) * 8;
+    const float* src = part + m * Ncol + c;
+    const int64_t kstride = (int64_t)kSkinnyMaxM * Ncol;
+    float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    for (int q0 = 0; q0 < nkb; q0 += kBatch) {
+        float4 lo[kBatch], hi[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {   // all loads of a batch in flight at once
+            const int q = (q0 + j < nkb) ? q0 + j : q0;
+            lo[j] = *reinterpret_cast<const float4*>(src + q * kstride);
+            hi[j] = *reinterpret_cast<const float4*>(src + q * kstride + 4);
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+            if (q0 + j < nkb) {
+                y[0] += lo[j].x; y[1] += lo[j].y; y[2] += lo[j].z; y[3] += lo[j].w;
+                y[4] += hi[j].x; y[5] += hi[j].y; y[6] += hi[j].z; y[7] += hi[j].w;
+            }
+        }
+    }
+    if (bias) {
+        const uint4 bb = ld16(bias + c);
+        const uint32_t bw[4] = {bb.x, bb.y, bb.z, bb.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            y[2 * i] += bf16_lo(bw[i]);
+            y[2 * i + 1] += bf16_hi(bw[i]);
+        }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) y[i] = apply_act(act, y[i]);
+    *reinterpret_cast<uint4*>(out + m * Ncol + c) =
+        make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
+                   pack_bf16x2(y[6], y[7]));
+}
+
 constexpr int kKSteps = 2;   // 32-deep MFMA steps per wave
 constexpr int64_t kKBlock = 4 * 32 * kKSteps;
 
@@ -172,26 +187,29 @@ size_t skinny_partial_floats(int64_t K, int64_t Ncol) {
     return nkb > 1 ? (size_t)(nkb * kSkinnyMaxM * Ncol) : 0;
 }
 
-int64_t skinny_counters(int64_t Ncol) { return (Ncol + kSkinnyCols - 1) / kSkinnyCols; }
 
 hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* W, const uint16_t* bias,
-                              uint16_t* out, float* part, int32_t* counters, int64_t M,
-                              int64_t K, int64_t Ncol, int act, hipStream_t stream) {
+                              uint16_t* out, float* part, int64_t M, int64_t K, int64_t Ncol,
+                              int act, hipStream_t stream) {
     SkinnyArgs a;
     a.A = A;
     a.W = W;
     a.bias = bias;
     a.out = out;
     a.part = part;
-    a.counters = counters;
     a.M = M;
     a.K = K;
     a.Ncol = Ncol;
     a.kblock = kKBlock;
     a.nkb = (int)((K + kKBlock - 1) / kKBlock);
     a.act = act;
-    dim3 grid((unsigned)skinny_counters(Ncol), (unsigned)a.nkb);
+    dim3 grid((unsigned)((Ncol + kSkinnyCols - 1) / kSkinnyCols), (unsigned)a.nkb);
     hipLaunchKernelGGL(skinny_bf16_kernel<kKSteps>, grid, dim3(kThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess || a.nkb <= 1) return e;
+    const int64_t nvec = M * (Ncol / 8);
+    hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0,
+                       stream, part, a.nkb, bias, out, M, Ncol, act);
     return hipGetLastError();
 }
 
