@@ -131,51 +131,48 @@ __global__ __launch_bounds__(kThreads) void skinny_bf16_kernel(SkinnyArgs a) {
 }
 
 // out[m][c] = act(sum_kb part[kb][m][c] + bias[c]), K blocks in ascending order.
-__global__ __launch_bounds__(256) void skinny_reduce_kernel(const float* __restrict__ part, int nkb,
-                                                            const uint16_t* __restrict__ bias,
-                                                            uint16_t* __restrict__ out, int64_t M,
-                                                            int64_t Ncol, int act) {
-    const int64_t nvec = M * (Ncol / 8);
+// One thread per 4 output columns; small blocks so the few thousand threads
+// spread over many CUs (the partials are L2/MALL-resident, just written).
+__global__ __launch_bounds__(64) void skinny_reduce_kernel(const float* __restrict__ part, int nkb,
+                                                           const uint16_t* __restrict__ bias,
+                                                           uint16_t* __restrict__ out, int64_t M,
+                                                           int64_t Ncol, int act) {
+    const int64_t nvec = M * (Ncol / 4);
     const int64_t v = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
     if (v >= nvec) return;
-    const int64_t m = v / (Ncol / 8);
-    const int64_t c = (v - m * (Ncol / 8)) * 8;
+    const int64_t m = v / (Ncol / 4);
+    const int64_t c = (v - m * (Ncol / 4)) * 4;
     const float* src = part + m * Ncol + c;
     const int64_t kstride = (int64_t)kSkinnyMaxM * Ncol;
-    float y[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int q0 = 0; q0 < nkb; q0 += kBatch) {
-        float4 lo[kBatch], hi[kBatch];
+    float y[4] = {0.f, 0.f, 0.f, 0.f};
+    for (int q0 = 0; q0 < nkb; q0 += 2 * kBatch) {
+        float4 t[2 * kBatch];
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {   // all loads of a batch in flight at once
+        for (int j = 0; j < 2 * kBatch; ++j) {   // all loads of a batch in flight at once
             const int q = (q0 + j < nkb) ? q0 + j : q0;
-            lo[j] = *reinterpret_cast<const float4*>(src + q * kstride);
-            hi[j] = *reinterpret_cast<const float4*>(src + q * kstride + 4);
+            t[j] = *reinterpret_cast<const float4*>(src + q * kstride);
         }
 #pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
+        for (int j = 0; j < 2 * kBatch; ++j) {
             if (q0 + j < nkb) {
-                y[0] += lo[j].x; y[1] += lo[j].y; y[2] += lo[j].z; y[3] += lo[j].w;
-                y[4] += hi[j].x; y[5] += hi[j].y; y[6] += hi[j].z; y[7] += hi[j].w;
+                y[0] += t[j].x; y[1] += t[j].y; y[2] += t[j].z; y[3] += t[j].w;
             }
         }
     }
     if (bias) {
-        const uint4 bb = ld16(bias + c);
-        const uint32_t bw[4] = {bb.x, bb.y, bb.z, bb.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            y[2 * i] += bf16_lo(bw[i]);
-            y[2 * i + 1] += bf16_hi(bw[i]);
-        }
+        const uint2 bb = *reinterpret_cast<const uint2*>(bias + c);
+        y[0] += bf16_lo(bb.x);
+        y[1] += bf16_hi(bb.x);
+        y[2] += bf16_lo(bb.y);
+        y[3] += bf16_hi(bb.y);
     }
 #pragma unroll
-    for (int i = 0; i < 8; ++i) y[i] = apply_act(act, y[i]);
-    *reinterpret_cast<uint4*>(out + m * Ncol + c) =
-        make_uint4(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]), pack_bf16x2(y[4], y[5]),
-                   pack_bf16x2(y[6], y[7]));
+    for (int i = 0; i < 4; ++i) y[i] = apply_act(act, y[i]);
+    *reinterpret_cast<uint2*>(out + m * Ncol + c) =
+        make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
 }
 
-constexpr int kKSteps = 2;   // 32-deep MFMA steps per wave
+constexpr int kKSteps = 1;   // 32-deep MFMA steps per wave
 constexpr int64_t kKBlock = 4 * 32 * kKSteps;
 
 }  // namespace
@@ -207,8 +204,8 @@ hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* W, const uint16
     hipLaunchKernelGGL(skinny_bf16_kernel<kKSteps>, grid, dim3(kThreads), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nkb <= 1) return e;
-    const int64_t nvec = M * (Ncol / 8);
-    hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((nvec + 255) / 256)), dim3(256), 0,
+    const int64_t nvec = M * (Ncol / 4);
+    hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((nvec + 63) / 64)), dim3(64), 0,
                        stream, part, a.nkb, bias, out, M, Ncol, act);
     return hipGetLastError();
 }
