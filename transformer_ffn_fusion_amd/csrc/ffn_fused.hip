@@ -19,9 +19,12 @@
 //    once (the tensor-parallel equation: the bias is added after the sum) and
 //    casts.  No floating-point atomics: results are bitwise reproducible.
 //  * weights are row-major (N x O, O x P: output index contiguous).  The MFMA
-//    wants k-contiguous operands, so each thread loads an 8x8 block (8 rows of
-//    16 bytes), transposes it in registers and writes 8 k-contiguous chunks to
-//    the swizzled LDS tile.
+//    wants k-contiguous operands: weight stages go to LDS row by row through
+//    direct global->LDS loads (coalesced, no registers involved) and come back
+//    k-contiguous through the gfx950 transposing LDS read (ds_read_b64_tr_b16);
+//  * each workgroup runs 4 loader waves (they only issue the direct-to-LDS
+//    loads) beside 4 multiplier waves (LDS reads + MFMA), one of each per SIMD,
+//    so that the address unit's back-pressure never stalls the matrix cores;
 //  * the grouped form (Mixture-of-Experts) takes its rows from a tile table:
 //    expert id, first row of the expert's sorted token list, valid rows; X
 //    rows are gathered by token id on load.
@@ -32,7 +35,8 @@ namespace ffn {
 
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kMulWaves = 4;              // waves that multiply (one per SIMD)
+constexpr int kThreads = 128 * kMulWaves; // ... plus as many waves that only load
 constexpr int kBK = 32;                // k-stage depth of both products (one MFMA k-step)
 constexpr int kFrag = 1024;            // bytes of one 16-index x 32-deep operand fragment
 constexpr int kSub = kBM * kBK * 2;    // one 32-deep slab of X or H in LDS: 4 KiB
@@ -41,11 +45,16 @@ constexpr int kSub = kBM * kBK * 2;    // one 32-deep slab of X or H in LDS: 4 K
 // direct global->LDS loads and read back through the transposing LDS read.
 // The stage is cut into 1 KiB blocks of 8 k-rows x 64 columns, block
 // (r, c) at (r * cols/64 + c) KiB.  Inside a block the 16-byte unit holding
-// row kk (0..7) and 8-column group u (0..7) sits at slot 8u + (kk ^ 4(u&1)):
-// the loading lane l writes slot l, and the 16 lanes of one transposing read
-// (4 rows x 2 neighbouring 8-column groups) hit 8 distinct 16-byte slots of a
-// 128-byte window -- no bank conflicts on either side.
-__device__ __forceinline__ uint32_t wtile_dma_row(int l) { return (l & 7) ^ (((l >> 3) & 1) << 2); }
+// row kk (0..7) and 8-column group u (0..7) sits at slot 8kk + (u ^ 2kk mod 8).
+// The loading lane l writes slot l, so lanes 8kk..8kk+7 bring the 128
+// contiguous bytes of row kk (every aligned lane quad stays inside one 64-byte
+// segment: the loads coalesce).  The 16 lanes of one transposing read (4 rows
+// x 2 neighbouring 8-column groups) hit 8 distinct 16-byte slots of a 128-byte
+// window -- no bank conflicts on the read side either.
+__device__ __forceinline__ uint32_t wtile_dma_off(int l, uint32_t row_bytes) {
+    const int kk = l >> 3;
+    return (uint32_t)kk * row_bytes + 16u * (uint32_t)((l & 7) ^ ((2 * kk) & 7));
+}
 
 // Byte offset, inside a weight stage with `nb` 64-column blocks per row group,
 // of the 8-byte chunk that lane l of a transposing read supplies for operand
@@ -53,9 +62,17 @@ __device__ __forceinline__ uint32_t wtile_dma_row(int l) { return (l & 7) ^ (((l
 __device__ __forceinline__ uint32_t wtile_tr_off(int l, int nb, int f, int t) {
     const int g = l >> 4, s = l & 15, j = s >> 2, q = s & 3;
     const int c8 = 2 * f + (q >> 1);
-    const int slot = 8 * (c8 & 7) + ((j + 4 * t) ^ ((c8 & 1) << 2));
+    const int kk = j + 4 * t;
+    const int slot = 8 * kk + ((c8 & 7) ^ ((2 * kk) & 7));
     return (uint32_t)((g * nb + (c8 >> 3)) * kFrag + 16 * slot + 8 * (q & 1));
 }
+
+// LDS layout of one X fragment (16 rows x 32 k, 1 KiB): the 16-byte unit of
+// row r and 8-deep k-group c sits at slot 4r + (c ^ (r/2 mod 4)).  The loading
+// lane l writes slot l, so lanes 4r..4r+3 bring row r's 64 contiguous bytes;
+// the operand read (lane l: row l%16, k-group l/16) is conflict-free within
+// every group of 8 lanes.
+__device__ __forceinline__ int xfrag_slot(int r, int c) { return 4 * r + (c ^ ((r >> 1) & 3)); }
 
 template <int C>
 struct FusedCfg {
@@ -115,13 +132,16 @@ __device__ __forceinline__ void map_unit(int64_t unit, int64_t row_blocks, int s
     }
 }
 
-// Both products run the same pipeline: a ring of LDS stages filled by direct
-// global->LDS loads issued NS-1 stages ahead.  At the top of every iteration
-// each wave waits until its loads of the current stage have landed (the
-// newer stages stay in flight), a barrier publishes the stage to all waves,
-// the buffer freed by the previous stage is refilled, and the stage is
-// multiplied out.  Loads past the end read zeros through out-of-range
-// offsets, so every stage issues the same number of loads.
+// Both products run the same pipeline, split between two kinds of wave.  The
+// four loader waves only issue direct global->LDS loads; the four multiplier
+// waves only read LDS and issue MFMAs.  Each SIMD holds one wave of each kind,
+// so a loader stalled on the address unit never holds back the matrix core.
+// The LDS ring holds NS stages; the loaders run NS-1 stages ahead.  At the top
+// of every iteration the loaders wait until their loads of the current stage
+// have landed, one barrier publishes the stage and releases the buffer read in
+// the previous iteration, then the loaders refill that buffer while the
+// multipliers work on the current one.  Loads past the end of K are never
+// issued; the last iterations wait for every load still in flight instead.
 template <int C, bool kGrouped>
 __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a) {
     using Cfg = FusedCfg<C>;
@@ -129,7 +149,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool loader = wave >= kMulWaves;   // wave-uniform role
+    const int w4 = wave & (kMulWaves - 1);   // index within the role
     const int li = lane & 15;   // fragment index
     const int lg = lane >> 4;   // fragment k-group
 
@@ -159,121 +181,155 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     const int64_t o0 = (int64_t)s * C;
     const int64_t oc = (O - o0) < C ? (O - o0) : C;  // valid hidden columns of this chunk
 
-    // ---- X slab loads: wave w fills fragment w (rows 16w..16w+15); lane l
-    // brings row 16w + l%16, k-group l/16, straight into fragment slot l.
-    const int xr = 16 * wave + li;
+    // ---- X slab loads: loader w fills fragment w (rows 16w..16w+15); lane l
+    // brings row 16w + l/4, k-group xc into fragment slot l (see xfrag_slot).
+    const int xr = 16 * w4 + (lane >> 2);
+    const int xc = (lane & 3) ^ ((lane >> 3) & 3);
     int32x4_t rx;
     uint32_t xrow_off = kOOB;
     if constexpr (kGrouped) {
         rx = make_srd(a.X, a.M * N * 2);
-        if (xr < valid) xrow_off = (uint32_t)((a.g.sorted[row0 + xr] / a.g.k) * N * 2);
+        if (loader && xr < valid) xrow_off = (uint32_t)((a.g.sorted[row0 + xr] / a.g.k) * N * 2);
     } else {
         rx = make_srd(a.X + row0 * N, (int64_t)valid * N * 2);
         if (xr < valid) xrow_off = (uint32_t)(xr * N * 2);
     }
-    // ---- weight loads: lane l brings k-row wtile_dma_row(l), column group l/8.
+    // ---- weight loads: lane l brings slot l of a block (see wtile_dma_off).
     // The W1 resource ends at the end of W1, so rows past N read zeros; columns
     // past this chunk's valid width read finite neighbours whose H columns the
     // epilogue forces to zero.
     const int32x4_t rw1 = make_srd(W1 + o0, (N * O - o0) * 2);
-    const uint32_t w1_lane = (uint32_t)wtile_dma_row(lane) * (uint32_t)(O * 2) + 16u * (lane >> 3);
+    const uint32_t w1_lane = wtile_dma_off(lane, (uint32_t)(O * 2));
 
-    // one W1 block (8 k-rows x 64 columns) of stage kt, block index blk
-    auto dma_w1 = [&](int64_t kt, int buf, int blk) {
-        char* sw = smem + buf * Cfg::kStage1 + kSub;
-        const int r = blk / Cfg::kNB1, c = blk % Cfg::kNB1;
-        const uint32_t base = (uint32_t)(((kt * kBK + 8 * r) * O + 64 * c) * 2);
-        dma16(rw1, base + w1_lane, sw + blk * kFrag);
-    };
-    auto dma_x = [&](int64_t kt, int buf) {
-        const int64_t kx = kt * kBK + 8 * lg;
-        dma16(rx, kx < N ? xrow_off + (uint32_t)(kx * 2) : kOOB, smem + buf * Cfg::kStage1 + wave * kFrag);
-    };
-    auto issue1 = [&](int64_t kt, int buf) {
-        dma_x(kt, buf);
+    const int64_t nk = (N + kBK - 1) / kBK;
+
+    // W2 stage: 32 hidden rows x 512 output columns.  The W2 resource covers
+    // exactly this chunk's rows, so rows past the chunk read zeros; columns
+    // past P read finite neighbours that reach only unstored partial columns.
+    const int64_t np = (P + kBN2 - 1) / kBN2;
+    const int64_t nsteps = np * Cfg::kKS;   // GEMM2 stages; the ring runs across passes
+    // Staggered stage order.  The workgroups of one XCD share the weight chunk;
+    // walking it in the same order they would all request the same lines at
+    // the same moment and queue on the same L2 channels.  Workgroup j of the
+    // XCD starts instead at K stage j (wrapping) and at W2 stage (j, j) of the
+    // (pass, k) grid, so at any moment they read different stages.
+    const int64_t jx = blockIdx.x >> 3;
+    const int64_t rot1 = jx % nk;
+    const int64_t rotp = jx % np;
+    const int rotk = (int)(jx % Cfg::kKS);
+    char* const hreg = smem;
+    char* const w2reg = smem + Cfg::kHBytes;
+    const int32x4_t rw2 = make_srd(W2 + o0 * P, oc * P * 2);
+
+    // The two roles run separate loops that execute the same number of
+    // barriers: nk for GEMM1, one between the products, nsteps for GEMM2.
+    if (loader) {
+        // =================== loads of GEMM1 (X slab + W1 chunk) =============
+        auto issue1 = [&](int64_t kt, int buf) {
+            char* st = smem + buf * Cfg::kStage1;
+            const int64_t kx = kt * kBK + 8 * xc;
+            dma16(rx, kx < N ? xrow_off + (uint32_t)(kx * 2) : kOOB, st + w4 * kFrag);
 #pragma unroll
-        for (int i = 0; i < Cfg::kNB1; ++i) dma_w1(kt, buf, wave + 4 * i);
-    };
+            for (int i = 0; i < Cfg::kNB1; ++i) {
+                const int blk = w4 + kMulWaves * i;
+                const int r = blk / Cfg::kNB1, c = blk % Cfg::kNB1;
+                const uint32_t base = (uint32_t)(((kt * kBK + 8 * r) * O + 64 * c) * 2);
+                dma16(rw1, base + w1_lane, st + kSub + blk * kFrag);
+            }
+        };
+#pragma unroll
+        for (int i = 0; i < Cfg::kNS1 - 1; ++i)
+            if (i < nk) issue1(i + rot1 < nk ? i + rot1 : i + rot1 - nk, i);
+        int ibuf = Cfg::kNS1 - 1;
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            // stages kt .. min(kt + NS1 - 2, nk - 1) are in flight
+            if (kt + Cfg::kNS1 - 2 < nk) wait_vmcnt<Cfg::kD1 * (Cfg::kNS1 - 2)>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+            if (kt + Cfg::kNS1 - 1 < nk) {
+                const int64_t kl = kt + Cfg::kNS1 - 1 + rot1;
+                issue1(kl < nk ? kl : kl - nk, ibuf);
+            }
+            ibuf = (ibuf + 1 == Cfg::kNS1) ? 0 : ibuf + 1;
+        }
+        __syncthreads();   // the multipliers are done with the GEMM1 ring
 
+        // =================== loads of GEMM2 (W2 chunk) ======================
+        const uint32_t w2_lane =
+            wtile_dma_off(lane, (uint32_t)(P * 2));
+        auto issue2 = [&](int64_t step) {
+            const int64_t pr = step / Cfg::kKS;
+            const int kr = (int)(step - pr * Cfg::kKS);
+            const int64_t pt = pr + rotp < np ? pr + rotp : pr + rotp - np;
+            const int ks = kr + rotk < Cfg::kKS ? kr + rotk : kr + rotk - Cfg::kKS;
+            char* st = w2reg + (int)(step % Cfg::kNS2) * Cfg::kStage2;
+#pragma unroll
+            for (int i = 0; i < Cfg::kNB2; ++i) {
+                const int blk = w4 + kMulWaves * i;
+                const int r = blk / Cfg::kNB2, c = blk % Cfg::kNB2;
+                const uint32_t base =
+                    (uint32_t)(((int64_t)(ks * kBK + 8 * r) * P + pt * kBN2 + 64 * c) * 2);
+                dma16(rw2, base + w2_lane, st + blk * kFrag);
+            }
+        };
+        // the first W2 stages do not depend on H: they load during the epilogue
+#pragma unroll
+        for (int i = 0; i < Cfg::kNS2 - 1; ++i)
+            if (i < nsteps) issue2(i);
+        for (int64_t step = 0; step < nsteps; ++step) {
+            if (step + Cfg::kNS2 - 2 < nsteps) wait_vmcnt<Cfg::kD2 * (Cfg::kNS2 - 2)>();
+            else wait_vmcnt<0>();
+            __syncthreads();
+            if (step + Cfg::kNS2 - 1 < nsteps) issue2(step + Cfg::kNS2 - 1);
+        }
+        // the last iterations waited for every load: none outlives the workgroup
+        return;
+    }
+
+    // ======================= GEMM1: A^T = W1_chunk^T X^T ===================
     floatx4_t acc[Cfg::kFO][4];
 #pragma unroll
     for (int i = 0; i < Cfg::kFO; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-    const uint32_t trw1_0 = wtile_tr_off(lane, Cfg::kNB1, wave * Cfg::kFO, 0);
-    const uint32_t trw1_1 = wtile_tr_off(lane, Cfg::kNB1, wave * Cfg::kFO, 1);
-    // Multiply stage `buf` out of LDS while issuing the loads of stage kt_next
-    // into buffer `nbuf`: one load after each fragment's four MFMAs, so that a
-    // load waiting for the address unit never holds back a long run of MFMAs.
-    auto step1 = [&](int buf, int64_t kt_next, int nbuf) {
-        const char* st = smem + buf * Cfg::kStage1;
-        const char* sw = st + kSub;
-        uint4 bx[4], aw[Cfg::kFO];
+    {
+        const int xoff = 16 * xfrag_slot(li, lg);
+        uint32_t trw1[Cfg::kFO][2];   // per-fragment read offsets (the swizzle is not linear in f)
 #pragma unroll
-        for (int fm = 0; fm < 4; ++fm) bx[fm] = ld16(st + fm * kFrag + 16 * lane);
+        for (int fo = 0; fo < Cfg::kFO; ++fo)
 #pragma unroll
-        for (int fo = 0; fo < Cfg::kFO; ++fo) {
-            // fragment offsets are linear in f: 256 bytes per 16 columns
-            const uint2 lo = lds_read_tr16(sw + trw1_0 + 256 * fo);
-            const uint2 hi = lds_read_tr16(sw + trw1_1 + 256 * fo);
-            aw[fo] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-        }
+            for (int t = 0; t < 2; ++t) trw1[fo][t] = wtile_tr_off(lane, Cfg::kNB1, w4 * Cfg::kFO + fo, t);
+        int cbuf = 0;
+        for (int64_t kt = 0; kt < nk; ++kt) {
+            __syncthreads();
+            // 4 row fragments x kFO hidden fragments of stage `cbuf`
+            const char* st = smem + cbuf * Cfg::kStage1;
+            const char* sw = st + kSub;
+            uint4 bx[4], aw[Cfg::kFO];
 #pragma unroll
-        for (int fo = 0; fo < Cfg::kFO; ++fo) {
+            for (int fm = 0; fm < 4; ++fm) bx[fm] = ld16(st + fm * kFrag + xoff);
 #pragma unroll
-            for (int fm = 0; fm < 4; ++fm) acc[fo][fm] = mfma16x16x32(aw[fo], bx[fm], acc[fo][fm]);
+            for (int fo = 0; fo < Cfg::kFO; ++fo) {
+                const uint2 lo = lds_read_tr16(sw + trw1[fo][0]);
+                const uint2 hi = lds_read_tr16(sw + trw1[fo][1]);
+                aw[fo] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            }
+            // every read of the stage is in flight before the first MFMA waits
             __builtin_amdgcn_sched_barrier(0);
-            if (fo < Cfg::kNB1) dma_w1(kt_next, nbuf, wave + 4 * fo);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        dma_x(kt_next, nbuf);
-    };
-
-    // =========================== GEMM1: A^T = W1_chunk^T X^T ===============
-    const int64_t nk = (N + kBK - 1) / kBK;
 #pragma unroll
-    for (int i = 0; i < Cfg::kNS1 - 1; ++i) issue1(i, i);
-    int cbuf = 0, ibuf = Cfg::kNS1 - 1;
-    for (int64_t kt = 0; kt < nk; ++kt) {
-        wait_vmcnt<Cfg::kD1 * (Cfg::kNS1 - 2)>();
-        __syncthreads();
-        step1(cbuf, kt + Cfg::kNS1 - 1, ibuf);
-        cbuf = (cbuf + 1 == Cfg::kNS1) ? 0 : cbuf + 1;
-        ibuf = (ibuf + 1 == Cfg::kNS1) ? 0 : ibuf + 1;
+            for (int fo = 0; fo < Cfg::kFO; ++fo)
+#pragma unroll
+                for (int fm = 0; fm < 4; ++fm)
+                    acc[fo][fm] = mfma16x16x32(aw[fo], bx[fm], acc[fo][fm]);
+            cbuf = (cbuf + 1 == Cfg::kNS1) ? 0 : cbuf + 1;
+        }
     }
-    wait_vmcnt<0>();   // the stages loaded past the end still write LDS
-    __syncthreads();
-
-    // =========================== GEMM2 setup ==============================
-    // W2 stage: 32 hidden rows x 512 output columns.  The W2 resource covers
-    // exactly this chunk's rows, so rows past the chunk read zeros; columns
-    // past P read finite neighbours that reach only unstored partial columns.
-    const int32x4_t rw2 = make_srd(W2 + o0 * P, oc * P * 2);
-    const uint32_t w2_lane = (uint32_t)wtile_dma_row(lane) * (uint32_t)(P * 2) + 16u * (lane >> 3);
-    const int64_t np = (P + kBN2 - 1) / kBN2;
-    char* const w2reg = smem + Cfg::kHBytes;
-    auto dma_w2 = [&](int64_t step, int blk) {
-        const int64_t pt = step / Cfg::kKS;
-        const int ks = (int)(step - pt * Cfg::kKS);
-        char* st = w2reg + (int)(step % Cfg::kNS2) * Cfg::kStage2;
-        const int r = blk / Cfg::kNB2, c = blk % Cfg::kNB2;
-        const uint32_t base = (uint32_t)(((int64_t)(ks * kBK + 8 * r) * P + pt * kBN2 + 64 * c) * 2);
-        dma16(rw2, base + w2_lane, st + blk * kFrag);
-    };
-    auto issue2 = [&](int64_t step) {
-#pragma unroll
-        for (int i = 0; i < Cfg::kNB2; ++i) dma_w2(step, wave + 4 * i);
-    };
-    // the first W2 stages do not depend on H: start them before the epilogue
-#pragma unroll
-    for (int i = 0; i < Cfg::kNS2 - 1; ++i) issue2(i);
+    __syncthreads();   // every multiplier is done with the GEMM1 ring
 
     // ---- epilogue 1: H = act(A + b1) -> bf16 -> LDS (GEMM2 operand layout)
-    char* const hreg = smem;
 #pragma unroll
     for (int fo = 0; fo < Cfg::kFO; ++fo) {
-        const int ol = 16 * (wave * Cfg::kFO + fo) + 4 * lg;  // first of 4 hidden cols
+        const int ol = 16 * (w4 * Cfg::kFO + fo) + 4 * lg;  // first of 4 hidden cols
         const int64_t og = o0 + ol;
         float bias[4] = {0.f, 0.f, 0.f, 0.f};
         const bool colok = og < O;  // O % 8 == 0, so the 4 columns are all in or all out
@@ -298,60 +354,64 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
         }
     }
 
-    // =========================== GEMM2: Ypart^T = W2_chunk^T H^T ==========
+    // ======================= GEMM2: Ypart^T = W2_chunk^T H^T ===============
     floatx4_t acc2[8][4];
 #pragma unroll
     for (int i = 0; i < 8; ++i)
 #pragma unroll
         for (int j = 0; j < 4; ++j) acc2[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-    const uint32_t trw2_0 = wtile_tr_off(lane, Cfg::kNB2, 8 * wave, 0);
-    const uint32_t trw2_1 = wtile_tr_off(lane, Cfg::kNB2, 8 * wave, 1);
-    float* const part = a.part + (int64_t)s * a.rows_out * P;
-    int64_t step = 0;   // global stage counter; the load ring runs across passes
+    uint32_t trw2[8][2];
+#pragma unroll
+    for (int fp = 0; fp < 8; ++fp)
+#pragma unroll
+        for (int t = 0; t < 2; ++t) trw2[fp][t] = wtile_tr_off(lane, Cfg::kNB2, 8 * w4 + fp, t);
+    // lane's partial rows: 16 fm + li; columns pass * 512 + 128 w4 + 16 fp + 4 lg
+    float* const part = a.part + (int64_t)s * a.rows_out * P + (row0 + 4 * lg) * P + 128 * w4 + li;
+    int sbuf = 0;
     for (int64_t pt = 0; pt < np; ++pt) {
-#pragma unroll 2
-        for (int ks = 0; ks < Cfg::kKS; ++ks, ++step) {
-            wait_vmcnt<Cfg::kD2 * (Cfg::kNS2 - 2)>();
-            __syncthreads();
-            const char* sw = w2reg + (int)(step % Cfg::kNS2) * Cfg::kStage2;
-            const char* hs = hreg + ks * kSub;
+        for (int ks = 0; ks < Cfg::kKS; ++ks) {
+            __syncthreads();   // (the first one also publishes H)
+            const char* sw = w2reg + sbuf * Cfg::kStage2;
+            const int kr = ks + rotk < Cfg::kKS ? ks + rotk : ks + rotk - Cfg::kKS;
+            const char* hs = hreg + kr * kSub;
             uint4 bh[4], aw[8];
 #pragma unroll
             for (int fm = 0; fm < 4; ++fm) bh[fm] = ld16(hs + frag_off(16 * fm + li, lg));
 #pragma unroll
             for (int fp = 0; fp < 8; ++fp) {
-                const uint2 lo = lds_read_tr16(sw + trw2_0 + 256 * fp);
-                const uint2 hi = lds_read_tr16(sw + trw2_1 + 256 * fp);
+                const uint2 lo = lds_read_tr16(sw + trw2[fp][0]);
+                const uint2 hi = lds_read_tr16(sw + trw2[fp][1]);
                 aw[fp] = make_uint4(lo.x, lo.y, hi.x, hi.y);
             }
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int fp = 0; fp < 8; ++fp) {
+            for (int fp = 0; fp < 8; ++fp)
 #pragma unroll
                 for (int fm = 0; fm < 4; ++fm)
-                    acc2[fp][fm] = mfma16x16x32(aw[fp], bh[fm], acc2[fp][fm]);
-                __builtin_amdgcn_sched_barrier(0);
-                dma_w2(step + Cfg::kNS2 - 1, wave + 4 * fp);  // kNB2 == 8 loads per stage
-                __builtin_amdgcn_sched_barrier(0);
-            }
+                    acc2[fp][fm] = mfma16x16x32(bh[fm], aw[fp], acc2[fp][fm]);
+            sbuf = (sbuf + 1 == Cfg::kNS2) ? 0 : sbuf + 1;
         }
-        // this pass's partial: lane holds 4 consecutive columns of row m
+        // this pass's partial.  H is the first MFMA operand, so lane (li, lg)
+        // holds rows 16 fm + 4 lg + r (r = 0..3) of column 16 fp + li: each
+        // store writes 64 contiguous bytes of a row per 16 lanes.
+        const int64_t pr = pt + rotp < np ? pt + rotp : pt + rotp - np;   // pass stored
+        const int64_t pl = pr * kBN2 + 128 * w4 + li;                     // column, fp = 0
 #pragma unroll
-        for (int fp = 0; fp < 8; ++fp) {
-            const int64_t p = pt * kBN2 + 128 * wave + 16 * fp + 4 * lg;
+        for (int fm = 0; fm < 4; ++fm) {
 #pragma unroll
-            for (int fm = 0; fm < 4; ++fm) {
-                const int m = 16 * fm + li;
-                if (m < valid && p < P) {
-                    // streaming store: the partial is read once, by the reduction pass
-                    floatx4_t* dst = reinterpret_cast<floatx4_t*>(part + (row0 + m) * P + p);
-                    __builtin_nontemporal_store(acc2[fp][fm], dst);
+            for (int r = 0; r < 4; ++r) {
+                if (16 * fm + 4 * lg + r < valid) {
+                    float* rowp = part + (int64_t)(16 * fm + r) * P + pr * kBN2;
+#pragma unroll
+                    for (int fp = 0; fp < 8; ++fp)   // streaming: read once, by the reduction
+                        if (pl + 16 * fp < P) __builtin_nontemporal_store(acc2[fp][fm][r], rowp + 16 * fp);
                 }
-                acc2[fp][fm] = floatx4_t{0.f, 0.f, 0.f, 0.f};
             }
+#pragma unroll
+            for (int fp = 0; fp < 8; ++fp) acc2[fp][fm] = floatx4_t{0.f, 0.f, 0.f, 0.f};
         }
     }
-    wait_vmcnt<0>();   // no load into LDS may outlive the workgroup
 }
 
 // ---------------------------------------------------------------- reduce
