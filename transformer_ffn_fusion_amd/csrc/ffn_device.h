@@ -106,6 +106,25 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&rows)[8], uint4 (&col
     for (int j = 0; j < 8; ++j) cols[j] = make_uint4(c[j][0], c[j][1], c[j][2], c[j][3]);
 }
 
+// rows[e] holds 4 bf16 (columns 0..3) of row e.  On return cols[j] holds the
+// 8 bf16 of column j, rows 0..7 in order.
+__device__ __forceinline__ void transpose8x4(const uint2 (&rows)[8], uint4 (&cols)[4]) {
+    const uint32_t LO = 0x05040100u;
+    const uint32_t HI = 0x07060302u;
+    uint32_t c[4][4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint2 a = rows[2 * q];
+        const uint2 b = rows[2 * q + 1];
+        c[0][q] = __builtin_amdgcn_perm(b.x, a.x, LO);
+        c[1][q] = __builtin_amdgcn_perm(b.x, a.x, HI);
+        c[2][q] = __builtin_amdgcn_perm(b.y, a.y, LO);
+        c[3][q] = __builtin_amdgcn_perm(b.y, a.y, HI);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) cols[j] = make_uint4(c[j][0], c[j][1], c[j][2], c[j][3]);
+}
+
 __device__ __forceinline__ uint4 ld16(const void* p) { return *reinterpret_cast<const uint4*>(p); }
 
 // ---------------------------------------------------------------- LDS transposing read
@@ -141,6 +160,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, in
 
 __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
     return __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0));
+}
+__device__ __forceinline__ uint2 bload8(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+    return __builtin_bit_cast(uint2, __builtin_amdgcn_raw_buffer_load_b64(r, byte_off, 0, 0));
 }
 
 // Direct global -> LDS load: lane l's 16 bytes land at lds_base + 16*l

@@ -76,24 +76,20 @@ __device__ __forceinline__ int xfrag_slot(int r, int c) { return 4 * r + (c ^ ((
 
 template <int C>
 struct FusedCfg {
-    static constexpr int kFO = C / 64;                 // hidden fragments per wave
+    static constexpr int kFO = C / 64;                 // hidden fragments per multiplier wave
     static constexpr int kNB1 = C / 64;                // W1 stage: 64-column blocks per row group
-    static constexpr int kNB2 = kBN2 / 64;             // W2 stage: 8
     static constexpr int kKS = C / kBK;                // GEMM2 k-stages per output pass
     static constexpr int kW1Stage = 4 * kNB1 * kFrag;  // 32 x C bf16
     static constexpr int kStage1 = kSub + kW1Stage;    // X slab + W1 slab
-    static constexpr int kStage2 = 4 * kNB2 * kFrag;   // 32 x 512 bf16 = 32 KiB
     static constexpr int kHBytes = kKS * kSub;         // H: C/32 slabs of 64 x 32
     static constexpr int kNS1 = 4;                     // GEMM1 stages in flight
-    static constexpr int kNS2 = (kHBytes + 3 * kStage2 <= 152 * 1024) ? 3 : 2;
-    static constexpr int kD1 = 1 + kNB1;               // DMA instructions per wave per GEMM1 stage
-    static constexpr int kD2 = kNB2;                   // ... per GEMM2 stage
+    static constexpr int kD1 = 1 + kNB1;               // loads per loader wave per GEMM1 stage
     static constexpr int kLds1 = kNS1 * kStage1;
-    static constexpr int kLds2 = kHBytes + kNS2 * kStage2;
-    static constexpr int kLds = kLds1 > kLds2 ? kLds1 : kLds2;
-    static_assert(C % 64 == 0 && (4 * kNB1) % 4 == 0, "chunk must split over four waves");
+    static constexpr int kLds = kLds1 > kHBytes ? kLds1 : kHBytes;
+    static_assert(C % 64 == 0, "chunk must split over four waves");
+    static_assert(kKS % 2 == 0, "GEMM2 runs its stages in pairs");
+    static_assert(kBN2 == 64 * 2 * kMulWaves, "each of the eight waves owns 64 columns of a pass");
     static_assert(kLds <= 160 * 1024, "LDS budget");
-    static_assert(kNB1 <= kFO && kNB2 == 8, "one load slot per fragment");
 };
 
 struct FusedArgs {
@@ -218,8 +214,6 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     const int64_t rotp = jx % np;
     const int rotk = (int)(jx % Cfg::kKS);
     char* const hreg = smem;
-    char* const w2reg = smem + Cfg::kHBytes;
-    const int32x4_t rw2 = make_srd(W2 + o0 * P, oc * P * 2);
 
     // The two roles run separate loops that execute the same number of
     // barriers: nk for GEMM1, one between the products, nsteps for GEMM2.
@@ -253,164 +247,154 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
             ibuf = (ibuf + 1 == Cfg::kNS1) ? 0 : ibuf + 1;
         }
         __syncthreads();   // the multipliers are done with the GEMM1 ring
-
-        // =================== loads of GEMM2 (W2 chunk) ======================
-        const uint32_t w2_lane =
-            wtile_dma_off(lane, (uint32_t)(P * 2));
-        auto issue2 = [&](int64_t step) {
-            const int64_t pr = step / Cfg::kKS;
-            const int kr = (int)(step - pr * Cfg::kKS);
-            const int64_t pt = pr + rotp < np ? pr + rotp : pr + rotp - np;
-            const int ks = kr + rotk < Cfg::kKS ? kr + rotk : kr + rotk - Cfg::kKS;
-            char* st = w2reg + (int)(step % Cfg::kNS2) * Cfg::kStage2;
+    } else {
+        // ======================= GEMM1: A^T = W1_chunk^T X^T ===================
+        floatx4_t acc[Cfg::kFO][4];
 #pragma unroll
-            for (int i = 0; i < Cfg::kNB2; ++i) {
-                const int blk = w4 + kMulWaves * i;
-                const int r = blk / Cfg::kNB2, c = blk % Cfg::kNB2;
-                const uint32_t base =
-                    (uint32_t)(((int64_t)(ks * kBK + 8 * r) * P + pt * kBN2 + 64 * c) * 2);
-                dma16(rw2, base + w2_lane, st + blk * kFrag);
-            }
-        };
-        // the first W2 stages do not depend on H: they load during the epilogue
+        for (int i = 0; i < Cfg::kFO; ++i)
 #pragma unroll
-        for (int i = 0; i < Cfg::kNS2 - 1; ++i)
-            if (i < nsteps) issue2(i);
-        for (int64_t step = 0; step < nsteps; ++step) {
-            if (step + Cfg::kNS2 - 2 < nsteps) wait_vmcnt<Cfg::kD2 * (Cfg::kNS2 - 2)>();
-            else wait_vmcnt<0>();
-            __syncthreads();
-            if (step + Cfg::kNS2 - 1 < nsteps) issue2(step + Cfg::kNS2 - 1);
-        }
-        // the last iterations waited for every load: none outlives the workgroup
-        return;
-    }
-
-    // ======================= GEMM1: A^T = W1_chunk^T X^T ===================
-    floatx4_t acc[Cfg::kFO][4];
-#pragma unroll
-    for (int i = 0; i < Cfg::kFO; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-    {
-        const int xoff = 16 * xfrag_slot(li, lg);
-        uint32_t trw1[Cfg::kFO][2];   // per-fragment read offsets (the swizzle is not linear in f)
-#pragma unroll
-        for (int fo = 0; fo < Cfg::kFO; ++fo)
-#pragma unroll
-            for (int t = 0; t < 2; ++t) trw1[fo][t] = wtile_tr_off(lane, Cfg::kNB1, w4 * Cfg::kFO + fo, t);
-        int cbuf = 0;
-        for (int64_t kt = 0; kt < nk; ++kt) {
-            __syncthreads();
-            // 4 row fragments x kFO hidden fragments of stage `cbuf`
-            const char* st = smem + cbuf * Cfg::kStage1;
-            const char* sw = st + kSub;
-            uint4 bx[4], aw[Cfg::kFO];
-#pragma unroll
-            for (int fm = 0; fm < 4; ++fm) bx[fm] = ld16(st + fm * kFrag + xoff);
-#pragma unroll
-            for (int fo = 0; fo < Cfg::kFO; ++fo) {
-                const uint2 lo = lds_read_tr16(sw + trw1[fo][0]);
-                const uint2 hi = lds_read_tr16(sw + trw1[fo][1]);
-                aw[fo] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            }
-            // every read of the stage is in flight before the first MFMA waits
-            __builtin_amdgcn_sched_barrier(0);
+            for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        {
+            const int xoff = 16 * xfrag_slot(li, lg);
+            uint32_t trw1[Cfg::kFO][2];   // per-fragment read offsets (the swizzle is not linear in f)
 #pragma unroll
             for (int fo = 0; fo < Cfg::kFO; ++fo)
 #pragma unroll
-                for (int fm = 0; fm < 4; ++fm)
-                    acc[fo][fm] = mfma16x16x32(aw[fo], bx[fm], acc[fo][fm]);
-            cbuf = (cbuf + 1 == Cfg::kNS1) ? 0 : cbuf + 1;
-        }
-    }
-    __syncthreads();   // every multiplier is done with the GEMM1 ring
-
-    // ---- epilogue 1: H = act(A + b1) -> bf16 -> LDS (GEMM2 operand layout)
+                for (int t = 0; t < 2; ++t) trw1[fo][t] = wtile_tr_off(lane, Cfg::kNB1, w4 * Cfg::kFO + fo, t);
+            int cbuf = 0;
+            for (int64_t kt = 0; kt < nk; ++kt) {
+                __syncthreads();
+                // 4 row fragments x kFO hidden fragments of stage `cbuf`
+                const char* st = smem + cbuf * Cfg::kStage1;
+                const char* sw = st + kSub;
+                uint4 bx[4], aw[Cfg::kFO];
 #pragma unroll
-    for (int fo = 0; fo < Cfg::kFO; ++fo) {
-        const int ol = 16 * (w4 * Cfg::kFO + fo) + 4 * lg;  // first of 4 hidden cols
-        const int64_t og = o0 + ol;
-        float bias[4] = {0.f, 0.f, 0.f, 0.f};
-        const bool colok = og < O;  // O % 8 == 0, so the 4 columns are all in or all out
-        if (colok && b1) {
-            uint2 bb = *reinterpret_cast<const uint2*>(b1 + og);
-            bias[0] = bf16_lo(bb.x);
-            bias[1] = bf16_hi(bb.x);
-            bias[2] = bf16_lo(bb.y);
-            bias[3] = bf16_hi(bb.y);
-        }
-        const int slab = ol / 32;
-        const int g = (ol % 32) / 8;
-        const int e = ol % 8;
+                for (int fm = 0; fm < 4; ++fm) bx[fm] = ld16(st + fm * kFrag + xoff);
 #pragma unroll
-        for (int fm = 0; fm < 4; ++fm) {
-            float h[4];
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                h[r] = colok ? apply_act(a.act1, acc[fo][fm][r] + bias[r]) : 0.f;
-            uint2 pk = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-            *reinterpret_cast<uint2*>(hreg + slab * kSub + frag_off(16 * fm + li, g) + 2 * e) = pk;
-        }
-    }
-
-    // ======================= GEMM2: Ypart^T = W2_chunk^T H^T ===============
-    floatx4_t acc2[8][4];
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc2[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-    uint32_t trw2[8][2];
-#pragma unroll
-    for (int fp = 0; fp < 8; ++fp)
-#pragma unroll
-        for (int t = 0; t < 2; ++t) trw2[fp][t] = wtile_tr_off(lane, Cfg::kNB2, 8 * w4 + fp, t);
-    // lane's partial rows: 16 fm + li; columns pass * 512 + 128 w4 + 16 fp + 4 lg
-    float* const part = a.part + (int64_t)s * a.rows_out * P + (row0 + 4 * lg) * P + 128 * w4 + li;
-    int sbuf = 0;
-    for (int64_t pt = 0; pt < np; ++pt) {
-        for (int ks = 0; ks < Cfg::kKS; ++ks) {
-            __syncthreads();   // (the first one also publishes H)
-            const char* sw = w2reg + sbuf * Cfg::kStage2;
-            const int kr = ks + rotk < Cfg::kKS ? ks + rotk : ks + rotk - Cfg::kKS;
-            const char* hs = hreg + kr * kSub;
-            uint4 bh[4], aw[8];
-#pragma unroll
-            for (int fm = 0; fm < 4; ++fm) bh[fm] = ld16(hs + frag_off(16 * fm + li, lg));
-#pragma unroll
-            for (int fp = 0; fp < 8; ++fp) {
-                const uint2 lo = lds_read_tr16(sw + trw2[fp][0]);
-                const uint2 hi = lds_read_tr16(sw + trw2[fp][1]);
-                aw[fp] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-            }
-            __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-            for (int fp = 0; fp < 8; ++fp)
-#pragma unroll
-                for (int fm = 0; fm < 4; ++fm)
-                    acc2[fp][fm] = mfma16x16x32(bh[fm], aw[fp], acc2[fp][fm]);
-            sbuf = (sbuf + 1 == Cfg::kNS2) ? 0 : sbuf + 1;
-        }
-        // this pass's partial.  H is the first MFMA operand, so lane (li, lg)
-        // holds rows 16 fm + 4 lg + r (r = 0..3) of column 16 fp + li: each
-        // store writes 64 contiguous bytes of a row per 16 lanes.
-        const int64_t pr = pt + rotp < np ? pt + rotp : pt + rotp - np;   // pass stored
-        const int64_t pl = pr * kBN2 + 128 * w4 + li;                     // column, fp = 0
-#pragma unroll
-        for (int fm = 0; fm < 4; ++fm) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                if (16 * fm + 4 * lg + r < valid) {
-                    float* rowp = part + (int64_t)(16 * fm + r) * P + pr * kBN2;
-#pragma unroll
-                    for (int fp = 0; fp < 8; ++fp)   // streaming: read once, by the reduction
-                        if (pl + 16 * fp < P) __builtin_nontemporal_store(acc2[fp][fm][r], rowp + 16 * fp);
+                for (int fo = 0; fo < Cfg::kFO; ++fo) {
+                    const uint2 lo = lds_read_tr16(sw + trw1[fo][0]);
+                    const uint2 hi = lds_read_tr16(sw + trw1[fo][1]);
+                    aw[fo] = make_uint4(lo.x, lo.y, hi.x, hi.y);
                 }
-            }
+                // every read of the stage is in flight before the first MFMA waits
+                __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int fp = 0; fp < 8; ++fp) acc2[fp][fm] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+                for (int fo = 0; fo < Cfg::kFO; ++fo)
+#pragma unroll
+                    for (int fm = 0; fm < 4; ++fm)
+                        acc[fo][fm] = mfma16x16x32(aw[fo], bx[fm], acc[fo][fm]);
+                cbuf = (cbuf + 1 == Cfg::kNS1) ? 0 : cbuf + 1;
+            }
         }
+        __syncthreads();   // every multiplier is done with the GEMM1 ring
+
+        // ---- epilogue 1: H = act(A + b1) -> bf16 -> LDS (GEMM2 operand layout)
+#pragma unroll
+        for (int fo = 0; fo < Cfg::kFO; ++fo) {
+            const int ol = 16 * (w4 * Cfg::kFO + fo) + 4 * lg;  // first of 4 hidden cols
+            const int64_t og = o0 + ol;
+            float bias[4] = {0.f, 0.f, 0.f, 0.f};
+            const bool colok = og < O;  // O % 8 == 0, so the 4 columns are all in or all out
+            if (colok && b1) {
+                uint2 bb = *reinterpret_cast<const uint2*>(b1 + og);
+                bias[0] = bf16_lo(bb.x);
+                bias[1] = bf16_hi(bb.x);
+                bias[2] = bf16_lo(bb.y);
+                bias[3] = bf16_hi(bb.y);
+            }
+            const int slab = ol / 32;
+            const int g = (ol % 32) / 8;
+            const int e = ol % 8;
+#pragma unroll
+            for (int fm = 0; fm < 4; ++fm) {
+                float h[4];
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    h[r] = colok ? apply_act(a.act1, acc[fo][fm][r] + bias[r]) : 0.f;
+                uint2 pk = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+                *reinterpret_cast<uint2*>(hreg + slab * kSub + frag_off(16 * fm + li, g) + 2 * e) = pk;
+            }
+        }
+    }
+    __syncthreads();   // H is complete
+
+    // ======================= GEMM2: Y_part = H W2_chunk =====================
+    // All eight waves.  Wave w owns columns 64w .. 64w+63 of every 512-column
+    // pass and streams its own W2 columns straight into registers -- no LDS
+    // staging and no barriers.  Lane (i, g) loads, for each k-row 8g..8g+7 of
+    // a stage, the four columns 4i..4i+3 (8 bytes: the 16 lanes of a k-group
+    // read 128 contiguous bytes of a row).  Eight rows x four columns are
+    // transposed in registers into four k-contiguous operands; operand j,
+    // index i stands for column 4i + j.  H is the first MFMA operand, so lane
+    // (i, g) ends up with rows 16 fm + 4g + r of the four consecutive columns
+    // 4i..4i+3 and stores them as one 16-byte write.
+    const int wc = wave;
+    const __amdgpu_buffer_rsrc_t rw2 = make_rsrc(W2 + o0 * P, oc * P * 2);
+    const uint32_t w2_lane = (uint32_t)(8 * lg) * (uint32_t)(P * 2) + (uint32_t)(64 * wc + 4 * li) * 2u;
+    // loads of stage `step` into R; a step past the end reads zeros (out of
+    // range), so that every stage refills its registers unconditionally
+    auto load2 = [&](int64_t step, uint2 (&R)[8]) {
+        const int64_t pr = step / Cfg::kKS;
+        const int kr = (int)(step - pr * Cfg::kKS);
+        const int64_t pt = pr + rotp < np ? pr + rotp : pr + rotp - np;
+        const int ks = kr + rotk < Cfg::kKS ? kr + rotk : kr + rotk - Cfg::kKS;
+        const uint32_t base = step < nsteps
+            ? (uint32_t)(((int64_t)ks * kBK * P + pt * kBN2) * 2) + w2_lane : kOOB;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) R[e] = bload8(rw2, base + (uint32_t)(e * P * 2));
+    };
+
+    floatx4_t acc2[4][4];   // [operand j][row fragment fm]
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int fm = 0; fm < 4; ++fm) acc2[j][fm] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+    // one stage: H fragments from LDS, W2 operands from the registers loaded
+    // two stages earlier (refilled with stage step + 2 once transposed)
+    auto mma2 = [&](int64_t step, uint2 (&R)[8]) {
+        const int64_t pr = step / Cfg::kKS;
+        const int kr = (int)(step - pr * Cfg::kKS);
+        const int ks = kr + rotk < Cfg::kKS ? kr + rotk : kr + rotk - Cfg::kKS;
+        const char* hs = hreg + ks * kSub;
+        uint4 bh[4], wop[4];
+#pragma unroll
+        for (int fm = 0; fm < 4; ++fm) bh[fm] = ld16(hs + frag_off(16 * fm + li, lg));
+        transpose8x4(R, wop);
+        __builtin_amdgcn_sched_barrier(0);
+        load2(step + 2, R);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int fm = 0; fm < 4; ++fm) acc2[j][fm] = mfma16x16x32(bh[fm], wop[j], acc2[j][fm]);
+    };
+
+    float* const part = a.part + (int64_t)s * a.rows_out * P + (row0 + 4 * lg) * P + 64 * wc + 4 * li;
+    uint2 RA[8], RB[8];
+    load2(0, RA);
+    load2(1, RB);   // the stage count is even
+    for (int64_t st = 0; st < nsteps; st += 2) {
+        mma2(st, RA);
+        mma2(st + 1, RB);
+        if ((st + 2) % Cfg::kKS != 0) continue;
+        // pass complete: lane holds rows 16 fm + 4 lg + r, columns 4 li .. 4 li + 3
+        const int64_t pd = st / Cfg::kKS;
+        const int64_t pt = pd + rotp < np ? pd + rotp : pd + rotp - np;
+        if (pt * kBN2 + 64 * wc + 4 * li < P) {
+#pragma unroll
+            for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (16 * fm + 4 * lg + r < valid)   // streaming: read once, by the reduction
+                        __builtin_nontemporal_store(
+                            floatx4_t{acc2[0][fm][r], acc2[1][fm][r], acc2[2][fm][r], acc2[3][fm][r]},
+                            reinterpret_cast<floatx4_t*>(part + (int64_t)(16 * fm + r) * P + pt * kBN2));
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int fm = 0; fm < 4; ++fm) acc2[j][fm] = floatx4_t{0.f, 0.f, 0.f, 0.f};
     }
 }
 
