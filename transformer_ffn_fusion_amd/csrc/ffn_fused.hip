@@ -58,13 +58,14 @@ __device__ __forceinline__ uint32_t wtile_dma_off(int l, uint32_t row_bytes) {
 
 // Byte offset, inside a weight stage with `nb` 64-column blocks per row group,
 // of the 8-byte chunk that lane l of a transposing read supplies for operand
-// fragment f (columns 16f..16f+15), half t (k-rows 8g+4t..8g+4t+3).
-__device__ __forceinline__ uint32_t wtile_tr_off(int l, int nb, int f, int t) {
+// fragment f (columns 16f..16f+15), half t (k-rows 8g+4t..8g+4t+3), with
+// g = l/16, j = (l%16)/4, q = l%4: row 8g + j + 4t, 8-column group 2f + q/2,
+// 4-column half q%2.  Written out with the slot rule above this is
+//   wtile_tr_base(l, nb, f % 4) + 1024 * (f / 4) + 512 * t,
+// so a wave whose fragments share f % 4 needs one offset register.
+__device__ __forceinline__ uint32_t wtile_tr_base(int l, int nb, int fq) {
     const int g = l >> 4, s = l & 15, j = s >> 2, q = s & 3;
-    const int c8 = 2 * f + (q >> 1);
-    const int kk = j + 4 * t;
-    const int slot = 8 * kk + ((c8 & 7) ^ ((2 * kk) & 7));
-    return (uint32_t)((g * nb + (c8 >> 3)) * kFrag + 16 * slot + 8 * (q & 1));
+    return (uint32_t)(g * nb * kFrag + 128 * j + 16 * (q >> 1) + 8 * (q & 1) + 32 * (fq ^ j));
 }
 
 // LDS layout of one X fragment (16 rows x 32 k, 1 KiB): the 16-byte unit of
@@ -76,17 +77,18 @@ __device__ __forceinline__ int xfrag_slot(int r, int c) { return 4 * r + (c ^ ((
 
 template <int C>
 struct FusedCfg {
-    static constexpr int kFO = C / 64;                 // hidden fragments per multiplier wave
+    static constexpr int kFO = C / 64;                 // hidden fragments per multiplier wave (every 4th)
     static constexpr int kNB1 = C / 64;                // W1 stage: 64-column blocks per row group
     static constexpr int kKS = C / kBK;                // GEMM2 k-stages per output pass
     static constexpr int kW1Stage = 4 * kNB1 * kFrag;  // 32 x C bf16
     static constexpr int kStage1 = kSub + kW1Stage;    // X slab + W1 slab
     static constexpr int kHBytes = kKS * kSub;         // H: C/32 slabs of 64 x 32
-    static constexpr int kNS1 = 4;                     // GEMM1 stages in flight
+    static constexpr int kNS1 = 4;                     // GEMM1 stages in the LDS ring
     static constexpr int kD1 = 1 + kNB1;               // loads per loader wave per GEMM1 stage
     static constexpr int kLds1 = kNS1 * kStage1;
     static constexpr int kLds = kLds1 > kHBytes ? kLds1 : kHBytes;
     static_assert(C % 64 == 0, "chunk must split over four waves");
+    static_assert(kNS1 >= 3, "the multipliers read one stage ahead; the loaders need one more");
     static_assert(kKS % 2 == 0, "GEMM2 runs its stages in pairs");
     static_assert(kBN2 == 64 * 2 * kMulWaves, "each of the eight waves owns 64 columns of a pass");
     static_assert(kLds <= 160 * 1024, "LDS budget");
@@ -198,6 +200,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     const uint32_t w1_lane = wtile_dma_off(lane, (uint32_t)(O * 2));
 
     const int64_t nk = (N + kBK - 1) / kBK;
+    const int64_t nk2 = (nk + 1) & ~(int64_t)1;   // GEMM1 stages walked, padded to even
 
     // W2 stage: 32 hidden rows x 512 output columns.  The W2 resource covers
     // exactly this chunk's rows, so rows past the chunk read zeros; columns
@@ -219,31 +222,37 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     // barriers: nk for GEMM1, one between the products, nsteps for GEMM2.
     if (loader) {
         // =================== loads of GEMM1 (X slab + W1 chunk) =============
-        auto issue1 = [&](int64_t kt, int buf) {
+        // loads of the i-th stage in walking order (K stage (i + rot1) mod nk); the
+        // padding stage i == nk of an odd stage count reads zeros
+        auto issue1 = [&](int64_t i, int buf) {
+            const bool real = i < nk;
+            const int64_t kt = !real ? 0 : (i + rot1 < nk ? i + rot1 : i + rot1 - nk);
             char* st = smem + buf * Cfg::kStage1;
             const int64_t kx = kt * kBK + 8 * xc;
-            dma16(rx, kx < N ? xrow_off + (uint32_t)(kx * 2) : kOOB, st + w4 * kFrag);
+            dma16(rx, real && kx < N ? xrow_off + (uint32_t)(kx * 2) : kOOB, st + w4 * kFrag);
 #pragma unroll
-            for (int i = 0; i < Cfg::kNB1; ++i) {
-                const int blk = w4 + kMulWaves * i;
+            for (int b = 0; b < Cfg::kNB1; ++b) {
+                const int blk = w4 + kMulWaves * b;
                 const int r = blk / Cfg::kNB1, c = blk % Cfg::kNB1;
                 const uint32_t base = (uint32_t)(((kt * kBK + 8 * r) * O + 64 * c) * 2);
-                dma16(rw1, base + w1_lane, st + kSub + blk * kFrag);
+                dma16(rw1, real ? base + w1_lane : kOOB, st + kSub + blk * kFrag);
             }
         };
 #pragma unroll
         for (int i = 0; i < Cfg::kNS1 - 1; ++i)
-            if (i < nk) issue1(i + rot1 < nk ? i + rot1 : i + rot1 - nk, i);
+            if (i < nk2) issue1(i, i);
+        // barrier -1 publishes stage 0; barrier kt publishes stage kt + 1 (the
+        // multipliers read one stage ahead of the one they multiply)
+        if (Cfg::kNS1 - 2 < nk2) wait_vmcnt<Cfg::kD1 * (Cfg::kNS1 - 2)>();
+        else wait_vmcnt<0>();
+        __syncthreads();
         int ibuf = Cfg::kNS1 - 1;
-        for (int64_t kt = 0; kt < nk; ++kt) {
-            // stages kt .. min(kt + NS1 - 2, nk - 1) are in flight
-            if (kt + Cfg::kNS1 - 2 < nk) wait_vmcnt<Cfg::kD1 * (Cfg::kNS1 - 2)>();
+        for (int64_t kt = 0; kt < nk2; ++kt) {
+            // stages kt+1 .. min(kt + NS1 - 2, nk2 - 1) may be in flight
+            if (kt + Cfg::kNS1 - 2 < nk2) wait_vmcnt<Cfg::kD1 * (Cfg::kNS1 - 3)>();
             else wait_vmcnt<0>();
             __syncthreads();
-            if (kt + Cfg::kNS1 - 1 < nk) {
-                const int64_t kl = kt + Cfg::kNS1 - 1 + rot1;
-                issue1(kl < nk ? kl : kl - nk, ibuf);
-            }
+            if (kt + Cfg::kNS1 - 1 < nk2) issue1(kt + Cfg::kNS1 - 1, ibuf);
             ibuf = (ibuf + 1 == Cfg::kNS1) ? 0 : ibuf + 1;
         }
         __syncthreads();   // the multipliers are done with the GEMM1 ring
@@ -256,34 +265,54 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
             for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
         {
             const int xoff = 16 * xfrag_slot(li, lg);
-            uint32_t trw1[Cfg::kFO][2];   // per-fragment read offsets (the swizzle is not linear in f)
+            // multiplier w owns hidden fragments w, w+4, w+8, ...: f % 4 == w
+            const uint32_t trw1 = wtile_tr_base(lane, Cfg::kNB1, w4);
+            // Software pipeline: after barrier kt (which publishes stage kt+1)
+            // the multiplier reads stage kt+1 while it multiplies stage kt from
+            // registers read one iteration earlier.  The reads are spread over
+            // the MFMAs (the X fragments first, then one W fragment ahead of
+            // each group of four MFMAs), so the LDS sees a steady stream and
+            // its latency hides behind the matrix work.  A read past the last
+            // stage fetches a stale buffer that is never multiplied.
+            auto step = [&](int buf, uint4 (&xn)[4], uint4 (&wn)[Cfg::kFO],
+                            const uint4 (&xc)[4], const uint4 (&wc)[Cfg::kFO]) {
+                const char* st = smem + buf * Cfg::kStage1;
+                const char* sw = st + kSub + trw1;
 #pragma unroll
-            for (int fo = 0; fo < Cfg::kFO; ++fo)
-#pragma unroll
-                for (int t = 0; t < 2; ++t) trw1[fo][t] = wtile_tr_off(lane, Cfg::kNB1, w4 * Cfg::kFO + fo, t);
-            int cbuf = 0;
-            for (int64_t kt = 0; kt < nk; ++kt) {
-                __syncthreads();
-                // 4 row fragments x kFO hidden fragments of stage `cbuf`
-                const char* st = smem + cbuf * Cfg::kStage1;
-                const char* sw = st + kSub;
-                uint4 bx[4], aw[Cfg::kFO];
-#pragma unroll
-                for (int fm = 0; fm < 4; ++fm) bx[fm] = ld16(st + fm * kFrag + xoff);
+                for (int fm = 0; fm < 4; ++fm) xn[fm] = ld16(st + fm * kFrag + xoff);
 #pragma unroll
                 for (int fo = 0; fo < Cfg::kFO; ++fo) {
-                    const uint2 lo = lds_read_tr16(sw + trw1[fo][0]);
-                    const uint2 hi = lds_read_tr16(sw + trw1[fo][1]);
-                    aw[fo] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                }
-                // every read of the stage is in flight before the first MFMA waits
-                __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                for (int fo = 0; fo < Cfg::kFO; ++fo)
+                    const uint2 lo = lds_read_tr16(sw + 1024 * fo);
+                    const uint2 hi = lds_read_tr16(sw + 1024 * fo + 512);
+                    wn[fo] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
                     for (int fm = 0; fm < 4; ++fm)
-                        acc[fo][fm] = mfma16x16x32(aw[fo], bx[fm], acc[fo][fm]);
-                cbuf = (cbuf + 1 == Cfg::kNS1) ? 0 : cbuf + 1;
+                        acc[fo][fm] = mfma16x16x32(wc[fo], xc[fm], acc[fo][fm]);
+                    __builtin_amdgcn_sched_barrier(0);
+                }
+            };
+            uint4 xa[4], wa[Cfg::kFO], xb[4], wb[Cfg::kFO];
+            __syncthreads();
+            {
+                const char* st = smem;
+#pragma unroll
+                for (int fm = 0; fm < 4; ++fm) xa[fm] = ld16(st + fm * kFrag + xoff);
+#pragma unroll
+                for (int fo = 0; fo < Cfg::kFO; ++fo) {
+                    const uint2 lo = lds_read_tr16(st + kSub + trw1 + 1024 * fo);
+                    const uint2 hi = lds_read_tr16(st + kSub + trw1 + 1024 * fo + 512);
+                    wa[fo] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+                }
+            }
+            int rbuf = 1;
+            for (int64_t kt = 0; kt < nk2; kt += 2) {
+                __syncthreads();
+                step(rbuf, xb, wb, xa, wa);
+                rbuf = (rbuf + 1 == Cfg::kNS1) ? 0 : rbuf + 1;
+                __syncthreads();
+                step(rbuf, xa, wa, xb, wb);
+                rbuf = (rbuf + 1 == Cfg::kNS1) ? 0 : rbuf + 1;
             }
         }
         __syncthreads();   // every multiplier is done with the GEMM1 ring
@@ -291,7 +320,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
         // ---- epilogue 1: H = act(A + b1) -> bf16 -> LDS (GEMM2 operand layout)
 #pragma unroll
         for (int fo = 0; fo < Cfg::kFO; ++fo) {
-            const int ol = 16 * (w4 * Cfg::kFO + fo) + 4 * lg;  // first of 4 hidden cols
+            const int ol = 16 * (w4 + kMulWaves * fo) + 4 * lg;  // first of 4 hidden cols
             const int64_t og = o0 + ol;
             float bias[4] = {0.f, 0.f, 0.f, 0.f};
             const bool colok = og < O;  // O % 8 == 0, so the 4 columns are all in or all out
