@@ -209,10 +209,16 @@ def test_moe_shapes(M, E, k, N, O, P):
     compare(got, ref, BF16_TOL, "moe")
 
 
-def test_moe_route_ties_bit_exact():
+@pytest.mark.parametrize("M,E,k", [
+    (1000, 8, 2),
+    (3000, 64, 8),    # several staged logit blocks (128 tokens each), k at its maximum
+    (700, 256, 5),    # the largest expert count: 32 tokens per staged block
+    (1, 3, 3),        # one token, every expert picked
+])
+def test_moe_route_ties_bit_exact(M, E, k):
     import torch
-    M, E, k = 1000, 8, 2
-    rng = np.random.default_rng(5)
+    log(f"case moe route M={M} E={E} k={k}")
+    rng = np.random.default_rng(5 + E)
     logits = (rng.integers(-3, 4, size=(M, E)) * 0.5).astype(np.float32)
     ids = torch.empty((M, k), dtype=torch.int32, device="cuda")
     w = torch.empty((M, k), dtype=torch.float32, device="cuda")

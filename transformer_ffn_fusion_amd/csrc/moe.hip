@@ -22,53 +22,79 @@ namespace ffn {
 namespace {
 
 constexpr int kRouteThreads = 1024;
+constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kMaxE = 256;
 constexpr int kMaxK = 8;
+constexpr int kLogitStage = 8192;   // floats of router logits staged in LDS per token block
 
+// One workgroup.  Pass 1 stages a block of router logits in LDS with coalesced
+// loads and gives each token to one thread (top-k by insertion into a list
+// sorted by decreasing logit, an equal logit staying behind the earlier
+// expert, which is the repeated strict arg-max order), then the gate weights
+// and the expert histogram.  Pass 2 scatters the entries into the per-expert
+// lists in token order: inside a block every wave ranks its entries per
+// expert with ballots, one barrier publishes the per-wave counts, and each
+// entry's position is the expert's running offset plus the counts of earlier
+// waves plus its rank.
 __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
     const float* __restrict__ logits, int64_t M, int E, int k, int32_t* ids, float* w,
     int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* pos, int32_t* tiles,
     int32_t* tile_count) {
+    __shared__ float s_log[kLogitStage];
     __shared__ int s_cnt[kMaxE];
     __shared__ int s_run[kMaxE];
-    __shared__ int s_wave[kRouteThreads / 64];
+    __shared__ int s_wcnt[kRouteWaves][kMaxE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = tid >> 6;
     for (int e = tid; e < E; e += kRouteThreads) s_cnt[e] = 0;
-    __syncthreads();
 
-    // ---- step 1: top-k and gate weights per token
-    for (int64_t t = tid; t < M; t += kRouteThreads) {
-        const float* l = logits + t * E;
-        int pick[kMaxK];
-        for (int s = 0; s < k; ++s) {
-            int best = -1;
-            float bv = 0.f;
-            for (int e = 0; e < E; ++e) {
-                bool taken = false;
-                for (int q = 0; q < s; ++q) taken |= (pick[q] == e);
-                if (taken) continue;
-                const float v = l[e];
-                if (best < 0 || v > bv) {  // strict: the first maximum wins
-                    best = e;
-                    bv = v;
-                }
-            }
-            pick[s] = best;
+    // ---- pass 1: top-k and gate weights per token, expert histogram
+    const int tb = (kLogitStage / E) < kRouteThreads ? (kLogitStage / E) : kRouteThreads;
+    for (int64_t base = 0; base < M; base += tb) {
+        const int nb = (M - base) < tb ? (int)(M - base) : tb;
+        __syncthreads();   // the previous block's logits are no longer read
+        for (int i = tid; i < nb * E; i += kRouteThreads) s_log[i] = logits[base * E + i];
+        __syncthreads();
+        if (tid >= nb) continue;
+        const int64_t t = base + tid;
+        const float* row = s_log + tid * E;
+        float bv[kMaxK];
+        int be[kMaxK];
+#pragma unroll
+        for (int j = 0; j < kMaxK; ++j) { bv[j] = 0.f; be[j] = 0; }
+        int nf = 0;
+        for (int e = 0; e < E; ++e) {
+            const float v = row[e];
+            int p = 0;   // entries that stay ahead: larger or equal logit
+#pragma unroll
+            for (int j = 0; j < kMaxK; ++j) p += (j < nf && bv[j] >= v) ? 1 : 0;
+            if (p >= k) continue;
+#pragma unroll
+            for (int j = kMaxK - 1; j > 0; --j)
+                if (j > p && j < k) { bv[j] = bv[j - 1]; be[j] = be[j - 1]; }
+#pragma unroll
+            for (int j = 0; j < kMaxK; ++j)
+                if (j == p) { bv[j] = v; be[j] = e; }
+            nf = nf + 1 < k ? nf + 1 : k;
         }
-        const float l0 = l[pick[0]];
         float ex[kMaxK];
         float den = 0.f;
-        for (int s = 0; s < k; ++s) {
-            ex[s] = expf(l[pick[s]] - l0);
-            den += ex[s];
+#pragma unroll
+        for (int s = 0; s < kMaxK; ++s) {
+            if (s < k) {
+                ex[s] = expf(bv[s] - bv[0]);
+                den += ex[s];
+            }
         }
-        for (int s = 0; s < k; ++s) {
-            ids[t * k + s] = pick[s];
-            w[t * k + s] = ex[s] / den;
-            atomicAdd(&s_cnt[pick[s]], 1);
+#pragma unroll
+        for (int s = 0; s < kMaxK; ++s) {
+            if (s < k) {
+                ids[t * k + s] = be[s];
+                w[t * k + s] = ex[s] / den;
+                atomicAdd(&s_cnt[be[s]], 1);
+            }
         }
     }
     __syncthreads();
@@ -86,47 +112,58 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
     }
     __syncthreads();
 
-    // ---- stable scatter: entry t*k+s goes to its expert's list in token order
+    // ---- pass 2: stable scatter, entry t*k+s into its expert's list in token order
     const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
     for (int64_t base = 0; base < M; base += kRouteThreads) {
         const int64_t t = base + tid;
         const bool have = t < M;
-        int mine[kMaxK];
-        for (int s = 0; s < k; ++s) mine[s] = have ? ids[t * k + s] : -1;
-        for (int e = 0; e < E; ++e) {
-            int slot = -1;
-            for (int s = 0; s < k; ++s)
-                if (mine[s] == e) slot = s;
-            const uint64_t mask = __ballot(slot >= 0);
-            const int rank = __popcll(mask & lt_mask);
-            if (lane == 0) s_wave[wave] = __popcll(mask);
-            __syncthreads();
-            int before = 0, total = 0;
-            for (int q = 0; q < kRouteThreads / 64; ++q) {
-                before += (q < wave) ? s_wave[q] : 0;
-                total += s_wave[q];
-            }
-            if (slot >= 0) {
-                const int p = s_run[e] + before + rank;
-                sorted[p] = (int32_t)(t * k + slot);
-                pos[t * k + slot] = p;
-            }
-            __syncthreads();
-            if (tid == 0) s_run[e] += total;
-            __syncthreads();
+        int mine[kMaxK], rank[kMaxK];
+#pragma unroll
+        for (int s = 0; s < kMaxK; ++s) {
+            mine[s] = (have && s < k) ? ids[t * k + s] : -1;
+            rank[s] = 0;
         }
+        for (int e = 0; e < E; ++e) {
+            bool hit = false;   // the k picks of a token are distinct experts
+#pragma unroll
+            for (int s = 0; s < kMaxK; ++s) hit |= (mine[s] == e);
+            const uint64_t mask = __ballot(hit);
+            const int r = __popcll(mask & lt_mask);
+#pragma unroll
+            for (int s = 0; s < kMaxK; ++s)
+                if (mine[s] == e) rank[s] = r;
+            if (lane == 0) s_wcnt[wave][e] = __popcll(mask);
+        }
+        __syncthreads();
+#pragma unroll
+        for (int s = 0; s < kMaxK; ++s) {
+            const int e = mine[s];
+            if (e < 0) continue;
+            int before = 0;
+            for (int q = 0; q < wave; ++q) before += s_wcnt[q][e];
+            const int p = s_run[e] + before + rank[s];
+            sorted[p] = (int32_t)(t * k + s);
+            pos[t * k + s] = p;
+        }
+        __syncthreads();
+        for (int e = tid; e < E; e += kRouteThreads) {
+            int tot = 0;
+            for (int q = 0; q < kRouteWaves; ++q) tot += s_wcnt[q][e];
+            s_run[e] += tot;
+        }
+        __syncthreads();
     }
 
     // ---- tile table, heaviest expert first (ties: smaller index first)
     if (tid == 0) {
         int n = 0;
-        bool done[kMaxE];
-        for (int e = 0; e < E; ++e) done[e] = false;
+        int* done = &s_wcnt[0][0];   // the per-wave counts are no longer needed
+        for (int e = 0; e < E; ++e) done[e] = 0;
         for (int it = 0; it < E; ++it) {
             int best = -1;
             for (int e = 0; e < E; ++e)
                 if (!done[e] && (best < 0 || s_cnt[e] > s_cnt[best])) best = e;
-            done[best] = true;
+            done[best] = 1;
             for (int r0 = 0; r0 < s_cnt[best]; r0 += kBM) {
                 const int v = (s_cnt[best] - r0) < kBM ? (s_cnt[best] - r0) : kBM;
                 tiles[3 * n + 0] = best;
