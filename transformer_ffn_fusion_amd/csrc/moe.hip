@@ -24,7 +24,6 @@ namespace {
 constexpr int kRouteThreads = 1024;
 constexpr int kRouteWaves = kRouteThreads / 64;
 constexpr int kMaxE = 256;
-constexpr int kMaxK = 8;
 constexpr int kLogitStage = 8192;   // floats of router logits staged in LDS per token block
 
 // One workgroup.  Pass 1 stages a block of router logits in LDS with coalesced
@@ -36,13 +35,15 @@ constexpr int kLogitStage = 8192;   // floats of router logits staged in LDS per
 // expert with ballots, one barrier publishes the per-wave counts, and each
 // entry's position is the expert's running offset plus the counts of earlier
 // waves plus its rank.
+template <int k>
 __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
-    const float* __restrict__ logits, int64_t M, int E, int k, int32_t* ids, float* w,
+    const float* __restrict__ logits, int64_t M, int E, int32_t* ids, float* w,
     int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* pos, int32_t* tiles,
     int32_t* tile_count) {
     __shared__ float s_log[kLogitStage];
     __shared__ int s_cnt[kMaxE];
     __shared__ int s_run[kMaxE];
+    __shared__ int s_off[kMaxE];
     __shared__ int s_wcnt[kRouteWaves][kMaxE];
 
     const int tid = threadIdx.x;
@@ -55,46 +56,65 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
     for (int64_t base = 0; base < M; base += tb) {
         const int nb = (M - base) < tb ? (int)(M - base) : tb;
         __syncthreads();   // the previous block's logits are no longer read
-        for (int i = tid; i < nb * E; i += kRouteThreads) s_log[i] = logits[base * E + i];
+        for (int i0 = tid; i0 < nb * E; i0 += 8 * kRouteThreads) {   // 8 loads in flight
+            float v[8];
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * kRouteThreads;
+                v[u] = i < nb * E ? logits[base * E + i] : 0.f;
+            }
+#pragma unroll
+            for (int u = 0; u < 8; ++u) {
+                const int i = i0 + u * kRouteThreads;
+                if (i < nb * E) s_log[i] = v[u];
+            }
+        }
         __syncthreads();
-        if (tid >= nb) continue;
+        const bool act = tid < nb;
         const int64_t t = base + tid;
         const float* row = s_log + tid * E;
-        float bv[kMaxK];
-        int be[kMaxK];
+        float bv[k];
+        int be[k];
 #pragma unroll
-        for (int j = 0; j < kMaxK; ++j) { bv[j] = 0.f; be[j] = 0; }
+        for (int j = 0; j < k; ++j) { bv[j] = 0.f; be[j] = 0; }
         int nf = 0;
-        for (int e = 0; e < E; ++e) {
+        for (int e = 0; act && e < E; ++e) {
             const float v = row[e];
             int p = 0;   // entries that stay ahead: larger or equal logit
 #pragma unroll
-            for (int j = 0; j < kMaxK; ++j) p += (j < nf && bv[j] >= v) ? 1 : 0;
+            for (int j = 0; j < k; ++j) p += (j < nf && bv[j] >= v) ? 1 : 0;
             if (p >= k) continue;
 #pragma unroll
-            for (int j = kMaxK - 1; j > 0; --j)
+            for (int j = k - 1; j > 0; --j)
                 if (j > p && j < k) { bv[j] = bv[j - 1]; be[j] = be[j - 1]; }
 #pragma unroll
-            for (int j = 0; j < kMaxK; ++j)
+            for (int j = 0; j < k; ++j)
                 if (j == p) { bv[j] = v; be[j] = e; }
             nf = nf + 1 < k ? nf + 1 : k;
         }
-        float ex[kMaxK];
+        float ex[k];
         float den = 0.f;
 #pragma unroll
-        for (int s = 0; s < kMaxK; ++s) {
+        for (int s = 0; s < k; ++s) {
             if (s < k) {
                 ex[s] = expf(bv[s] - bv[0]);
                 den += ex[s];
             }
         }
 #pragma unroll
-        for (int s = 0; s < kMaxK; ++s) {
-            if (s < k) {
+        for (int s = 0; s < k; ++s) {
+            if (act && s < k) {
                 ids[t * k + s] = be[s];
                 w[t * k + s] = ex[s] / den;
-                atomicAdd(&s_cnt[be[s]], 1);
             }
+        }
+        // expert histogram: one LDS add per wave and expert (ballot counts), not
+        // one contended add per entry
+        for (int e = 0; e < E; ++e) {
+            int c = 0;
+#pragma unroll
+            for (int s = 0; s < k; ++s) c += __popcll(__ballot(act && s < k && be[s] == e));
+            if (lane == 0 && c) atomicAdd(&s_cnt[e], c);
         }
     }
     __syncthreads();
@@ -106,6 +126,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
             counts[e] = s_cnt[e];
             offsets[e] = run;
             s_run[e] = run;
+            s_off[e] = run;
             run += s_cnt[e];
         }
         offsets[E] = run;
@@ -117,26 +138,26 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
     for (int64_t base = 0; base < M; base += kRouteThreads) {
         const int64_t t = base + tid;
         const bool have = t < M;
-        int mine[kMaxK], rank[kMaxK];
+        int mine[k], rank[k];
 #pragma unroll
-        for (int s = 0; s < kMaxK; ++s) {
+        for (int s = 0; s < k; ++s) {
             mine[s] = (have && s < k) ? ids[t * k + s] : -1;
             rank[s] = 0;
         }
         for (int e = 0; e < E; ++e) {
             bool hit = false;   // the k picks of a token are distinct experts
 #pragma unroll
-            for (int s = 0; s < kMaxK; ++s) hit |= (mine[s] == e);
+            for (int s = 0; s < k; ++s) hit |= (mine[s] == e);
             const uint64_t mask = __ballot(hit);
             const int r = __popcll(mask & lt_mask);
 #pragma unroll
-            for (int s = 0; s < kMaxK; ++s)
+            for (int s = 0; s < k; ++s)
                 if (mine[s] == e) rank[s] = r;
             if (lane == 0) s_wcnt[wave][e] = __popcll(mask);
         }
         __syncthreads();
 #pragma unroll
-        for (int s = 0; s < kMaxK; ++s) {
+        for (int s = 0; s < k; ++s) {
             const int e = mine[s];
             if (e < 0) continue;
             int before = 0;
@@ -167,7 +188,7 @@ __global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
             for (int r0 = 0; r0 < s_cnt[best]; r0 += kBM) {
                 const int v = (s_cnt[best] - r0) < kBM ? (s_cnt[best] - r0) : kBM;
                 tiles[3 * n + 0] = best;
-                tiles[3 * n + 1] = offsets[best] + r0;
+                tiles[3 * n + 1] = s_off[best] + r0;
                 tiles[3 * n + 2] = v;
                 ++n;
             }
@@ -230,8 +251,17 @@ hipError_t launch_moe_route(const float* logits, int64_t M, int64_t E, int k, in
                             float* w, int32_t* counts, int32_t* offsets, int32_t* sorted,
                             int32_t* pos, int32_t* tiles, int32_t* tile_count,
                             hipStream_t stream) {
-    hipLaunchKernelGGL(moe_route_kernel, dim3(1), dim3(kRouteThreads), 0, stream, logits, M,
-                       (int)E, k, ids, w, counts, offsets, sorted, pos, tiles, tile_count);
+    switch (k) {
+#define FFN_ROUTE_K(K)                                                                          \
+    case K:                                                                                      \
+        hipLaunchKernelGGL(moe_route_kernel<K>, dim3(1), dim3(kRouteThreads), 0, stream, logits, \
+                           M, (int)E, ids, w, counts, offsets, sorted, pos, tiles, tile_count);  \
+        break;
+        FFN_ROUTE_K(1) FFN_ROUTE_K(2) FFN_ROUTE_K(3) FFN_ROUTE_K(4)
+        FFN_ROUTE_K(5) FFN_ROUTE_K(6) FFN_ROUTE_K(7) FFN_ROUTE_K(8)
+#undef FFN_ROUTE_K
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
