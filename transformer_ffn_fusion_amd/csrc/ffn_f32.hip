@@ -46,8 +46,10 @@ __global__ __launch_bounds__(kThreads) void fused_ffn_f32_kernel(
             xs[r][kk] = (r < valid && k0 + kk < N) ? X[(row0 + r) * N + k0 + kk] : 0.f;
         }
         __syncthreads();
-        const int64_t kend = (N - k0) < kKChunk ? (N - k0) : kKChunk;
-        for (int64_t kk = 0; kk < kend; ++kk) {
+        const int kend = (N - k0) < kKChunk ? (int)(N - k0) : kKChunk;
+        // unrolled so that many independent W1 loads are in flight at once
+#pragma unroll 16
+        for (int kk = 0; kk < kend; ++kk) {
             float w[kColsPerThread];
 #pragma unroll
             for (int j = 0; j < kColsPerThread; ++j) {
@@ -78,7 +80,8 @@ __global__ __launch_bounds__(kThreads) void fused_ffn_f32_kernel(
         float y[kRows];
 #pragma unroll
         for (int r = 0; r < kRows; ++r) y[r] = 0.f;
-        for (int64_t o = 0; o < oc; ++o) {
+#pragma unroll 16
+        for (int o = 0; o < (int)oc; ++o) {
             const float w = W2[(o0 + o) * P + p];
 #pragma unroll
             for (int r = 0; r < kRows; ++r) y[r] = fmaf(hs[r][o], w, y[r]);

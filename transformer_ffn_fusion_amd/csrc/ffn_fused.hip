@@ -502,7 +502,10 @@ hipError_t launch_fused_impl(const FusedArgs& a, int64_t units, hipStream_t stre
 }  // namespace
 
 int fused_pick_chunk(int64_t O) {
-    // prefer the chunk that divides O exactly with the fewest splits
+    // prefer an exact chunk whose split count lets every XCD own one chunk
+    // (the split count divides 8), then any exact chunk, fewest splits first
+    for (int c : {512, 448})
+        if (O % c == 0 && 8 % (O / c) == 0) return c;
     if (O % 512 == 0) return 512;
     if (O % 448 == 0) return 448;
     return 512;
