@@ -148,9 +148,11 @@ const char* ffn_last_error(void);
 /* Library version (major * 10000 + minor * 100 + patch). */
 int ffn_version(void);
 
-/* Host-only self-check of the LDS operand swizzle: 0 when every fragment read
- * and every transposing tile write is a bijection onto distinct bank slots.
- * Makes no HIP call. */
+/* Host-only self-check of the LDS layouts the fused kernel relies on, using the
+ * kernel's own layout functions: the H-tile fragment reads, the weight-stage
+ * blocks (direct-load slots, coalesced lane quads, transposing-read addresses
+ * and their bank spread) and the X fragments.  Returns 0 when all hold, else
+ * the number of the first failed check.  Makes no HIP call. */
 int ffn_selftest_layout(void);
 
 #ifdef __cplusplus

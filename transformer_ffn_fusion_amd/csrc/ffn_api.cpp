@@ -448,23 +448,6 @@ int ffn_selftest_layout(void) {
             }
         }
     }
-    // Transposing writes: thread t owns k-group t%4 and 8-column group t/4 and
-    // writes column 8*(t/4)+j in step j.  Each 16-thread (and 8-thread) group
-    // must hit distinct slots.
-    for (uint32_t j = 0; j < 8; ++j) {
-        for (uint32_t t0 = 0; t0 < 256; t0 += 16) {
-            uint32_t seen16 = 0;
-            for (uint32_t t = t0; t < t0 + 16; ++t)
-                seen16 |= 1u << ((ffn::frag_off(8 * (t / 4) + j, t % 4) >> 4) & 15);
-            if (seen16 != 0xffffu) return 4;
-        }
-        for (uint32_t t0 = 0; t0 < 256; t0 += 8) {
-            uint32_t seen8 = 0;
-            for (uint32_t t = t0; t < t0 + 8; ++t)
-                seen8 |= 1u << ((ffn::frag_off(8 * (t / 4) + j, t % 4) >> 4) & 7);
-            if (seen8 != 0xffu) return 5;
-        }
-    }
     // The offsets of one tile are a bijection onto [0, 64 * idx_count).
     static unsigned char hit[64 * 512];
     std::memset(hit, 0, sizeof hit);
@@ -474,6 +457,61 @@ int ffn_selftest_layout(void) {
             if (off % 16 || off / 16 >= 4 * 512 || hit[off / 16]) return 6;
             hit[off / 16] = 1;
         }
+
+    // Weight stage blocks (8 k-rows x 64 columns, 1 KiB), filled by lane l of a
+    // direct-to-LDS load writing slot l.  slot -> (row, 8-column group) it holds:
+    auto wslot_row = [](uint32_t slot) { return slot >> 3; };
+    auto wslot_grp = [](uint32_t slot) { return (slot & 7) ^ ((2 * (slot >> 3)) & 7); };
+    const uint32_t rb = 4096;   // a row pitch larger than any in-row offset
+    for (uint32_t l = 0; l < 64; ++l) {
+        const uint32_t off = ffn::wtile_dma_off((int)l, rb);
+        if (off / rb != wslot_row(l) || (off % rb) % 16 || (off % rb) / 16 != wslot_grp(l)) return 7;
+    }
+    for (uint32_t q0 = 0; q0 < 64; q0 += 4) {   // each lane quad reads one 64-byte segment
+        const uint32_t seg = ffn::wtile_dma_off((int)q0, rb) / 64;
+        for (uint32_t l = q0; l < q0 + 4; ++l)
+            if (ffn::wtile_dma_off((int)l, rb) / 64 != seg) return 8;
+    }
+    // Transposing reads: lane l (g = l/16, j = (l%16)/4, q = l%4) of the read
+    // for fragment f, half t must address row 8g + j + 4t, column group 2f + q/2,
+    // 4-column half q%2; the 16 lanes of a group (4 rows) hit 16 distinct
+    // 8-byte bank positions modulo 128 bytes.
+    for (int nb = 7; nb <= 8; ++nb)
+        for (int f = 0; f < 4 * nb; ++f)
+            for (int t = 0; t < 2; ++t) {
+                for (int g0 = 0; g0 < 64; g0 += 16) {
+                    uint32_t seen = 0;
+                    for (int l = g0; l < g0 + 16; ++l) {
+                        const uint32_t off = ffn::wtile_tr_base(l, nb, f % 4) + 1024u * (f / 4) + 512u * t;
+                        const uint32_t g = l >> 4, j = (l & 15) >> 2, q = l & 3;
+                        const uint32_t c8 = 2 * f + (q >> 1);
+                        const uint32_t blk = off / 1024, slot = (off % 1024) / 16;
+                        if (blk != g * nb + (c8 >> 3)) return 9;
+                        if (wslot_row(slot) != j + 4 * t || wslot_grp(slot) != (c8 & 7)) return 10;
+                        if ((off % 16) / 8 != (q & 1) || off % 8) return 11;
+                        seen |= 1u << ((off % 128) / 8);
+                    }
+                    if (seen != 0xffffu) return 13;
+                }
+            }
+    // X fragments (16 rows x 32 k): lane l of the load writes slot l = row l/4,
+    // k-group (l%4) ^ (l/8 mod 4); the operand read of lane l (row l%16,
+    // k-group l/16) must find that unit, conflict-free in every 8-lane group.
+    for (int l = 0; l < 64; ++l) {
+        const int r = l >> 2, c = (l & 3) ^ ((l >> 3) & 3);
+        if (ffn::xfrag_slot(r, c) != l) return 14;
+    }
+    uint64_t all = 0;
+    for (int g0 = 0; g0 < 64; g0 += 8) {
+        uint32_t seen = 0;
+        for (int l = g0; l < g0 + 8; ++l) {
+            const int slot = ffn::xfrag_slot(l & 15, l >> 4);
+            seen |= 1u << (slot & 7);
+            all |= 1ull << slot;
+        }
+        if (seen != 0xffu) return 15;
+    }
+    if (all != ~0ull) return 16;
     return 0;
 }
 

@@ -71,6 +71,45 @@ __device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b
 
 // ---------------------------------------------------------------- LDS layout
 
+// ---------------------------------------------------------------- stage layouts
+
+constexpr int kFrag = 1024;   // bytes of one 16-index x 32-deep operand fragment
+
+// LDS layout of a row-major weight stage (32 k-rows x `cols` columns), filled by
+// direct global->LDS loads and read back through the transposing LDS read.
+// The stage is cut into 1 KiB blocks of 8 k-rows x 64 columns, block
+// (r, c) at (r * cols/64 + c) KiB.  Inside a block the 16-byte unit holding
+// row kk (0..7) and 8-column group u (0..7) sits at slot 8kk + (u ^ 2kk mod 8).
+// The loading lane l writes slot l, so lanes 8kk..8kk+7 bring the 128
+// contiguous bytes of row kk (every aligned lane quad stays inside one 64-byte
+// segment: the loads coalesce).  The 16 lanes of one transposing read (4 rows
+// x 2 neighbouring 8-column groups, 8 bytes each) land on 16 distinct 8-byte
+// bank positions modulo 128 bytes -- no bank conflicts on the read side either.
+__host__ __device__ __forceinline__ uint32_t wtile_dma_off(int l, uint32_t row_bytes) {
+    const int kk = l >> 3;
+    return (uint32_t)kk * row_bytes + 16u * (uint32_t)((l & 7) ^ ((2 * kk) & 7));
+}
+
+// Byte offset, inside a weight stage with `nb` 64-column blocks per row group,
+// of the 8-byte chunk that lane l of a transposing read supplies for operand
+// fragment f (columns 16f..16f+15), half t (k-rows 8g+4t..8g+4t+3), with
+// g = l/16, j = (l%16)/4, q = l%4: row 8g + j + 4t, 8-column group 2f + q/2,
+// 4-column half q%2.  Written out with the slot rule above this is
+//   wtile_tr_base(l, nb, f % 4) + 1024 * (f / 4) + 512 * t,
+// so a wave whose fragments share f % 4 needs one offset register.
+__host__ __device__ __forceinline__ uint32_t wtile_tr_base(int l, int nb, int fq) {
+    const int g = l >> 4, s = l & 15, j = s >> 2, q = s & 3;
+    return (uint32_t)(g * nb * kFrag + 128 * j + 16 * (q >> 1) + 8 * (q & 1) + 32 * (fq ^ j));
+}
+
+// LDS layout of one X fragment (16 rows x 32 k, 1 KiB): the 16-byte unit of
+// row r and 8-deep k-group c sits at slot 4r + (c ^ (r/2 mod 4)).  The loading
+// lane l writes slot l, so lanes 4r..4r+3 bring row r's 64 contiguous bytes;
+// the operand read (lane l: row l%16, k-group l/16) is conflict-free within
+// every group of 8 lanes.
+__host__ __device__ __forceinline__ int xfrag_slot(int r, int c) { return 4 * r + (c ^ ((r >> 1) & 3)); }
+
+
 // Byte offset of the 16-byte k-chunk (index idx, k-group g) inside a
 // fragment-major operand tile (see the file comment).
 __host__ __device__ __forceinline__ uint32_t frag_off(uint32_t idx, uint32_t g) {
