@@ -22,6 +22,8 @@ One JSON line goes to stdout:
              average duration, timed live with HIP events recorded on the launch
              stream around each kernel, against MI355X's published peak;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload;
+  box_ceilings  this GPU's own bf16 MFMA and HBM-read ceilings, measured in the same
+             run (roofline also carries the fraction of the measured ceiling);
   secondary  the decode shape (M=16: us/call, HBM GB/s) and, with --all, the others.
 """
 from __future__ import annotations
@@ -262,6 +264,39 @@ def run_moe(cfg, steps, warmup, hip, torch, ffn, synth, workload):
                 bytes=set_bytes, rotate=R)
 
 
+# ---------------------------------------------------------------- box ceilings
+
+def box_ceilings(hip, torch, ffn, reps=10):
+    """This GPU's own ceilings, measured in the same run: a loop of independent
+    bf16 MFMAs on register operands, and a streaming read of a 1 GiB buffer
+    (four times the Infinity Cache)."""
+    L = ffn.lib()
+    sink = torch.zeros(L.ffn_ceiling_sink_bytes() // 4, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream().cuda_stream
+    flops = ffn.ceiling_mfma(sink, 2048)          # warm-up
+    torch.cuda.synchronize()
+    t0, t1 = hip.event(), hip.event()
+    hip.record(t0, stream)
+    for _ in range(reps):
+        ffn.ceiling_mfma(sink, 2048)
+    hip.record(t1, stream)
+    mfma_ms = hip.ms(t0, t1) / reps
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    nbytes = ffn.ceiling_read(buf, sink)          # warm-up
+    torch.cuda.synchronize()
+    hip.record(t0, stream)
+    for _ in range(reps):
+        ffn.ceiling_read(buf, sink)
+    hip.record(t1, stream)
+    read_ms = hip.ms(t0, t1) / reps
+    hip.destroy([t0, t1])
+    del buf
+    return {"mfma_bf16_tflops": flops / (mfma_ms * 1e-3) / 1e12,
+            "hbm_read_gbs": nbytes / (read_ms * 1e-3) / 1e9,
+            "how": "loop of independent v_mfma_f32_16x16x32_bf16 (2048 workgroups x 4 waves); "
+                   "16-byte streaming read of 1 GiB; mean of %d launches each" % reps}
+
+
 # ---------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(cfg, inputs, rows, synth, workload):
@@ -372,6 +407,14 @@ def main():
                                      "us_per_call": 1e3 * m["ms_per_step"],
                                      "kernel1_us": 1e3 * m["k1_ms"], "kernel2_us": 1e3 * m["k2_ms"]}
 
+    ceil = box_ceilings(hip, torch, ffn)
+    if roof["unit"] == "TFLOP/s" and head.dtype == "bf16":
+        roof["measured_peak"] = ceil["mfma_bf16_tflops"]
+        roof["frac_of_measured_peak"] = roof["achieved"] / ceil["mfma_bf16_tflops"]
+    elif roof["unit"] == "GB/s":
+        roof["measured_peak"] = ceil["hbm_read_gbs"]
+        roof["frac_of_measured_peak"] = roof["achieved"] / ceil["hbm_read_gbs"]
+
     cpu = None
     if dense is not None and args.cpu_rows > 0 and head.dtype == "bf16":
         rows = min(args.cpu_rows, head.M)
@@ -397,6 +440,7 @@ def main():
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS if unit == "TFLOP/s" else None,
         "roofline": roof,
         "cpu_baseline": cpu,
+        "box_ceilings": ceil,
         "secondary": secondary,
     }
     print(json.dumps(out), flush=True)

@@ -21,10 +21,11 @@
  *    workspace must be 256-byte aligned.  The caller allocates and owns every
  *    buffer, the workspace included; the library never allocates, frees or
  *    keeps a pointer after the call returns.
- *  - Workspace.  Query the size with the matching *_workspace_size call and
- *    zero-fill the workspace ONCE after allocating it.  Every call leaves its
- *    counters at zero again, so no per-call clearing is needed.  Calls that
- *    share a workspace must be ordered (same stream).
+ *  - Workspace.  Query the size with the matching *_workspace_size call.
+ *    The workspace holds only per-call intermediates (split partials, the
+ *    decode shape's H, the routing tables); it needs no initialisation and
+ *    keeps nothing between calls.  Calls that share a workspace must be
+ *    ordered (same stream).
  *  - Asynchrony.  Calls only enqueue work on `stream` (a hipStream_t; NULL is
  *    the default stream) and return without synchronising.
  *  - Errors.  Every argument check runs on the host before anything is
@@ -147,6 +148,22 @@ const char* ffn_last_error(void);
 
 /* Library version (major * 10000 + minor * 100 + patch). */
 int ffn_version(void);
+
+/* ---- Measurement support (not part of the FFN path) --------------------
+ * Two kernels that give a benchmark this GPU's own ceilings beside the
+ * published peaks: a loop of independent bf16 MFMAs on register operands, and
+ * a streaming 16-byte read of a device buffer.  Both only enqueue on `stream`;
+ * time them with events.  `sink` is a device buffer of at least
+ * ffn_ceiling_sink_bytes() bytes that the kernels may write (in practice they
+ * never do; it keeps their work from being optimised away). */
+size_t ffn_ceiling_sink_bytes(void);
+/* Enqueues the MFMA loop (`iters` steps per wave) and returns in
+ * *flops_per_launch the floating-point operations one launch performs. */
+int ffn_ceiling_mfma(void* sink, size_t sink_bytes, int iters, double* flops_per_launch,
+                     void* stream);
+/* Enqueues one read of `bytes` bytes (a positive multiple of 16) at `src`
+ * (16-byte aligned). */
+int ffn_ceiling_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream);
 
 /* Host-only self-check of the LDS layouts the fused kernel relies on, using the
  * kernel's own layout functions: the H-tile fragment reads, the weight-stage

@@ -127,3 +127,19 @@ def test_route_rejects():
     assert L.moe_route(None, 8, 8, 2, None, None, None, None, FAKE, 1 << 20, None) == E_INVAL
     assert L.moe_route(FAKE, 8, 8, 2, None, None, None, None, FAKE, 0, None) == E_WS
     assert L.moe_route(FAKE, 8, 8, 2, None, None, None, None, FAKE + 8, 1 << 20, None) == E_ALIGN
+
+
+def test_ceiling_entry_points_reject_before_launch():
+    """The measurement kernels check their arguments on the host (no GPU needed)."""
+    import ctypes
+    L = ffn.lib()
+    sink_bytes = L.ffn_ceiling_sink_bytes()
+    assert L.ffn_ceiling_read(FAKE, 1 << 20, None, sink_bytes, None) == E_INVAL
+    assert sink_bytes > 0
+    f = ctypes.c_double()
+    assert L.ffn_ceiling_mfma(None, sink_bytes, 16, ctypes.byref(f), None) == E_INVAL
+    assert L.ffn_ceiling_mfma(FAKE, sink_bytes - 4, 16, ctypes.byref(f), None) == E_WS
+    assert L.ffn_ceiling_mfma(FAKE, sink_bytes, 0, ctypes.byref(f), None) == E_INVAL
+    assert L.ffn_ceiling_read(FAKE + 4, 1 << 20, FAKE, sink_bytes, None) == E_ALIGN
+    assert L.ffn_ceiling_read(FAKE, 24, FAKE, sink_bytes, None) == E_INVAL
+    assert L.ffn_ceiling_read(FAKE, 1 << 20, FAKE, 8, None) == E_WS

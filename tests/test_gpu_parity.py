@@ -267,3 +267,16 @@ def test_large_workload_sampled_rows():
     log(f"case {c.name}, {rows.size} sampled rows")
     got, ref, _ = _run_dense(c.M, c.N, c.O, c.P, rows=rows)
     compare(got, ref, BF16_TOL, c.name)
+
+
+def test_ceiling_kernels_run():
+    """The measurement-support kernels run and report their work (no parity: they compute nothing)."""
+    import torch
+    sink = torch.zeros(ffn.lib().ffn_ceiling_sink_bytes() // 4, dtype=torch.float32, device="cuda")
+    flops = ffn.ceiling_mfma(sink, 4)
+    buf = torch.ones(1 << 20, dtype=torch.uint8, device="cuda")
+    nbytes = ffn.ceiling_read(buf, sink)
+    torch.cuda.synchronize()
+    assert flops == 2048 * 4 * 4 * 8 * (2.0 * 16 * 16 * 32)
+    assert nbytes == 1 << 20
+    assert float(sink.abs().sum()) == 0.0   # the sink is never written

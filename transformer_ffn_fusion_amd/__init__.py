@@ -73,6 +73,12 @@ def lib():
         L.ffn_last_error.restype = ctypes.c_char_p
         L.ffn_version.restype = i32
         L.ffn_selftest_layout.restype = i32
+        L.ffn_ceiling_sink_bytes.argtypes = []
+        L.ffn_ceiling_sink_bytes.restype = sz
+        L.ffn_ceiling_mfma.argtypes = [vp, sz, i32, ctypes.POINTER(ctypes.c_double), vp]
+        L.ffn_ceiling_mfma.restype = i32
+        L.ffn_ceiling_read.argtypes = [vp, sz, vp, sz, vp]
+        L.ffn_ceiling_read.restype = i32
         _lib = L
     return _lib
 
@@ -172,3 +178,21 @@ def moe_ffn_forward(X, logits, k, W1, b1, W2, b2, Y, act1="gelu_tanh", act2="non
                                  _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets),
                                  _ptr(sorted_entries), _ptr(ws), ws.numel(), _stream(stream)))
     return Y
+
+
+# ---------------------------------------------------------------- measurement support
+
+def ceiling_mfma(sink, iters, stream=None) -> float:
+    """Enqueue the bf16 MFMA loop kernel; returns the FLOP count of the launch."""
+    f = ctypes.c_double()
+    _check(lib().ffn_ceiling_mfma(_ptr(sink), sink.numel() * sink.element_size(), iters,
+                                  ctypes.byref(f), _stream(stream)))
+    return f.value
+
+
+def ceiling_read(src, sink, stream=None) -> int:
+    """Enqueue one streaming read of ``src`` (a device tensor); returns the bytes read."""
+    nbytes = src.numel() * src.element_size()
+    _check(lib().ffn_ceiling_read(_ptr(src), nbytes, _ptr(sink), sink.numel() * sink.element_size(),
+                                  _stream(stream)))
+    return nbytes

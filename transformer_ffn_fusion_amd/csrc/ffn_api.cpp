@@ -426,6 +426,35 @@ int moe_ffn_forward_traced(const void* X, const float* logits, int64_t M, int64_
 
 // ---------------------------------------------------------------- self-check
 
+size_t ffn_ceiling_sink_bytes(void) { return (size_t)ffn::ceiling_sink_floats() * 4; }
+
+int ffn_ceiling_mfma(void* sink, size_t sink_bytes, int iters, double* flops_per_launch,
+                     void* stream) {
+    if (!sink || !flops_per_launch) return fail(FFN_EINVAL, "sink and flops_per_launch must not be NULL");
+    if (sink_bytes < ffn_ceiling_sink_bytes())
+        return fail(FFN_EWORKSPACE, "sink has %zu bytes, needs %zu", sink_bytes, ffn_ceiling_sink_bytes());
+    if (iters < 1) return fail(FFN_EINVAL, "iters must be >= 1 (got %d)", iters);
+    double f = 0.0;
+    int rc = launched(ffn::launch_ceiling_mfma(static_cast<float*>(sink), iters, &f,
+                                               reinterpret_cast<hipStream_t>(stream)),
+                      "MFMA ceiling kernel");
+    if (rc) return rc;
+    *flops_per_launch = f;
+    return ok();
+}
+
+int ffn_ceiling_read(const void* src, size_t bytes, void* sink, size_t sink_bytes, void* stream) {
+    if (!src || !sink) return fail(FFN_EINVAL, "src and sink must not be NULL");
+    if (!aligned16(src)) return fail(FFN_EALIGN, "src not 16-byte aligned");
+    if (bytes < 16 || bytes % 16) return fail(FFN_EINVAL, "bytes must be a positive multiple of 16");
+    if (sink_bytes < ffn_ceiling_sink_bytes())
+        return fail(FFN_EWORKSPACE, "sink has %zu bytes, needs %zu", sink_bytes, ffn_ceiling_sink_bytes());
+    int rc = launched(ffn::launch_ceiling_read(src, bytes, static_cast<uint32_t*>(sink),
+                                               reinterpret_cast<hipStream_t>(stream)),
+                      "read ceiling kernel");
+    return rc ? rc : ok();
+}
+
 int ffn_selftest_layout(void) {
     // Fragment reads: for each 16-index fragment and k-group, the 16 lanes hit
     // 16 distinct 16-byte slots of one 256-byte line (and 8 distinct slots in

@@ -69,4 +69,10 @@ hipError_t launch_moe_combine(const float* part, int splits, int64_t rows_total,
                               const uint16_t* b2, uint16_t* Y, int64_t M, int k, int64_t P,
                               int act2, hipStream_t stream);
 
+// ---- measurement support (ceilings.hip): the box's own MFMA and HBM ceilings
+
+int ceiling_sink_floats();
+hipError_t launch_ceiling_mfma(float* sink, int iters, double* flops, hipStream_t stream);
+hipError_t launch_ceiling_read(const void* src, size_t bytes, uint32_t* sink, hipStream_t stream);
+
 }  // namespace ffn
