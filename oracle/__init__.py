@@ -66,6 +66,10 @@ def _bind(lib):
     lib.oracle_moe_ffn.argtypes = [i32, vp, vp, i64, i64, i32, vp, vp, vp, vp, i64, i64, i64,
                                    i32, i32, vp, i64, dp]
     lib.oracle_moe_ffn.restype = ctypes.c_int
+    lib.oracle_swiglu.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i64, dp]
+    lib.oracle_swiglu.restype = ctypes.c_int
+    lib.oracle_silu.argtypes = [ctypes.c_double]
+    lib.oracle_silu.restype = ctypes.c_double
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_act.argtypes = [i32, ctypes.c_double]
@@ -125,6 +129,36 @@ def ffn(X, W1, b1, W2, b2, act1=ACT_GELU_TANH, act2=ACT_NONE, rows=None, lib=Non
                         act1, act2, Y.ctypes.data)
     if rc != 0:
         raise ValueError("oracle_ffn rejected its arguments")
+    return Y
+
+
+def silu(x: float, lib=None) -> float:
+    """The oracle's silu applied to one double (for the closed-form pins)."""
+    return (lib or load()).oracle_silu(float(x))
+
+
+def swiglu(X, Wg, Wu, Wd, rows=None, lib=None):
+    """fp64 ``Y[rows] = (silu(X Wg) * (X Wu)) Wd`` (the SwiGLU FFN: no biases).
+
+    ``X`` (M x N), ``Wg`` and ``Wu`` (N x O), ``Wd`` (O x P): float32 arrays or uint16
+    arrays of bf16 bit patterns."""
+    lib = lib or load()
+    dt = _dtype_of(X)
+    M, N = X.shape
+    O = Wg.shape[1]
+    P = Wd.shape[1]
+    assert Wg.shape == (N, O) and Wu.shape == (N, O) and Wd.shape == (O, P)
+    keep = [_as_input(a, dt) for a in (X, Wg, Wu, Wd)]
+    ptr = [k[1] for k in keep]
+    if rows is None:
+        rws, rp, nr = None, None, M
+    else:
+        rws = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        rp, nr = rws.ctypes.data, rws.size
+    Y = np.empty((nr, P), dtype=np.float64)
+    rc = lib.oracle_swiglu(dt, ptr[0], ptr[1], ptr[2], ptr[3], rp, nr, M, N, O, P, Y.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_swiglu rejected its arguments")
     return Y
 
 

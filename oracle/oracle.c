@@ -15,6 +15,12 @@
  *  - Same page, same section, the tensor-parallel equation: the per-shard
  *    partial H^(g) W2^(g) carries no b2; b2 (and act2) are applied once after
  *    the sum over shards.  oracle_ffn() with b2 == NULL computes that partial.
+ *  - Same post, section "Benchmarks": a SwiGLU FFN has a third weight matrix
+ *    whose product with the input gates the activation, and no biases.
+ *    oracle_swiglu() computes H = silu(X Wg) * (X Wu) elementwise and
+ *    Y = H Wd, with silu(x) = x / (1 + exp(-x)) (the Swish-1 / SiLU unit of
+ *    Ramachandran et al. and Elfwing et al.; the page names the activation
+ *    but does not write it out).
  *  - "Fine-Grained Compute-Communication Overlap for MoE" review
  *    (zhongzhuzhou.org), section 2.1 (Mixture-of-Experts, briefly) and 2.2
  *    (five steps): the router picks the top-k experts per token and the
@@ -131,6 +137,68 @@ int oracle_ffn(int dtype, const void* X, const void* W1, const void* b1,
             }
         }
         free(h);
+        free(acc);
+    }
+    return bad ? -1 : 0;
+}
+
+/* silu(x) = x * sigmoid(x), written as x / (1 + exp(-x)). */
+double oracle_silu(double x) { return x / (1.0 + exp(-x)); }
+
+/* One output row of the SwiGLU FFN:
+ * g[o] = sum_n X[m,n] Wg[n,o], u[o] = sum_n X[m,n] Wu[n,o]  (ascending n)
+ * h[o] = silu(g[o]) * u[o]
+ * y[p] = sum_o h[o] Wd[o,p]  (ascending o).  No biases. */
+static void swiglu_row(int dtype, const void* X, const void* Wg, const void* Wu,
+                       const void* Wd, int64_t m, int64_t N, int64_t O, int64_t P,
+                       double* g, double* u, double* acc, double* yrow) {
+    for (int64_t o = 0; o < O; ++o) g[o] = u[o] = 0.0;
+    for (int64_t n = 0; n < N; ++n) {
+        double x = load(dtype, X, m * N + n);
+        for (int64_t o = 0; o < O; ++o) {
+            g[o] += x * load(dtype, Wg, n * O + o);
+            u[o] += x * load(dtype, Wu, n * O + o);
+        }
+    }
+    for (int64_t o = 0; o < O; ++o) g[o] = oracle_silu(g[o]) * u[o];
+    for (int64_t p = 0; p < P; ++p) acc[p] = 0.0;
+    for (int64_t o = 0; o < O; ++o) {
+        double hv = g[o];
+        for (int64_t p = 0; p < P; ++p) acc[p] += hv * load(dtype, Wd, o * P + p);
+    }
+    for (int64_t p = 0; p < P; ++p) yrow[p] = acc[p];
+}
+
+/* SwiGLU FFN rows, as oracle_ffn (rows == NULL: all M rows). */
+int oracle_swiglu(int dtype, const void* X, const void* Wg, const void* Wu, const void* Wd,
+                  const int64_t* rows, int64_t nrows, int64_t M, int64_t N, int64_t O,
+                  int64_t P, double* Y) {
+    if (!X || !Wg || !Wu || !Wd || !Y || M < 0 || N < 1 || O < 1 || P < 1) return -1;
+    if (dtype != OR_F32 && dtype != OR_BF16) return -1;
+    if (!rows) nrows = M;
+    int bad = 0;
+#pragma omp parallel
+    {
+        double* g = (double*)malloc(sizeof(double) * (size_t)O);
+        double* u = (double*)malloc(sizeof(double) * (size_t)O);
+        double* acc = (double*)malloc(sizeof(double) * (size_t)P);
+        if (!g || !u || !acc) {
+#pragma omp atomic write
+            bad = 1;
+        } else {
+#pragma omp for schedule(dynamic, 1)
+            for (int64_t r = 0; r < nrows; ++r) {
+                int64_t m = rows ? rows[r] : r;
+                if (m < 0 || m >= M) {
+#pragma omp atomic write
+                    bad = 1;
+                    continue;
+                }
+                swiglu_row(dtype, X, Wg, Wu, Wd, m, N, O, P, g, u, acc, Y + r * P);
+            }
+        }
+        free(g);
+        free(u);
         free(acc);
     }
     return bad ? -1 : 0;

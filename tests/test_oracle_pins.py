@@ -315,6 +315,116 @@ def test_flop_and_byte_counts():
 
 
 # ----------------------------------------------------------------------------
+# 7b. SwiGLU FFN (gated activation, no biases)
+# ----------------------------------------------------------------------------
+
+def _sigmoid_tanh_form(x):
+    # sigmoid(x) = (1 + tanh(x / 2)) / 2: a different formula from 1 / (1 + e^-x)
+    return 0.5 * (1.0 + np.tanh(0.5 * x))
+
+
+def test_silu_pins():
+    assert oracle.silu(0.0) == 0.0
+    for x in np.linspace(-20, 20, 161):
+        x = float(x)
+        assert abs(oracle.silu(x) - x * _sigmoid_tanh_form(x)) <= 1e-15 * max(1.0, abs(x))
+        # x sigmoid(x) - (-x) sigmoid(-x) = x (sigmoid(x) + sigmoid(-x)) = x
+        assert abs(oracle.silu(x) - oracle.silu(-x) - x) <= 1e-14 * max(1.0, abs(x))
+    assert oracle.silu(60.0) == 60.0          # gate fully open: exp(-60) is below half an ulp
+    assert oracle.silu(-800.0) == 0.0         # gate shut
+
+
+def test_swiglu_identity_closed_form():
+    """N=O=P, Wg = 2I, Wu = Wd = I: y = silu(2x) * x = 2x^2 sigmoid(2x).  Swapping the
+    gate and the up projection would give silu(x) * 2x instead."""
+    n = 16
+    rng = np.random.default_rng(4)
+    X = rng.standard_normal((7, n)).astype(np.float32)
+    eye = np.eye(n, dtype=np.float32)
+    Y = oracle.swiglu(X, 2 * eye, eye, eye)
+    x = X.astype(np.float64)
+    expect = 2 * x * x * _sigmoid_tanh_form(2 * x)
+    np.testing.assert_allclose(Y, expect, rtol=1e-14, atol=1e-300)
+    swapped = 2 * x * x * _sigmoid_tanh_form(x)
+    assert np.abs(Y - swapped).max() > 1e-3
+
+
+def _saturated_gate_inputs(rng, M, N, O, P):
+    """Dyadic inputs whose gate pre-activations are all >= 40, where silu(g) == g in
+    fp64: the first input column is 8 and the first row of Wg is 8 (64 from that
+    term), every other term is at most 4 in magnitude and there are at most 5 of them."""
+    assert N <= 6
+    X, Wg, Wu, Wd = (_dyadic(rng, s) for s in [(M, N), (N, O), (N, O), (O, P)])
+    X[:, 0] = 8.0
+    Wg[0, :] = 8.0
+    return X, Wg, Wu, Wd
+
+
+def _frac_swiglu_open_gate(X, Wg, Wu, Wd):
+    """Exact Y = ((X Wg) * (X Wu)) Wd in Fractions (the gate is fully open)."""
+    M, N = X.shape
+    O, P = Wd.shape
+    F = lambda v: Fraction(float(v))  # noqa: E731
+    out = []
+    for m in range(M):
+        g = [sum(F(X[m, n]) * F(Wg[n, o]) for n in range(N)) for o in range(O)]
+        u = [sum(F(X[m, n]) * F(Wu[n, o]) for n in range(N)) for o in range(O)]
+        assert min(g) >= 40
+        out.append([sum(g[o] * u[o] * F(Wd[o, p]) for o in range(O)) for p in range(P)])
+    return out
+
+
+@pytest.mark.parametrize("shape", [(2, 3, 4, 2), (3, 5, 7, 4), (1, 1, 1, 1), (4, 6, 3, 5)])
+@pytest.mark.parametrize("as_bf16", [False, True])
+def test_swiglu_open_gate_exact(shape, as_bf16):
+    """With the gate open the SwiGLU FFN is bilinear and exact in fp64: every index of
+    Wg, Wu, Wd and X is checked against a Fraction brute force."""
+    M, N, O, P = shape
+    rng = np.random.default_rng(sum(shape) * 31 + as_bf16)
+    X, Wg, Wu, Wd = _saturated_gate_inputs(rng, M, N, O, P)
+    exact = _frac_swiglu_open_gate(X, Wg, Wu, Wd)
+    conv = _to_bf16 if as_bf16 else (lambda a: a)
+    Y = oracle.swiglu(conv(X), conv(Wg), conv(Wu), conv(Wd))
+    for m in range(M):
+        for p in range(P):
+            assert Y[m, p] == float(exact[m][p]), (m, p)
+
+
+def test_swiglu_shut_gate_and_zero_input():
+    rng = np.random.default_rng(8)
+    M, N, O, P = 3, 4, 5, 6
+    X, Wg, Wu, Wd = (_dyadic(rng, s) for s in [(M, N), (N, O), (N, O), (O, P)])
+    X[:, 0] = 8.0
+    Wg[:] = 0.0
+    Wg[0, :] = -200.0                     # g = -1600: silu(g) == -0 in fp64
+    assert np.all(oracle.swiglu(X, Wg, Wu, Wd) == 0.0)
+    assert np.all(oracle.swiglu(np.zeros_like(X), Wg, Wu, Wd) == 0.0)
+
+
+@pytest.mark.parametrize("G", [2, 4, 8])
+def test_swiglu_tensor_parallel_invariant(G):
+    """Column-split Wg and Wu, row-split Wd: the FFN is the sum of the shard outputs."""
+    M, N, O, P = 6, 32, 64, 24
+    X, Wg, Wu, Wd = synth.swiglu_inputs(M, N, O, P, dtype="bf16", seed=6)
+    full = oracle.swiglu(X, Wg, Wu, Wd)
+    w = O // G
+    total = np.zeros_like(full)
+    for g in range(G):
+        sl = slice(g * w, (g + 1) * w)
+        total += oracle.swiglu(X, np.ascontiguousarray(Wg[:, sl]), np.ascontiguousarray(Wu[:, sl]),
+                               np.ascontiguousarray(Wd[sl, :]))
+    np.testing.assert_allclose(total, full, rtol=1e-12, atol=1e-12 * np.abs(full).max())
+
+
+def test_swiglu_rows_bit_exact():
+    M, N, O, P = 10, 16, 24, 8
+    X, Wg, Wu, Wd = synth.swiglu_inputs(M, N, O, P, dtype="bf16", seed=2)
+    Y = oracle.swiglu(X, Wg, Wu, Wd)
+    rows = [9, 0, 4]
+    assert np.array_equal(oracle.swiglu(X, Wg, Wu, Wd, rows=rows), Y[rows])
+
+
+# ----------------------------------------------------------------------------
 # 8. planted mistakes in the oracle must be caught (CPU only)
 # ----------------------------------------------------------------------------
 
@@ -333,6 +443,14 @@ MUTANTS = {
     "lists_descending": ("for (int64_t t = 0; t < M; ++t)\n                    for (int s = 0; s < k; ++s)\n                        if",
                          "for (int64_t t = M - 1; t >= 0; --t)\n                    for (int s = 0; s < k; ++s)\n                        if"),
     "moe_weight_dropped": ("y[p] += w[t * k + s] * z[p];", "y[p] += z[p];"),
+    "swiglu_gate_up_swapped": ("g[o] = oracle_silu(g[o]) * u[o];", "g[o] = oracle_silu(u[o]) * g[o];"),
+    "swiglu_no_silu": ("g[o] = oracle_silu(g[o]) * u[o];", "g[o] = g[o] * u[o];"),
+    "silu_sign": ("x / (1.0 + exp(-x))", "x / (1.0 + exp(x))"),
+    "swiglu_wg_cols_reversed": ("load(dtype, Wg, n * O + o)", "load(dtype, Wg, n * O + (O - 1 - o))"),
+    "swiglu_wu_cols_reversed": ("load(dtype, Wu, n * O + o)", "load(dtype, Wu, n * O + (O - 1 - o))"),
+    "swiglu_wd_cols_reversed": ("load(dtype, Wd, o * P + p)", "load(dtype, Wd, o * P + (P - 1 - p))"),
+    "swiglu_skip_first_n": ("x = load(dtype, X, m * N + n);\n        for (int64_t o = 0; o < O; ++o) {\n            g[o]",
+                            "x = n ? load(dtype, X, m * N + n) : 0.0;\n        for (int64_t o = 0; o < O; ++o) {\n            g[o]"),
 }
 
 
@@ -384,8 +502,22 @@ def _pin_suite(lib):
             ref = w[t, 0] * z[ids[t, 0]][t] + w[t, 1] * z[ids[t, 1]][t]
             assert np.allclose(Y[t], ref, rtol=1e-13, atol=1e-13)
 
+    def swiglu():
+        for shape in [(3, 5, 7, 4), (2, 3, 4, 2)]:
+            rng = np.random.default_rng(11)
+            X, Wg, Wu, Wd = _saturated_gate_inputs(rng, *shape)
+            exact = _frac_swiglu_open_gate(X, Wg, Wu, Wd)
+            Y = oracle.swiglu(X, Wg, Wu, Wd, lib=lib)
+            assert all(Y[m, p] == float(exact[m][p]) for m in range(shape[0]) for p in range(shape[3]))
+        n = 8
+        x = np.linspace(-3, 3, 3 * n).reshape(3, n).astype(np.float32)
+        eye = np.eye(n, dtype=np.float32)
+        Y = oracle.swiglu(x, 2 * eye, eye, eye, lib=lib)
+        xd = x.astype(np.float64)
+        assert np.allclose(Y, 2 * xd * xd * _sigmoid_tanh_form(2 * xd), rtol=1e-13, atol=0)
+
     for name, fn in [("brute", brute), ("act2", act2), ("gelu", gelu), ("routing", routing),
-                     ("moe_combine", moe_combine)]:
+                     ("moe_combine", moe_combine), ("swiglu", swiglu)]:
         check(name, fn)
     return failures
 

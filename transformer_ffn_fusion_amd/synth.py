@@ -64,6 +64,22 @@ def dense_inputs(M, N, O, P, *, dtype="bf16", bias_var=0.02, seed=0, with_bias=T
     return out
 
 
+def swiglu_inputs(M, N, O, P, *, dtype="bf16", seed=0):
+    """X (MxN), Wg and Wu (NxO), Wd (OxP) for the SwiGLU FFN (no biases); the same
+    Gaussian scaling as dense_inputs (unit-variance X, 1/sqrt(fan_in) weights)."""
+    rng = np.random.default_rng(seed)
+    X = _draw(rng, (M, N), 1.0)
+    Wg = _draw(rng, (N, O), 1.0 / np.sqrt(N))
+    Wu = _draw(rng, (N, O), 1.0 / np.sqrt(N))
+    Wd = _draw(rng, (O, P), 1.0 / np.sqrt(O))
+    out = (X, Wg, Wu, Wd)
+    if dtype == "bf16":
+        out = tuple(f32_to_bf16_bits(a) for a in out)
+    elif dtype != "f32":
+        raise ValueError(dtype)
+    return out
+
+
 def moe_inputs(M, E, N, O, P, *, offsets=MOE_SKEW_OFFSETS, bias_var=0.02, seed=0):
     """bf16 MoE inputs: X (MxN), logits (MxE, fp32), W1 (ExNxO), b1 (ExO), W2 (ExOxP), b2 (ExP)."""
     rng = np.random.default_rng(seed)
