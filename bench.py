@@ -1,12 +1,15 @@
 #!/usr/bin/env python3
 """Benchmark of the fused FFN on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--workload prefill|decode|large|moe|tiny] [--all]
+    python bench.py [--steps K] [--warmup W]
+                    [--workload prefill|decode|large|moe|tiny|swiglu|swiglu_decode] [--all]
 
 A step is one call of the whole path on one batch of synthetic input that is
 already resident in HBM: for the dense workloads the fused FFN kernel and the
 ordered split reduction (or the two skinny layers at M <= 16); for the MoE
-workload routing, the grouped fused FFN and the combine.  W untimed warm-up
+workload routing, the grouped fused FFN and the combine; for the SwiGLU
+workloads the gated fused FFN and the reduction (two gated skinny layers at
+M <= 16).  W untimed warm-up
 steps, then K timed steps bracketed by a device synchronisation on both sides
 (region 1, the headline value), then K more steps with HIP events recorded on
 the launch stream before, between and after the kernels (region 2, the
@@ -138,22 +141,34 @@ def to_dev(a, torch):
 # ---------------------------------------------------------------- dense
 
 def run_dense(cfg, steps, warmup, hip, torch, ffn, synth, workload):
+    """Dense FFN workloads, and the SwiGLU ones (cfg a workload.Gated: its inputs
+    are X, Wg, Wu, Wd and it has no biases)."""
     dt = cfg.dtype
-    X, W1, b1, W2, b2 = synth.dense_inputs(cfg.M, cfg.N, cfg.O, cfg.P, dtype=dt,
-                                           bias_var=cfg.bias_var, seed=0)
+    gated = isinstance(cfg, workload.Gated)
     es = workload.esize(dt)
-    set_bytes = workload.dense_bytes(cfg.M, cfg.N, cfg.O, cfg.P, es)
+    if gated:
+        X, W1, b1, W2 = synth.swiglu_inputs(cfg.M, cfg.N, cfg.O, cfg.P, dtype=dt, seed=0)
+        b2 = None
+        set_bytes = workload.swiglu_bytes(cfg.M, cfg.N, cfg.O, cfg.P, es)
+    else:
+        X, W1, b1, W2, b2 = synth.dense_inputs(cfg.M, cfg.N, cfg.O, cfg.P, dtype=dt,
+                                               bias_var=cfg.bias_var, seed=0)
+        set_bytes = workload.dense_bytes(cfg.M, cfg.N, cfg.O, cfg.P, es)
+    # gated: the slots (X, W1, b1, W2, b2) hold X, Wg, Wu, Wd and no b2
     R = max(1, min(64, math.ceil(MALL_DEFEAT_BYTES / set_bytes)))
     tdt = torch.bfloat16 if dt == "bf16" else torch.float32
     base = [to_dev(a, torch) for a in (X, W1, b1, W2, b2)]
-    sets = [[t.clone() for t in base] + [torch.empty((cfg.M, cfg.P), dtype=tdt, device="cuda")]
+    sets = [[None if t is None else t.clone() for t in base] + [torch.empty((cfg.M, cfg.P), dtype=tdt, device="cuda")]
             for _ in range(R)]
     del base
     code = ffn.BF16 if dt == "bf16" else ffn.F32
-    ws = ffn.workspace(ffn.ffn_workspace_size(cfg.M, cfg.N, cfg.O, cfg.P, code))
+    if gated:
+        ws = ffn.workspace(ffn.ffn_swiglu_workspace_size(cfg.M, cfg.N, cfg.O, cfg.P, code))
+    else:
+        ws = ffn.workspace(ffn.ffn_workspace_size(cfg.M, cfg.N, cfg.O, cfg.P, code))
     L = ffn.lib()
     stream = torch.cuda.current_stream().cuda_stream
-    act1 = ffn.ACTS[cfg.act1]
+    act1 = 0 if gated else ffn.ACTS[cfg.act1]
     nev = 3
     evs = [hip.event(device_only=True) for _ in range(nev * steps)]
     arr_t = ctypes.c_void_p * nev
@@ -161,7 +176,13 @@ def run_dense(cfg, steps, warmup, hip, torch, ffn, synth, workload):
     def call(i, ev=None):
         x, w1, c1, w2, c2, y = sets[i % R]
         p = lambda t: None if t is None else t.data_ptr()  # noqa: E731
-        if ev is None:
+        if gated and ev is None:
+            rc = L.ffn_swiglu_forward(p(x), p(w1), p(c1), p(w2), p(y), cfg.M, cfg.N, cfg.O, cfg.P,
+                                      code, 0, p(ws), ws.numel(), stream)
+        elif gated:
+            rc = L.ffn_swiglu_forward_traced(p(x), p(w1), p(c1), p(w2), p(y), cfg.M, cfg.N, cfg.O,
+                                             cfg.P, code, 0, p(ws), ws.numel(), stream, ev, nev)
+        elif ev is None:
             rc = L.ffn_forward(p(x), p(w1), p(c1), p(w2), p(c2), p(y), cfg.M, cfg.N, cfg.O, cfg.P,
                                code, act1, 0, p(ws), ws.numel(), stream)
         else:
@@ -199,7 +220,7 @@ def run_dense(cfg, steps, warmup, hip, torch, ffn, synth, workload):
     k1 = [hip.ms(evs[nev * s], evs[nev * s + 1]) for s in range(steps)]
     k2 = [hip.ms(evs[nev * s + 1], evs[nev * s + 2]) for s in range(steps)]
     hip.destroy(evs + [t0, t1, t2, t3])
-    flops = workload.dense_flops(cfg.M, cfg.N, cfg.O, cfg.P)
+    flops = (workload.swiglu_flops if gated else workload.dense_flops)(cfg.M, cfg.N, cfg.O, cfg.P)
     nbytes = set_bytes
     ms = total_ms / steps
     return dict(ms_per_step=ms, wall_ms_per_step=1e3 * wall / steps,
@@ -303,10 +324,14 @@ def cpu_baseline(cfg, inputs, rows, synth, workload):
     import oracle  # the reported CPU baseline is the oracle as it stands
     X, W1, b1, W2, b2 = inputs
     sel = np.arange(rows, dtype=np.int64)
+    gated = isinstance(cfg, workload.Gated)
     t0 = time.perf_counter()
-    oracle.ffn(X, W1, b1, W2, b2, act1=oracle.ACT_GELU_TANH, rows=sel)
+    if gated:
+        oracle.swiglu(X, W1, b1, W2, rows=sel)
+    else:
+        oracle.ffn(X, W1, b1, W2, b2, act1=oracle.ACT_GELU_TANH, rows=sel)
     dt = time.perf_counter() - t0
-    flops = workload.dense_flops(rows, cfg.N, cfg.O, cfg.P)
+    flops = (workload.swiglu_flops if gated else workload.dense_flops)(rows, cfg.N, cfg.O, cfg.P)
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": oracle.threads(),
             "kind": "oracle",
             "sample": f"{rows} of {cfg.M} rows of {cfg.name} (fp64, {dt:.2f} s); "
@@ -320,7 +345,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="prefill", choices=["prefill", "decode", "large", "moe", "tiny"])
+    ap.add_argument("--workload", default="prefill",
+                    choices=["prefill", "decode", "large", "moe", "tiny", "swiglu", "swiglu_decode"])
     ap.add_argument("--all", action="store_true", help="also time the large and MoE workloads")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle sample rows (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -344,7 +370,8 @@ def main():
     ffn.lib()  # fail loudly when the library is missing
     hip = Hip()
     cfgs = {"prefill": workload.PREFILL, "decode": workload.DECODE, "large": workload.LARGE,
-            "tiny": workload.TINY_F32, "moe": workload.MOE}
+            "tiny": workload.TINY_F32, "moe": workload.MOE, "swiglu": workload.SWIGLU_PREFILL,
+            "swiglu_decode": workload.SWIGLU_DECODE}
     head = cfgs[args.workload]
     log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {head.name}")
 
@@ -364,8 +391,12 @@ def main():
         if head.M <= 16 and head.dtype == "bf16":
             value = r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
             unit = "GB/s"
-            # layer 1 and layer 2 each stream one weight matrix: count each layer's own bytes
-            k1_bytes = 2 * (head.M * head.N + head.N * head.O + head.O + head.M * head.O)
+            # layer 1 and layer 2 each stream their own weights: count each layer's own bytes
+            # (the gated first layer streams Wg and Wu and has no bias)
+            if isinstance(head, workload.Gated):
+                k1_bytes = 2 * (head.M * head.N + 2 * head.N * head.O + head.M * head.O)
+            else:
+                k1_bytes = 2 * (head.M * head.N + head.N * head.O + head.O + head.M * head.O)
             ach = k1_bytes / (r["k1_ms"] * 1e-3) / 1e9
             roof = {"bound": "hbm", "kernel": "skinny layer 1 (stream + ordered reduce)", "achieved": ach,
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
@@ -375,7 +406,8 @@ def main():
             unit = "TFLOP/s"
             ach = r["flops"] / (r["k1_ms"] * 1e-3) / 1e12
             peak = PEAK_BF16_TFLOPS if head.dtype == "bf16" else 157.3
-            roof = {"bound": "mfma", "kernel": "fused FFN (H in LDS)", "achieved": ach, "peak": peak,
+            kname = "gated fused FFN (H in LDS)" if isinstance(head, workload.Gated) else "fused FFN (H in LDS)"
+            roof = {"bound": "mfma", "kernel": kname, "achieved": ach, "peak": peak,
                     "unit": "TFLOP/s", "frac": ach / peak, "traffic": recorded_traffic(head.name),
                     "kernel_us": 1e3 * r["k1_ms"], "reduce_us": 1e3 * r["k2_ms"]}
 
@@ -390,7 +422,7 @@ def main():
             "kernels_GB_per_s": d["bytes"] / ((d["k1_ms"] + d["k2_ms"]) * 1e-3) / 1e9,
             "rotate": d["rotate"]}
     if args.all:
-        for name in ("large", "moe", "tiny"):
+        for name in ("large", "moe", "tiny", "swiglu", "swiglu_decode"):
             c = cfgs[name]
             if c is head:
                 continue
@@ -404,6 +436,7 @@ def main():
             else:
                 m = run_dense(c, args.steps, args.warmup, hip, torch, ffn, synth, workload)
                 secondary[c.name] = {"TFLOP_per_s": m["flops"] / (m["ms_per_step"] * 1e-3) / 1e12,
+                                     "GB_per_s": m["bytes"] / (m["ms_per_step"] * 1e-3) / 1e9,
                                      "us_per_call": 1e3 * m["ms_per_step"],
                                      "kernel1_us": 1e3 * m["k1_ms"], "kernel2_us": 1e3 * m["k2_ms"]}
 
@@ -436,7 +469,7 @@ def main():
         "dtype": head.dtype,
         "data": "synthetic (seeded normal inputs, random-init weights of the workload's shape)",
         "config": {"workload": head.name, **{k: getattr(head, k) for k in ("M", "N", "O", "P")},
-                   "act1": head.act1, "rotate_input_sets": r["rotate"]},
+                   "act1": getattr(head, "act1", "swiglu"), "rotate_input_sets": r["rotate"]},
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS if unit == "TFLOP/s" else None,
         "roofline": roof,
         "cpu_baseline": cpu,

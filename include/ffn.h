@@ -101,6 +101,38 @@ int ffn_forward_traced(const void* X, const void* W1, const void* b1, const void
                        int dtype, int act1, int act2, int variant, void* workspace,
                        size_t workspace_bytes, void* stream, void** events, int n_events);
 
+/* ---------------------------------------------------------------- SwiGLU
+ * The gated FFN the benchmarked models use (the kernel-fusion post,
+ * brunomaga.github.io, section "Benchmarks": a third weight matrix whose
+ * product with the input gates the activation; no biases):
+ *
+ *     H = silu(X Wg) * (X Wu)      X: M x N, Wg, Wu: N x O   (* elementwise)
+ *     Y = H Wd                     Wd: O x P, Y: M x P
+ *
+ * with silu(x) = x / (1 + exp(-x)) (the page names the unit; this definition
+ * is the published SiLU / Swish-1 one).  Same conventions as ffn_forward: for
+ * a tensor-parallel shard pass the shard's columns of Wg and Wu and rows of Wd
+ * and sum the shards' Y.  H is rounded to bf16 once (bf16 data) and never goes
+ * to global memory on the FUSED family.  Variants as for ffn_forward: AUTO
+ * picks SKINNY for bf16 with M <= 16 (the gated first layer writes H, 16 x O
+ * bf16, to the workspace), FUSED for other bf16 shapes, F32 for fp32 data. */
+size_t ffn_swiglu_workspace_size(int64_t M, int64_t N, int64_t O, int64_t P, int dtype,
+                                 int variant);
+
+/* Y = (silu(X Wg) * (X Wu)) Wd.  All of X, Wg, Wu, Wd, Y in `dtype`; none may be
+ * NULL (X and Y may be NULL when M == 0).  Returns FFN_OK or FFN_E*. */
+int ffn_swiglu_forward(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y,
+                       int64_t M, int64_t N, int64_t O, int64_t P, int dtype, int variant,
+                       void* workspace, size_t workspace_bytes, void* stream);
+
+/* As ffn_swiglu_forward, with events recorded as for ffn_forward_traced:
+ * events[0] before, events[1] between the first kernel (the fused FFN, the
+ * fp32 FFN or the gated first layer) and the rest, events[2] after. */
+int ffn_swiglu_forward_traced(const void* X, const void* Wg, const void* Wu, const void* Wd,
+                              void* Y, int64_t M, int64_t N, int64_t O, int64_t P, int dtype,
+                              int variant, void* workspace, size_t workspace_bytes, void* stream,
+                              void** events, int n_events);
+
 /* ---------------------------------------------------------------- MoE
  * Grouped form over the per-expert token lists of a top-k Mixture-of-Experts
  * layer (the MoE tile-signalling review, zhongzhuzhou.org, sections 2.1-2.2:

@@ -93,6 +93,47 @@ def test_workspace_size_invalid_shapes():
     assert ffn.moe_workspace_size(64, 2, 3, 64, 448, 64) == 0
 
 
+def _swiglu(X=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, Y=FAKE2, M=64, N=64, O=256, P=64, dtype=ffn.BF16,
+            variant=0, ws=FAKE, wsb=0):
+    return ffn.lib().ffn_swiglu_forward(X, Wg, Wu, Wd, Y, M, N, O, P, dtype, variant, ws, wsb, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(X=None), E_INVAL),
+    (dict(Wg=None), E_INVAL),
+    (dict(Wu=None), E_INVAL),
+    (dict(Wd=None), E_INVAL),
+    (dict(Y=None), E_INVAL),
+    (dict(ws=None), E_INVAL),
+    (dict(M=-1), E_INVAL),
+    (dict(O=12), E_UNSUP),
+    (dict(dtype=3), E_INVAL),
+    (dict(variant=9), E_INVAL),
+    (dict(Wu=FAKE + 8), E_ALIGN),
+    (dict(Wd=FAKE + 4), E_ALIGN),
+    (dict(variant=ffn.VARIANT_SKINNY, M=17), E_UNSUP),
+    (dict(dtype=ffn.F32, variant=ffn.VARIANT_SKINNY), E_UNSUP),
+    (dict(), E_WS),
+])
+def test_swiglu_rejects(kw, code):
+    rc = _swiglu(**kw)
+    assert rc == code, (rc, ffn.ffn_last_error())
+    assert ffn.ffn_last_error() != ""
+
+
+def test_swiglu_workspace_sizes():
+    S = ffn.ffn_swiglu_workspace_size
+    fused = S(4096, 4096, 1792, 4096)
+    assert fused >= 7 * 4096 * 4096 * 4         # seven 256-column hidden chunks of fp32 partials
+    assert _swiglu(M=4096, N=4096, O=1792, P=4096, wsb=fused - 1) == E_WS
+    dec = S(16, 4096, 1792, 4096)
+    assert 0 < dec < fused
+    assert _swiglu(M=16, N=4096, O=1792, P=4096, wsb=dec - 1) == E_WS
+    assert S(16, 4096, 1792, 4096, ffn.BF16, ffn.VARIANT_FUSED) == 7 * 16 * 4096 * 4
+    assert S(4, 4, 448, 64) == 0
+    assert S(4, 64, 448, 64, 5) == 0
+
+
 def _moe(**kw):
     a = dict(X=FAKE, logits=FAKE, M=64, E=8, k=2, W1=FAKE, b1=None, W2=FAKE, b2=None, Y=FAKE2,
              N=64, O=448, P=64, dtype=ffn.BF16, act1=2, act2=0, ws=FAKE, wsb=0)

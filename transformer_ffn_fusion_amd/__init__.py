@@ -69,6 +69,13 @@ def lib():
         L.moe_ffn_forward_traced.argtypes = [vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, i64, i64,
                                              i64, i32, i32, i32, vp, sz, vp, evp, i32]
         L.moe_ffn_forward_traced.restype = i32
+        L.ffn_swiglu_workspace_size.argtypes = [i64, i64, i64, i64, i32, i32]
+        L.ffn_swiglu_workspace_size.restype = sz
+        L.ffn_swiglu_forward.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp, sz, vp]
+        L.ffn_swiglu_forward.restype = i32
+        L.ffn_swiglu_forward_traced.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp,
+                                                sz, vp, ctypes.POINTER(vp), i32]
+        L.ffn_swiglu_forward_traced.restype = i32
         L.ffn_last_error.argtypes = []
         L.ffn_last_error.restype = ctypes.c_char_p
         L.ffn_version.restype = i32
@@ -150,6 +157,23 @@ def ffn_forward_ex(X, W1, b1, W2, b2, Y, act1="gelu_tanh", act2="none", variant=
 
 def ffn_forward(X, W1, b1, W2, b2, Y, act1="gelu_tanh", act2="none", ws=None, stream=None):
     return ffn_forward_ex(X, W1, b1, W2, b2, Y, act1, act2, VARIANT_AUTO, ws, stream)
+
+
+def ffn_swiglu_workspace_size(M, N, O, P, dtype=BF16, variant=VARIANT_AUTO) -> int:
+    return lib().ffn_swiglu_workspace_size(M, N, O, P, dtype, variant)
+
+
+def ffn_swiglu_forward(X, Wg, Wu, Wd, Y, variant=VARIANT_AUTO, ws=None, stream=None):
+    """``Y = (silu(X Wg) * (X Wu)) Wd`` on the GPU; ``Y`` is written in place."""
+    M, N = X.shape
+    O = Wg.shape[1]
+    P = Wd.shape[1]
+    dt = _dtype_code(X)
+    if ws is None:
+        ws = workspace(ffn_swiglu_workspace_size(M, N, O, P, dt, variant), X.device)
+    _check(lib().ffn_swiglu_forward(_ptr(X), _ptr(Wg), _ptr(Wu), _ptr(Wd), _ptr(Y), M, N, O, P,
+                                    dt, int(variant), _ptr(ws), ws.numel(), _stream(stream)))
+    return Y
 
 
 def moe_route(logits, k, topk_ids=None, topk_w=None, expert_offsets=None, sorted_entries=None,

@@ -95,6 +95,36 @@ DenseLayout dense_layout(int64_t M, int64_t N, int64_t O, int64_t P, int variant
     return L;
 }
 
+// ---- SwiGLU workspace layouts
+struct SwigluLayout {
+    size_t part = 0;                          // fused / f32: fp32 partials
+    size_t part_g = 0, part_u = 0, h = 0, part2 = 0;  // skinny
+    size_t total = 0;
+};
+
+SwigluLayout swiglu_layout(int64_t M, int64_t N, int64_t O, int64_t P, int variant) {
+    SwigluLayout L;
+    if (variant == FFN_VARIANT_FUSED) {
+        L.total = align_up((size_t)ffn::fused_swiglu_splits(O) * M * P * sizeof(float));
+    } else if (variant == FFN_VARIANT_F32) {
+        const int64_t S = (O + ffn::kF32Chunk - 1) / ffn::kF32Chunk;
+        L.total = align_up((size_t)S * M * P * sizeof(float));
+    } else {
+        size_t off = 0;
+        L.part_g = off;
+        off += align_up(sizeof(float) * ffn::skinny_gated_partial_floats(N, O));
+        L.part_u = off;
+        off += align_up(sizeof(float) * ffn::skinny_gated_partial_floats(N, O));
+        L.h = off;
+        off += align_up(sizeof(uint16_t) * ffn::kSkinnyMaxM * O);
+        L.part2 = off;
+        off += align_up(sizeof(float) * ffn::skinny_partial_floats(O, P));
+        L.total = off;
+    }
+    if (L.total == 0) L.total = kAlign;
+    return L;
+}
+
 // ---- MoE workspace layout
 struct MoeLayout {
     size_t ids, w, counts, offsets, sorted, pos, tiles, tile_count, part, total;
@@ -265,6 +295,105 @@ int ffn_forward(const void* X, const void* W1, const void* b1, const void* W2, c
                 int act2, void* workspace, size_t workspace_bytes, void* stream) {
     return ffn_forward_ex(X, W1, b1, W2, b2, Y, M, N, O, P, dtype, act1, act2,
                           FFN_VARIANT_AUTO, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- SwiGLU
+
+size_t ffn_swiglu_workspace_size(int64_t M, int64_t N, int64_t O, int64_t P, int dtype,
+                                 int variant) {
+    if (check_dims(M, N, O, P) != FFN_OK) return 0;
+    if (dtype != FFN_F32 && dtype != FFN_BF16) return 0;
+    const int v = resolve_variant(variant, dtype, M);
+    if (v < FFN_VARIANT_FUSED || v > FFN_VARIANT_F32) return 0;
+    return swiglu_layout(M, N, O, P, v).total;
+}
+
+static int swiglu_forward(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y,
+                          int64_t M, int64_t N, int64_t O, int64_t P, int dtype, int variant,
+                          void* workspace, size_t workspace_bytes, void* stream, void** events,
+                          int n_events) {
+    if (events && n_events < 3) return fail(FFN_EINVAL, "traced calls take at least 3 events");
+    int rc = check_dims(M, N, O, P);
+    if (rc) return rc;
+    if (dtype != FFN_F32 && dtype != FFN_BF16) return fail(FFN_EINVAL, "unknown dtype %d", dtype);
+    if (variant < FFN_VARIANT_AUTO || variant > FFN_VARIANT_F32)
+        return fail(FFN_EINVAL, "unknown variant %d", variant);
+    if (!Wu) return fail(FFN_EINVAL, "Wu must not be NULL");
+    if (!aligned16(Wu)) return fail(FFN_EALIGN, "Wu is not 16-byte aligned");
+    rc = check_common_ptrs(X, Wg, nullptr, Wd, nullptr, Y, workspace, M);
+    if (rc) return rc;
+    const int v = resolve_variant(variant, dtype, M);
+    if ((v == FFN_VARIANT_F32) != (dtype == FFN_F32))
+        return fail(FFN_EUNSUPPORTED, "variant %d does not take dtype %d", v, dtype);
+    if (v == FFN_VARIANT_SKINNY && M > ffn::kSkinnyMaxM)
+        return fail(FFN_EUNSUPPORTED, "the skinny variant takes M <= %d (got %lld)",
+                    ffn::kSkinnyMaxM, (long long)M);
+    const SwigluLayout L = swiglu_layout(M, N, O, P, v);
+    if (workspace_bytes < L.total)
+        return fail(FFN_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+    if (M == 0) return ok();
+
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    if ((rc = mark(events, n_events, 0, st))) return rc;
+    if (v == FFN_VARIANT_FUSED) {
+        float* part = reinterpret_cast<float*>(ws + L.part);
+        rc = launched(ffn::launch_fused_swiglu_bf16((const uint16_t*)X, (const uint16_t*)Wg,
+                                                    (const uint16_t*)Wu, (const uint16_t*)Wd, part,
+                                                    M, N, O, P, st),
+                      "fused SwiGLU kernel");
+        if (rc) return rc;
+        if ((rc = mark(events, n_events, 1, st))) return rc;
+        rc = launched(ffn::launch_reduce_splits(part, ffn::fused_swiglu_splits(O), nullptr, 0, Y,
+                                                0, M, P, FFN_ACT_NONE, st),
+                      "split reduction kernel");
+        if (rc) return rc;
+    } else if (v == FFN_VARIANT_F32) {
+        const int S = (int)((O + ffn::kF32Chunk - 1) / ffn::kF32Chunk);
+        float* part = reinterpret_cast<float*>(ws + L.part);
+        rc = launched(ffn::launch_fused_swiglu_f32((const float*)X, (const float*)Wg,
+                                                   (const float*)Wu, (const float*)Wd, part, M, N,
+                                                   O, P, st),
+                      "fp32 SwiGLU kernel");
+        if (rc) return rc;
+        if ((rc = mark(events, n_events, 1, st))) return rc;
+        rc = launched(ffn::launch_reduce_splits(part, S, nullptr, 1, Y, 1, M, P, FFN_ACT_NONE, st),
+                      "split reduction kernel");
+        if (rc) return rc;
+    } else {
+        uint16_t* H = reinterpret_cast<uint16_t*>(ws + L.h);
+        rc = launched(ffn::launch_skinny_swiglu_bf16((const uint16_t*)X, (const uint16_t*)Wg,
+                                                     (const uint16_t*)Wu, H,
+                                                     reinterpret_cast<float*>(ws + L.part_g),
+                                                     reinterpret_cast<float*>(ws + L.part_u), M,
+                                                     N, O, st),
+                      "skinny gated layer-1 kernel");
+        if (rc) return rc;
+        if ((rc = mark(events, n_events, 1, st))) return rc;
+        rc = launched(ffn::launch_skinny_bf16(H, (const uint16_t*)Wd, nullptr, (uint16_t*)Y,
+                                              reinterpret_cast<float*>(ws + L.part2), M, O, P,
+                                              FFN_ACT_NONE, st),
+                      "skinny layer-2 kernel");
+        if (rc) return rc;
+    }
+    if ((rc = mark(events, n_events, 2, st))) return rc;
+    return ok();
+}
+
+int ffn_swiglu_forward(const void* X, const void* Wg, const void* Wu, const void* Wd, void* Y,
+                       int64_t M, int64_t N, int64_t O, int64_t P, int dtype, int variant,
+                       void* workspace, size_t workspace_bytes, void* stream) {
+    return swiglu_forward(X, Wg, Wu, Wd, Y, M, N, O, P, dtype, variant, workspace,
+                          workspace_bytes, stream, nullptr, 0);
+}
+
+int ffn_swiglu_forward_traced(const void* X, const void* Wg, const void* Wu, const void* Wd,
+                              void* Y, int64_t M, int64_t N, int64_t O, int64_t P, int dtype,
+                              int variant, void* workspace, size_t workspace_bytes, void* stream,
+                              void** events, int n_events) {
+    if (!events) return fail(FFN_EINVAL, "events must not be NULL");
+    return swiglu_forward(X, Wg, Wu, Wd, Y, M, N, O, P, dtype, variant, workspace,
+                          workspace_bytes, stream, events, n_events);
 }
 
 // ---------------------------------------------------------------- MoE

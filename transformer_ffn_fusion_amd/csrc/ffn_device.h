@@ -56,6 +56,12 @@ __device__ __forceinline__ float gelu_tanh(float x) {
     return x * __builtin_amdgcn_rcpf(1.0f + e);
 }
 
+// silu(x) = x sigmoid(x) = x / (1 + exp(-x)) (the SiLU / Swish-1 unit);
+// saturates as gelu_tanh does: -0 for very negative x, x for large x.
+__device__ __forceinline__ float silu(float x) {
+    return x * __builtin_amdgcn_rcpf(1.0f + __expf(-x));
+}
+
 __device__ __forceinline__ float apply_act(int act, float x) {
     if (act == ACT_RELU) return x > 0.0f ? x : 0.0f;
     if (act == ACT_GELU_TANH) return gelu_tanh(x);

@@ -7,6 +7,9 @@
 // in LDS and multiplies it by the matching rows of W2, writing an fp32 partial
 // of Y per hidden chunk.  The shared split reduction adds b2 once and applies
 // the second activation.  Everything stays fp32 (no rounding to bf16).
+// The gated form (SwiGLU, same post, section "Benchmarks") accumulates the
+// gate product X Wg and the up product X Wu side by side and keeps
+// H = silu(gate) * up; it has no biases.
 #include "ffn_device.h"
 #include "ffn_internal.h"
 
@@ -19,10 +22,11 @@ constexpr int kRows = 8;
 constexpr int kKChunk = 256;
 constexpr int kColsPerThread = kF32Chunk / kThreads;  // 2
 
+template <bool kGated>
 __global__ __launch_bounds__(kThreads) void fused_ffn_f32_kernel(
-    const float* __restrict__ X, const float* __restrict__ W1, const float* __restrict__ b1,
-    const float* __restrict__ W2, float* __restrict__ part, int64_t M, int64_t N, int64_t O,
-    int64_t P, int act1, int splits) {
+    const float* __restrict__ X, const float* __restrict__ W1, const float* __restrict__ W1u,
+    const float* __restrict__ b1, const float* __restrict__ W2, float* __restrict__ part,
+    int64_t M, int64_t N, int64_t O, int64_t P, int act1, int splits) {
     __shared__ float xs[kRows][kKChunk];
     __shared__ float hs[kRows][kF32Chunk];
 
@@ -34,10 +38,11 @@ __global__ __launch_bounds__(kThreads) void fused_ffn_f32_kernel(
     const int64_t o0 = (int64_t)s * kF32Chunk;
 
     float acc[kRows][kColsPerThread];
+    float accu[kRows][kColsPerThread];   // gated form: the up product
 #pragma unroll
     for (int r = 0; r < kRows; ++r)
 #pragma unroll
-        for (int j = 0; j < kColsPerThread; ++j) acc[r][j] = 0.f;
+        for (int j = 0; j < kColsPerThread; ++j) acc[r][j] = accu[r][j] = 0.f;
 
     // layer 1: acc[r][j] = sum_n X[row0 + r][n] W1[n][o0 + tid + 256 j]
     for (int64_t k0 = 0; k0 < N; k0 += kKChunk) {
@@ -50,16 +55,20 @@ __global__ __launch_bounds__(kThreads) void fused_ffn_f32_kernel(
         // unrolled so that many independent W1 loads are in flight at once
 #pragma unroll 16
         for (int kk = 0; kk < kend; ++kk) {
-            float w[kColsPerThread];
+            float w[kColsPerThread], wu[kColsPerThread];
 #pragma unroll
             for (int j = 0; j < kColsPerThread; ++j) {
                 const int64_t o = o0 + tid + kThreads * j;
                 w[j] = o < O ? W1[(k0 + kk) * O + o] : 0.f;
+                if constexpr (kGated) wu[j] = o < O ? W1u[(k0 + kk) * O + o] : 0.f;
             }
 #pragma unroll
             for (int r = 0; r < kRows; ++r)
 #pragma unroll
-                for (int j = 0; j < kColsPerThread; ++j) acc[r][j] = fmaf(xs[r][kk], w[j], acc[r][j]);
+                for (int j = 0; j < kColsPerThread; ++j) {
+                    acc[r][j] = fmaf(xs[r][kk], w[j], acc[r][j]);
+                    if constexpr (kGated) accu[r][j] = fmaf(xs[r][kk], wu[j], accu[r][j]);
+                }
         }
         __syncthreads();
     }
@@ -69,7 +78,12 @@ __global__ __launch_bounds__(kThreads) void fused_ffn_f32_kernel(
         const int64_t o = o0 + ol;
         const float bias = (o < O && b1) ? b1[o] : 0.f;
 #pragma unroll
-        for (int r = 0; r < kRows; ++r) hs[r][ol] = o < O ? apply_act(act1, acc[r][j] + bias) : 0.f;
+        for (int r = 0; r < kRows; ++r) {
+            if constexpr (kGated)
+                hs[r][ol] = o < O ? silu(acc[r][j]) * accu[r][j] : 0.f;
+            else
+                hs[r][ol] = o < O ? apply_act(act1, acc[r][j] + bias) : 0.f;
+        }
     }
     __syncthreads();
 
@@ -98,8 +112,19 @@ hipError_t launch_fused_f32(const float* X, const float* W1, const float* b1, co
     const int splits = (int)((O + kF32Chunk - 1) / kF32Chunk);
     const int64_t rbs = (M + kRows - 1) / kRows;
     if (rbs <= 0) return hipSuccess;
-    hipLaunchKernelGGL(fused_ffn_f32_kernel, dim3((unsigned)(rbs * splits)), dim3(kThreads), 0,
-                       stream, X, W1, b1, W2, part, M, N, O, P, act1, splits);
+    hipLaunchKernelGGL(fused_ffn_f32_kernel<false>, dim3((unsigned)(rbs * splits)), dim3(kThreads),
+                       0, stream, X, W1, nullptr, b1, W2, part, M, N, O, P, act1, splits);
+    return hipGetLastError();
+}
+
+hipError_t launch_fused_swiglu_f32(const float* X, const float* Wg, const float* Wu,
+                                   const float* Wd, float* part, int64_t M, int64_t N, int64_t O,
+                                   int64_t P, hipStream_t stream) {
+    const int splits = (int)((O + kF32Chunk - 1) / kF32Chunk);
+    const int64_t rbs = (M + kRows - 1) / kRows;
+    if (rbs <= 0) return hipSuccess;
+    hipLaunchKernelGGL(fused_ffn_f32_kernel<true>, dim3((unsigned)(rbs * splits)), dim3(kThreads),
+                       0, stream, X, Wg, Wu, nullptr, Wd, part, M, N, O, P, 0, splits);
     return hipGetLastError();
 }
 

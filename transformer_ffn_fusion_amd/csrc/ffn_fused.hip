@@ -27,7 +27,13 @@
 //    so that the address unit's back-pressure never stalls the matrix cores;
 //  * the grouped form (Mixture-of-Experts) takes its rows from a tile table:
 //    expert id, first row of the expert's sorted token list, valid rows; X
-//    rows are gathered by token id on load.
+//    rows are gathered by token id on load;
+//  * the gated form (SwiGLU: same post, section "Benchmarks": a third weight
+//    matrix gates the activation, no biases) keeps the same pipeline.  Its
+//    first product is C wide but covers C/2 hidden columns: the left half of
+//    the W1 stage comes from the gate matrix Wg, the right half from the up
+//    matrix Wu, so each multiplier wave holds the gate and the up value of
+//    the same hidden columns and the epilogue writes silu(gate) * up to H.
 #include "ffn_device.h"
 #include "ffn_internal.h"
 
@@ -40,11 +46,12 @@ constexpr int kThreads = 128 * kMulWaves; // ... plus as many waves that only lo
 constexpr int kBK = 32;                // k-stage depth of both products (one MFMA k-step)
 constexpr int kSub = kBM * kBK * 2;    // one 32-deep slab of X or H in LDS: 4 KiB
 
-template <int C>
+template <int C, bool kGated>
 struct FusedCfg {
-    static constexpr int kFO = C / 64;                 // hidden fragments per multiplier wave (every 4th)
+    static constexpr int kHid = kGated ? C / 2 : C;    // hidden columns per chunk
+    static constexpr int kFO = C / 64;                 // first-product fragments per multiplier wave (every 4th)
     static constexpr int kNB1 = C / 64;                // W1 stage: 64-column blocks per row group
-    static constexpr int kKS = C / kBK;                // GEMM2 k-stages per output pass
+    static constexpr int kKS = kHid / kBK;             // GEMM2 k-stages per output pass
     static constexpr int kW1Stage = 4 * kNB1 * kFrag;  // 32 x C bf16
     static constexpr int kStage1 = kSub + kW1Stage;    // X slab + W1 slab
     static constexpr int kHBytes = kKS * kSub;         // H: C/32 slabs of 64 x 32
@@ -53,6 +60,7 @@ struct FusedCfg {
     static constexpr int kLds1 = kNS1 * kStage1;
     static constexpr int kLds = kLds1 > kHBytes ? kLds1 : kHBytes;
     static_assert(C % 64 == 0, "chunk must split over four waves");
+    static_assert(!kGated || kNB1 % 2 == 0, "gate and up halves are whole 64-column blocks");
     static_assert(kNS1 >= 3, "the multipliers read one stage ahead; the loaders need one more");
     static_assert(kKS % 2 == 0, "GEMM2 runs its stages in pairs");
     static_assert(kBN2 == 64 * 2 * kMulWaves, "each of the eight waves owns 64 columns of a pass");
@@ -61,7 +69,8 @@ struct FusedCfg {
 
 struct FusedArgs {
     const uint16_t* X;
-    const uint16_t* W1;
+    const uint16_t* W1;   // gated form: the gate matrix Wg
+    const uint16_t* W1u;  // gated form: the up matrix Wu (unused otherwise)
     const uint16_t* b1;
     const uint16_t* W2;
     float* part;
@@ -105,9 +114,10 @@ __device__ __forceinline__ void map_unit(int64_t unit, int64_t row_blocks, int s
 // the previous iteration, then the loaders refill that buffer while the
 // multipliers work on the current one.  Loads past the end of K are never
 // issued; the last iterations wait for every load still in flight instead.
-template <int C, bool kGrouped>
+template <int C, bool kGrouped, bool kGated>
 __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a) {
-    using Cfg = FusedCfg<C>;
+    using Cfg = FusedCfg<C, kGated>;
+    static_assert(!(kGrouped && kGated), "the grouped form is not gated");
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
     const int tid = threadIdx.x;
@@ -141,8 +151,8 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     const uint16_t* W1 = a.W1 + expert * a.g.w1_stride;
     const uint16_t* W2 = a.W2 + expert * a.g.w2_stride;
     const uint16_t* b1 = a.b1 ? a.b1 + expert * a.g.b1_stride : nullptr;
-    const int64_t o0 = (int64_t)s * C;
-    const int64_t oc = (O - o0) < C ? (O - o0) : C;  // valid hidden columns of this chunk
+    const int64_t o0 = (int64_t)s * Cfg::kHid;
+    const int64_t oc = (O - o0) < Cfg::kHid ? (O - o0) : Cfg::kHid;  // valid hidden columns of this chunk
 
     // ---- X slab loads: loader w fills fragment w (rows 16w..16w+15); lane l
     // brings row 16w + l/4, k-group xc into fragment slot l (see xfrag_slot).
@@ -162,6 +172,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     // past this chunk's valid width read finite neighbours whose H columns the
     // epilogue forces to zero.
     const int32x4_t rw1 = make_srd(W1 + o0, (N * O - o0) * 2);
+    const int32x4_t rw1u = kGated ? make_srd(a.W1u + o0, (N * O - o0) * 2) : rw1;
     const uint32_t w1_lane = wtile_dma_off(lane, (uint32_t)(O * 2));
 
     const int64_t nk = (N + kBK - 1) / kBK;
@@ -203,8 +214,12 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
             for (int b = 0; b < Cfg::kNB1; ++b) {
                 const int blk = w4 + kMulWaves * b;
                 const int r = blk / Cfg::kNB1, c = blk % Cfg::kNB1;
-                const uint32_t base = (uint32_t)(((kt * kBK + 8 * r) * O + 64 * c) * 2);
-                dma16(rw1, real ? base + w1_lane : kOOB, st + kSub + blk * kFrag);
+                // gated form: blocks c < kNB1/2 hold gate columns, the rest the up
+                // columns of the same hidden indices
+                const bool up = kGated && c >= Cfg::kNB1 / 2;
+                const int cc = up ? c - Cfg::kNB1 / 2 : c;
+                const uint32_t base = (uint32_t)(((kt * kBK + 8 * r) * O + 64 * cc) * 2);
+                dma16(up ? rw1u : rw1, real ? base + w1_lane : kOOB, st + kSub + blk * kFrag);
             }
         };
 #pragma unroll
@@ -286,9 +301,13 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
         }
         __syncthreads();   // every multiplier is done with the GEMM1 ring
 
-        // ---- epilogue 1: H = act(A + b1) -> bf16 -> LDS (GEMM2 operand layout)
+        // ---- epilogue 1: H = act(A + b1) -> bf16 -> LDS (GEMM2 operand layout).
+        // Gated form: fragment fo (< kFO/2) holds gate columns and fragment
+        // fo + kFO/2 the up columns of the same hidden indices (block fo of the
+        // W1 stage is fragment fo of every wave), so H = silu(gate) * up.
+        // Both forms round H to bf16 once.
 #pragma unroll
-        for (int fo = 0; fo < Cfg::kFO; ++fo) {
+        for (int fo = 0; fo < (kGated ? Cfg::kFO / 2 : Cfg::kFO); ++fo) {
             const int ol = 16 * (w4 + kMulWaves * fo) + 4 * lg;  // first of 4 hidden cols
             const int64_t og = o0 + ol;
             float bias[4] = {0.f, 0.f, 0.f, 0.f};
@@ -307,8 +326,12 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
             for (int fm = 0; fm < 4; ++fm) {
                 float h[4];
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    h[r] = colok ? apply_act(a.act1, acc[fo][fm][r] + bias[r]) : 0.f;
+                for (int r = 0; r < 4; ++r) {
+                    if constexpr (kGated)
+                        h[r] = colok ? silu(acc[fo][fm][r]) * acc[fo + Cfg::kFO / 2][fm][r] : 0.f;
+                    else
+                        h[r] = colok ? apply_act(a.act1, acc[fo][fm][r] + bias[r]) : 0.f;
+                }
                 uint2 pk = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
                 *reinterpret_cast<uint2*>(hreg + slab * kSub + frag_off(16 * fm + li, g) + 2 * e) = pk;
             }
@@ -449,10 +472,10 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
     }
 }
 
-template <int C, bool G>
+template <int C, bool G, bool kGated = false>
 hipError_t launch_fused_impl(const FusedArgs& a, int64_t units, hipStream_t stream) {
-    using Cfg = FusedCfg<C>;
-    auto kern = fused_ffn_bf16_kernel<C, G>;
+    using Cfg = FusedCfg<C, kGated>;
+    auto kern = fused_ffn_bf16_kernel<C, G, kGated>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -485,6 +508,7 @@ hipError_t launch_fused_bf16(const uint16_t* X, const uint16_t* W1, const uint16
     FusedArgs a;
     a.X = X;
     a.W1 = W1;
+    a.W1u = nullptr;
     a.b1 = b1;
     a.W2 = W2;
     a.part = part;
@@ -504,6 +528,33 @@ hipError_t launch_fused_bf16(const uint16_t* X, const uint16_t* W1, const uint16
                        : launch_fused_impl<448, false>(a, units, stream);
     return grouped ? launch_fused_impl<512, true>(a, units, stream)
                    : launch_fused_impl<512, false>(a, units, stream);
+}
+
+int fused_swiglu_splits(int64_t O) {
+    return (int)((O + FusedCfg<kSwigluChunk, true>::kHid - 1) / FusedCfg<kSwigluChunk, true>::kHid);
+}
+
+hipError_t launch_fused_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
+                                    const uint16_t* Wd, float* part, int64_t M, int64_t N,
+                                    int64_t O, int64_t P, hipStream_t stream) {
+    FusedArgs a;
+    a.X = X;
+    a.W1 = Wg;
+    a.W1u = Wu;
+    a.b1 = nullptr;
+    a.W2 = Wd;
+    a.part = part;
+    a.M = M;
+    a.N = N;
+    a.O = O;
+    a.P = P;
+    a.rows_out = M;
+    a.row_blocks = (M + kBM - 1) / kBM;
+    a.splits = fused_swiglu_splits(O);
+    a.act1 = 0;
+    const int64_t units = a.row_blocks * a.splits;
+    if (units <= 0) return hipSuccess;
+    return launch_fused_impl<kSwigluChunk, false, true>(a, units, stream);
 }
 
 hipError_t launch_reduce_splits(const float* part, int splits, const void* b2, int b2_f32,

@@ -32,6 +32,14 @@ hipError_t launch_fused_bf16(const uint16_t* X, const uint16_t* W1, const uint16
                              int64_t O, int64_t P, int act1, int chunk, int64_t row_blocks,
                              int64_t rows_out, const GroupedRows* grouped, hipStream_t stream);
 
+// SwiGLU form: part[s][row][p] for the hidden chunk s of kSwigluChunk/2
+// columns: H = silu(X Wg) * (X Wu) rounded to bf16, times the rows of Wd.
+constexpr int kSwigluChunk = 512;                // first-product width (gate + up)
+int fused_swiglu_splits(int64_t O);              // ceil(O / (kSwigluChunk / 2))
+hipError_t launch_fused_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
+                                    const uint16_t* Wd, float* part, int64_t M, int64_t N,
+                                    int64_t O, int64_t P, hipStream_t stream);
+
 // Y[m][p] = act2(sum_s part[s][m][p] + b2[p]) in ascending s; bf16 or fp32 out.
 hipError_t launch_reduce_splits(const float* part, int splits, const void* b2, int b2_f32,
                                 void* Y, int y_f32, int64_t M, int64_t P, int act2,
@@ -50,12 +58,22 @@ hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* W, const uint16
                               uint16_t* out, float* part, int64_t M, int64_t K, int64_t Ncol,
                               int act, hipStream_t stream);
 
+// Gated first layer: out = bf16(silu(A Wg) * (A Wu)); both products write
+// K-block partials (skinny_gated_partial_floats each), no bias.
+size_t skinny_gated_partial_floats(int64_t K, int64_t Ncol);
+hipError_t launch_skinny_swiglu_bf16(const uint16_t* A, const uint16_t* Wg, const uint16_t* Wu,
+                                     uint16_t* out, float* part_g, float* part_u, int64_t M,
+                                     int64_t K, int64_t Ncol, hipStream_t stream);
+
 // ---- fp32 path
 
 constexpr int kF32Chunk = 512;
 hipError_t launch_fused_f32(const float* X, const float* W1, const float* b1, const float* W2,
                             float* part, int64_t M, int64_t N, int64_t O, int64_t P, int act1,
                             hipStream_t stream);
+hipError_t launch_fused_swiglu_f32(const float* X, const float* Wg, const float* Wu,
+                                   const float* Wd, float* part, int64_t M, int64_t N, int64_t O,
+                                   int64_t P, hipStream_t stream);
 
 // ---- Mixture-of-Experts
 

@@ -21,6 +21,11 @@
 //    device-scope release per workgroup; on this part that fence writes back
 //    the XCD's L2 and the workgroups of an XCD serialise on it -- measured at
 //    ~20 us per layer, against ~1.5 us for the loads and the math.)
+//
+// Gated first layer (SwiGLU: same post, section "Benchmarks"): the grid gets a
+// second z-slice that streams the up matrix Wu beside the gate matrix Wg, both
+// slices always write partials, and the reduction forms
+// H = silu(sum gate) * (sum up) before its single rounding to bf16.
 #include "ffn_device.h"
 #include "ffn_internal.h"
 
@@ -34,13 +39,16 @@ constexpr int kBatch = 8;    // partials the last arriver loads at once
 struct SkinnyArgs {
     const uint16_t* A;
     const uint16_t* W;
+    const uint16_t* Wu;   // gated: the up matrix (grid z-slice 1)
     const uint16_t* bias;
     uint16_t* out;
     float* part;        // [nkb][16][Ncol]
+    float* part_u;      // gated: partials of the up product
     int64_t M, K, Ncol;
     int64_t kblock;
     int nkb;
     int act;
+    int gated;
 };
 
 template <int KSTEPS>
@@ -60,7 +68,7 @@ __global__ __launch_bounds__(kThreads) void skinny_bf16_kernel(SkinnyArgs a) {
 
     // ---- issue every load of this lane first (out-of-range rows/columns read zeros)
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(a.A, a.M * K * 2);
-    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.W, K * Ncol * 2);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(blockIdx.z ? a.Wu : a.W, K * Ncol * 2);
     const uint32_t arow = (uint32_t)(c * K * 2);
     uint4 af[KSTEPS];
     uint4 wr[KSTEPS][8];
@@ -105,9 +113,9 @@ __global__ __launch_bounds__(kThreads) void skinny_bf16_kernel(SkinnyArgs a) {
     const int64_t gc = cb * kSkinnyCols + cl;
     const bool outok = (m < a.M) && (gc < Ncol);
 
-    if (a.nkb > 1) {
+    if (a.nkb > 1 || a.gated) {
         if (gc < Ncol) {
-            float* mine = a.part + ((int64_t)kb * kSkinnyMaxM + m) * Ncol + gc;
+            float* mine = (blockIdx.z ? a.part_u : a.part) + ((int64_t)kb * kSkinnyMaxM + m) * Ncol + gc;
             *reinterpret_cast<float4*>(mine) = make_float4(v[0], v[1], v[2], v[3]);
             *reinterpret_cast<float4*>(mine + 4) = make_float4(v[4], v[5], v[6], v[7]);
         }
@@ -130,21 +138,10 @@ __global__ __launch_bounds__(kThreads) void skinny_bf16_kernel(SkinnyArgs a) {
     *reinterpret_cast<uint4*>(a.out + (int64_t)m * Ncol + gc) = o;
 }
 
-// out[m][c] = act(sum_kb part[kb][m][c] + bias[c]), K blocks in ascending order.
-// One thread per 4 output columns; small blocks so the few thousand threads
-// spread over many CUs (the partials are L2/MALL-resident, just written).
-__global__ __launch_bounds__(64) void skinny_reduce_kernel(const float* __restrict__ part, int nkb,
-                                                           const uint16_t* __restrict__ bias,
-                                                           uint16_t* __restrict__ out, int64_t M,
-                                                           int64_t Ncol, int act) {
-    const int64_t nvec = M * (Ncol / 4);
-    const int64_t v = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
-    if (v >= nvec) return;
-    const int64_t m = v / (Ncol / 4);
-    const int64_t c = (v - m * (Ncol / 4)) * 4;
-    const float* src = part + m * Ncol + c;
-    const int64_t kstride = (int64_t)kSkinnyMaxM * Ncol;
-    float y[4] = {0.f, 0.f, 0.f, 0.f};
+// Sum of the K-block partials of 4 columns, K blocks in ascending order.
+__device__ __forceinline__ void sum_kblocks(const float* src, int nkb, int64_t kstride,
+                                            float (&y)[4]) {
+    y[0] = y[1] = y[2] = y[3] = 0.f;
     for (int q0 = 0; q0 < nkb; q0 += 2 * kBatch) {
         float4 t[2 * kBatch];
 #pragma unroll
@@ -158,6 +155,36 @@ __global__ __launch_bounds__(64) void skinny_reduce_kernel(const float* __restri
                 y[0] += t[j].x; y[1] += t[j].y; y[2] += t[j].z; y[3] += t[j].w;
             }
         }
+    }
+}
+
+// out[m][c] = act(sum_kb part[kb][m][c] + bias[c]), K blocks in ascending order;
+// gated: out[m][c] = silu(sum_kb part[kb][m][c]) * sum_kb part_u[kb][m][c].
+// One thread per 4 output columns; small blocks so the few thousand threads
+// spread over many CUs (the partials are L2/MALL-resident, just written).
+template <bool kGated>
+__global__ __launch_bounds__(64) void skinny_reduce_kernel(const float* __restrict__ part,
+                                                           const float* __restrict__ part_u,
+                                                           int nkb,
+                                                           const uint16_t* __restrict__ bias,
+                                                           uint16_t* __restrict__ out, int64_t M,
+                                                           int64_t Ncol, int act) {
+    const int64_t nvec = M * (Ncol / 4);
+    const int64_t v = blockIdx.x * (int64_t)blockDim.x + threadIdx.x;
+    if (v >= nvec) return;
+    const int64_t m = v / (Ncol / 4);
+    const int64_t c = (v - m * (Ncol / 4)) * 4;
+    const int64_t kstride = (int64_t)kSkinnyMaxM * Ncol;
+    float y[4];
+    sum_kblocks(part + m * Ncol + c, nkb, kstride, y);
+    if constexpr (kGated) {
+        float u[4];
+        sum_kblocks(part_u + m * Ncol + c, nkb, kstride, u);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) y[i] = silu(y[i]) * u[i];
+        *reinterpret_cast<uint2*>(out + m * Ncol + c) =
+            make_uint2(pack_bf16x2(y[0], y[1]), pack_bf16x2(y[2], y[3]));
+        return;
     }
     if (bias) {
         const uint2 bb = *reinterpret_cast<const uint2*>(bias + c);
@@ -184,6 +211,10 @@ size_t skinny_partial_floats(int64_t K, int64_t Ncol) {
     return nkb > 1 ? (size_t)(nkb * kSkinnyMaxM * Ncol) : 0;
 }
 
+size_t skinny_gated_partial_floats(int64_t K, int64_t Ncol) {
+    return (size_t)(((K + kKBlock - 1) / kKBlock) * kSkinnyMaxM * Ncol);
+}
+
 
 hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* W, const uint16_t* bias,
                               uint16_t* out, float* part, int64_t M, int64_t K, int64_t Ncol,
@@ -191,9 +222,12 @@ hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* W, const uint16
     SkinnyArgs a;
     a.A = A;
     a.W = W;
+    a.Wu = W;
     a.bias = bias;
     a.out = out;
     a.part = part;
+    a.part_u = part;
+    a.gated = 0;
     a.M = M;
     a.K = K;
     a.Ncol = Ncol;
@@ -205,8 +239,36 @@ hipError_t launch_skinny_bf16(const uint16_t* A, const uint16_t* W, const uint16
     hipError_t e = hipGetLastError();
     if (e != hipSuccess || a.nkb <= 1) return e;
     const int64_t nvec = M * (Ncol / 4);
-    hipLaunchKernelGGL(skinny_reduce_kernel, dim3((unsigned)((nvec + 63) / 64)), dim3(64), 0,
-                       stream, part, a.nkb, bias, out, M, Ncol, act);
+    hipLaunchKernelGGL(skinny_reduce_kernel<false>, dim3((unsigned)((nvec + 63) / 64)), dim3(64), 0,
+                       stream, part, part, a.nkb, bias, out, M, Ncol, act);
+    return hipGetLastError();
+}
+
+hipError_t launch_skinny_swiglu_bf16(const uint16_t* A, const uint16_t* Wg, const uint16_t* Wu,
+                                     uint16_t* out, float* part_g, float* part_u, int64_t M,
+                                     int64_t K, int64_t Ncol, hipStream_t stream) {
+    SkinnyArgs a;
+    a.A = A;
+    a.W = Wg;
+    a.Wu = Wu;
+    a.bias = nullptr;
+    a.out = out;
+    a.part = part_g;
+    a.part_u = part_u;
+    a.M = M;
+    a.K = K;
+    a.Ncol = Ncol;
+    a.kblock = kKBlock;
+    a.nkb = (int)((K + kKBlock - 1) / kKBlock);
+    a.act = 0;
+    a.gated = 1;
+    dim3 grid((unsigned)((Ncol + kSkinnyCols - 1) / kSkinnyCols), (unsigned)a.nkb, 2);
+    hipLaunchKernelGGL(skinny_bf16_kernel<kKSteps>, grid, dim3(kThreads), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int64_t nvec = M * (Ncol / 4);
+    hipLaunchKernelGGL(skinny_reduce_kernel<true>, dim3((unsigned)((nvec + 63) / 64)), dim3(64), 0,
+                       stream, part_g, part_u, a.nkb, nullptr, out, M, Ncol, 0);
     return hipGetLastError();
 }
 

@@ -55,6 +55,23 @@ MOE = MoE("moe_top2_4096tok_8x4096x2048x4096", 4096, 8, 2, 4096, 2048, 4096, "bf
 ALL = (TINY_F32, DECODE, PREFILL, LARGE, MOE)
 
 
+@dataclass(frozen=True)
+class Gated:
+    """A SwiGLU FFN shard: (silu(X Wg) * (X Wu)) Wd, no biases (the kernel-fusion
+    post, section "Benchmarks": the benchmarked models are SwiGLU models)."""
+    name: str
+    M: int
+    N: int
+    O: int
+    P: int
+    dtype: str
+
+
+# the same one-GPU shard as PREFILL/DECODE (1792 = 14,336 / 8), with the gated FFN
+SWIGLU_PREFILL = Gated("swiglu_prefill_shard_4096x4096x1792x4096", 4096, 4096, 1792, 4096, "bf16")
+SWIGLU_DECODE = Gated("swiglu_decode_shard_16x4096x1792x4096", 16, 4096, 1792, 4096, "bf16")
+
+
 def esize(dtype: str) -> int:
     return 2 if dtype == "bf16" else 4
 
@@ -67,6 +84,16 @@ def dense_bytes(M, N, O, P, es=2, bias=True) -> int:
     """X + W1 + b1 + W2 + b2 + Y."""
     b = (O + P) if bias else 0
     return es * (M * N + N * O + O * P + M * P + b)
+
+
+def swiglu_flops(M, N, O, P) -> int:
+    """Two N x O products (gate and up) and one O x P product per row."""
+    return 2 * M * (2 * N * O + O * P)
+
+
+def swiglu_bytes(M, N, O, P, es=2) -> int:
+    """X + Wg + Wu + Wd + Y."""
+    return es * (M * N + 2 * N * O + O * P + M * P)
 
 
 def moe_flops(rows, N, O, P) -> int:
