@@ -124,12 +124,13 @@ def test_swiglu_rejects(kw, code):
 def test_swiglu_workspace_sizes():
     S = ffn.ffn_swiglu_workspace_size
     fused = S(4096, 4096, 1792, 4096)
-    assert fused >= 7 * 4096 * 4096 * 4         # seven 256-column hidden chunks of fp32 partials
+    assert fused >= 4 * 4096 * 4096 * 4         # four 448-column hidden chunks of fp32 partials
     assert _swiglu(M=4096, N=4096, O=1792, P=4096, wsb=fused - 1) == E_WS
     dec = S(16, 4096, 1792, 4096)
     assert 0 < dec < fused
     assert _swiglu(M=16, N=4096, O=1792, P=4096, wsb=dec - 1) == E_WS
-    assert S(16, 4096, 1792, 4096, ffn.BF16, ffn.VARIANT_FUSED) == 7 * 16 * 4096 * 4
+    assert S(16, 4096, 1792, 4096, ffn.BF16, ffn.VARIANT_FUSED) == 4 * 16 * 4096 * 4
+    assert S(16, 4096, 2048, 4096, ffn.BF16, ffn.VARIANT_FUSED) == 8 * 16 * 4096 * 4  # 256-wide
     assert S(4, 4, 448, 64) == 0
     assert S(4, 64, 448, 64, 5) == 0
 

@@ -35,11 +35,13 @@ def _run(M, N, O, P, *, dtype="bf16", variant=0, seed=0, rows=None, repeat=1):
 
 
 @pytest.mark.parametrize("shape", [
-    (1, 64, 256, 512),       # one row, one hidden chunk, one output pass
-    (65, 264, 456, 520),     # ragged rows, k tail, ragged second chunk, ragged output pass
-    (130, 512, 1792, 1032),  # 7 chunks of 256, 3 row tiles (last ragged)
-    (200, 128, 1024, 64),    # 4 chunks, narrow output
-    (64, 1000, 904, 1544),   # ragged everywhere
+    (1, 64, 256, 512),       # one row, one 256-column chunk (one pass), one output pass
+    (65, 264, 456, 520),     # two-pass chunks of 448: the second holds 8 columns (pass B empty)
+    (130, 512, 1792, 1032),  # 4 two-pass chunks of 448, 3 row tiles (last ragged)
+    (96, 192, 896, 520),     # 2 two-pass chunks, ragged output pass
+    (200, 128, 1024, 64),    # 4 one-pass chunks of 256, narrow output
+    (64, 1000, 904, 1544),   # ragged everywhere: chunks 448, 448, 8
+    (33, 96, 2048, 256),     # 8 one-pass chunks of 256
 ])
 def test_swiglu_fused_shapes(shape):
     M, N, O, P = shape

@@ -46,22 +46,46 @@ constexpr int kThreads = 128 * kMulWaves; // ... plus as many waves that only lo
 constexpr int kBK = 32;                // k-stage depth of both products (one MFMA k-step)
 constexpr int kSub = kBM * kBK * 2;    // one 32-deep slab of X or H in LDS: 4 KiB
 
-template <int C, bool kGated>
-struct FusedCfg {
-    static constexpr int kHid = kGated ? C / 2 : C;    // hidden columns per chunk
-    static constexpr int kFO = C / 64;                 // first-product fragments per multiplier wave (every 4th)
-    static constexpr int kNB1 = C / 64;                // W1 stage: 64-column blocks per row group
-    static constexpr int kKS = kHid / kBK;             // GEMM2 k-stages per output pass
-    static constexpr int kW1Stage = 4 * kNB1 * kFrag;  // 32 x C bf16
+// One first-product pass: a stage of 32 k-rows of X (64 rows) and of CP
+// columns of W1, held in an NS-deep LDS ring.
+template <int CP>
+struct PassCfg {
+    static constexpr int kNB1 = CP / 64;               // W1 stage: 64-column blocks per row group
+    static constexpr int kFO = CP / 64;                // fragments per multiplier wave (every 4th)
+    static constexpr int kW1Stage = 4 * kNB1 * kFrag;  // 32 x CP bf16
     static constexpr int kStage1 = kSub + kW1Stage;    // X slab + W1 slab
-    static constexpr int kHBytes = kKS * kSub;         // H: C/32 slabs of 64 x 32
-    static constexpr int kNS1 = 4;                     // GEMM1 stages in the LDS ring
-    static constexpr int kD1 = 1 + kNB1;               // loads per loader wave per GEMM1 stage
+    static constexpr int kNS1 = 4;                     // stages in the LDS ring
+    static constexpr int kD1 = 1 + kNB1;               // loads per loader wave per stage
     static constexpr int kLds1 = kNS1 * kStage1;
-    static constexpr int kLds = kLds1 > kHBytes ? kLds1 : kHBytes;
-    static_assert(C % 64 == 0, "chunk must split over four waves");
-    static_assert(!kGated || kNB1 % 2 == 0, "gate and up halves are whole 64-column blocks");
+    static_assert(CP % 64 == 0, "a pass splits over four waves in 16-column fragments");
     static_assert(kNS1 >= 3, "the multipliers read one stage ahead; the loaders need one more");
+};
+
+// Kernel configuration: pass A of CA first-product columns and, when CB > 0,
+// a second pass B of CB columns over the next hidden columns of the chunk.
+// The gated form halves each pass into gate and up columns (hidden columns
+// per pass = CP / 2).  H is kKS slabs of 64 x 32 at LDS offset kHOff: slabs
+// 0 .. kSlabsB-1 hold pass B's hidden columns, the rest pass A's.  With two
+// passes, pass B's ring ends where pass A's H begins (pass A's H must survive
+// pass B) and pass B's own H goes into the top of its ring once the pass is
+// over, so H is contiguous and the whole kernel needs max(ring A, ring B + H A).
+template <int CA, int CB, bool kGated>
+struct FusedCfg {
+    using PA = PassCfg<CA>;
+    using PB = PassCfg<(CB > 0 ? CB : 64)>;            // unused with one pass
+    static constexpr bool kTwoPass = CB > 0;
+    static constexpr int kHidA = kGated ? CA / 2 : CA;
+    static constexpr int kHidB = kTwoPass ? (kGated ? CB / 2 : CB) : 0;
+    static constexpr int kHid = kHidA + kHidB;         // hidden columns per chunk
+    static constexpr int kKS = kHid / kBK;             // GEMM2 k-stages per output pass
+    static constexpr int kSlabsB = kHidB / kBK;
+    static constexpr int kHOff = kTwoPass ? PB::kLds1 - kSlabsB * kSub : 0;
+    static constexpr int kHEnd = kHOff + kKS * kSub;
+    static constexpr int kLds = PA::kLds1 > kHEnd ? PA::kLds1 : kHEnd;
+    static_assert(kHidA % kBK == 0 && kHidB % kBK == 0, "passes cover whole H slabs");
+    static_assert(!kGated || (PA::kNB1 % 2 == 0 && (!kTwoPass || PB::kNB1 % 2 == 0)),
+                  "gate and up halves are whole 64-column blocks");
+    static_assert(!kTwoPass || kGated, "two passes are used by the gated form only");
     static_assert(kKS % 2 == 0, "GEMM2 runs its stages in pairs");
     static_assert(kBN2 == 64 * 2 * kMulWaves, "each of the eight waves owns 64 columns of a pass");
     static_assert(kLds <= 160 * 1024, "LDS budget");
@@ -104,6 +128,16 @@ __device__ __forceinline__ void map_unit(int64_t unit, int64_t row_blocks, int s
     }
 }
 
+// What both roles of a first-product pass share.
+struct G1Ctx {
+    char* smem;
+    int32x4_t rx;        // X rows of the tile
+    uint32_t xrow_off;   // this loader lane's X row (kOOB past the valid rows)
+    uint32_t w1_lane;    // this lane's slot offset inside a W1 block
+    int64_t N, O, nk, nk2, rot1;
+    int w4, xc, lane;
+};
+
 // Both products run the same pipeline, split between two kinds of wave.  The
 // four loader waves only issue direct global->LDS loads; the four multiplier
 // waves only read LDS and issue MFMAs.  Each SIMD holds one wave of each kind,
@@ -114,9 +148,163 @@ __device__ __forceinline__ void map_unit(int64_t unit, int64_t row_blocks, int s
 // the previous iteration, then the loaders refill that buffer while the
 // multipliers work on the current one.  Loads past the end of K are never
 // issued; the last iterations wait for every load still in flight instead.
-template <int C, bool kGrouped, bool kGated>
+// The two roles run separate loops that execute the same number of barriers
+// per pass: nk2 + 2.
+
+// Loader side of one pass.  rw1 / rw1u start at the pass's first gate / up
+// column (dense form: rw1 at the first W1 column; rw1u unused).
+template <class PC, bool kGated>
+__device__ __forceinline__ void gemm1_loads(const G1Ctx& c, int32x4_t rw1, int32x4_t rw1u) {
+    // loads of the i-th stage in walking order (K stage (i + rot1) mod nk); the
+    // padding stage i == nk of an odd stage count reads zeros
+    auto issue1 = [&](int64_t i, int buf) {
+        const bool real = i < c.nk;
+        const int64_t kt = !real ? 0 : (i + c.rot1 < c.nk ? i + c.rot1 : i + c.rot1 - c.nk);
+        char* st = c.smem + buf * PC::kStage1;
+        const int64_t kx = kt * kBK + 8 * c.xc;
+        dma16(c.rx, real && kx < c.N ? c.xrow_off + (uint32_t)(kx * 2) : kOOB, st + c.w4 * kFrag);
+#pragma unroll
+        for (int b = 0; b < PC::kNB1; ++b) {
+            const int blk = c.w4 + kMulWaves * b;
+            const int r = blk / PC::kNB1, cb = blk % PC::kNB1;
+            // gated form: blocks cb < kNB1/2 hold gate columns, the rest the up
+            // columns of the same hidden indices
+            const bool up = kGated && cb >= PC::kNB1 / 2;
+            const int cc = up ? cb - PC::kNB1 / 2 : cb;
+            const uint32_t base = (uint32_t)(((kt * kBK + 8 * r) * c.O + 64 * cc) * 2);
+            dma16(up ? rw1u : rw1, real ? base + c.w1_lane : kOOB, st + kSub + blk * kFrag);
+        }
+    };
+#pragma unroll
+    for (int i = 0; i < PC::kNS1 - 1; ++i)
+        if (i < c.nk2) issue1(i, i);
+    // barrier -1 publishes stage 0; barrier kt publishes stage kt + 1 (the
+    // multipliers read one stage ahead of the one they multiply)
+    if (PC::kNS1 - 2 < c.nk2) wait_vmcnt<PC::kD1 * (PC::kNS1 - 2)>();
+    else wait_vmcnt<0>();
+    __syncthreads();
+    int ibuf = PC::kNS1 - 1;
+    for (int64_t kt = 0; kt < c.nk2; ++kt) {
+        // stages kt+1 .. min(kt + NS1 - 2, nk2 - 1) may be in flight
+        if (kt + PC::kNS1 - 2 < c.nk2) wait_vmcnt<PC::kD1 * (PC::kNS1 - 3)>();
+        else wait_vmcnt<0>();
+        __syncthreads();
+        if (kt + PC::kNS1 - 1 < c.nk2) issue1(kt + PC::kNS1 - 1, ibuf);
+        ibuf = (ibuf + 1 == PC::kNS1) ? 0 : ibuf + 1;
+    }
+    __syncthreads();   // the multipliers are done with the ring
+}
+
+// Multiplier side of one pass: A^T = W1_pass^T X^T into acc[fo][fm] (hidden
+// fragment w4 + 4 fo, row fragment fm).
+template <class PC>
+__device__ __forceinline__ void gemm1_mma(const G1Ctx& c, floatx4_t (&acc)[PC::kFO][4]) {
+    const int li = c.lane & 15, lg = c.lane >> 4;
+#pragma unroll
+    for (int i = 0; i < PC::kFO; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+    const int xoff = 16 * xfrag_slot(li, lg);
+    // multiplier w owns hidden fragments w, w+4, w+8, ...: f % 4 == w
+    const uint32_t trw1 = wtile_tr_base(c.lane, PC::kNB1, c.w4);
+    // Software pipeline: after barrier kt (which publishes stage kt+1) the
+    // multiplier reads stage kt+1 while it multiplies stage kt from registers
+    // read one iteration earlier.  The reads are spread over the MFMAs (the X
+    // fragments first, then one W fragment ahead of each group of four MFMAs),
+    // so the LDS sees a steady stream and its latency hides behind the matrix
+    // work.  A read past the last stage fetches a stale buffer that is never
+    // multiplied.
+    auto step = [&](int buf, uint4 (&xn)[4], uint4 (&wn)[PC::kFO], const uint4 (&xcur)[4],
+                    const uint4 (&wcur)[PC::kFO]) {
+        const char* st = c.smem + buf * PC::kStage1;
+        const char* sw = st + kSub + trw1;
+#pragma unroll
+        for (int fm = 0; fm < 4; ++fm) xn[fm] = ld16(st + fm * kFrag + xoff);
+#pragma unroll
+        for (int fo = 0; fo < PC::kFO; ++fo) {
+            const uint2 lo = lds_read_tr16(sw + 1024 * fo);
+            const uint2 hi = lds_read_tr16(sw + 1024 * fo + 512);
+            wn[fo] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int fm = 0; fm < 4; ++fm)
+                acc[fo][fm] = mfma16x16x32(wcur[fo], xcur[fm], acc[fo][fm]);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+    };
+    uint4 xa[4], wa[PC::kFO], xb[4], wb[PC::kFO];
+    __syncthreads();
+    {
+        const char* st = c.smem;
+#pragma unroll
+        for (int fm = 0; fm < 4; ++fm) xa[fm] = ld16(st + fm * kFrag + xoff);
+#pragma unroll
+        for (int fo = 0; fo < PC::kFO; ++fo) {
+            const uint2 lo = lds_read_tr16(st + kSub + trw1 + 1024 * fo);
+            const uint2 hi = lds_read_tr16(st + kSub + trw1 + 1024 * fo + 512);
+            wa[fo] = make_uint4(lo.x, lo.y, hi.x, hi.y);
+        }
+    }
+    int rbuf = 1;
+    for (int64_t kt = 0; kt < c.nk2; kt += 2) {
+        __syncthreads();
+        step(rbuf, xb, wb, xa, wa);
+        rbuf = (rbuf + 1 == PC::kNS1) ? 0 : rbuf + 1;
+        __syncthreads();
+        step(rbuf, xa, wa, xb, wb);
+        rbuf = (rbuf + 1 == PC::kNS1) ? 0 : rbuf + 1;
+    }
+    __syncthreads();   // every multiplier is done with the ring
+}
+
+// Epilogue of one pass: H = act(A + b1) (gated: silu(gate) * up) -> bf16 ->
+// LDS slabs from `hs` on, in the GEMM2 operand layout.  og0 is the global
+// hidden index of the pass's first column; columns at or past O become zero.
+// Gated form: fragment fo (< kFO/2) holds gate columns and fragment fo + kFO/2
+// the up columns of the same hidden indices (block fo of the W1 stage is
+// fragment fo of every wave).  Both forms round H to bf16 once.
+template <class PC, bool kGated>
+__device__ __forceinline__ void gemm1_epilogue(const floatx4_t (&acc)[PC::kFO][4], char* hs,
+                                               int64_t og0, int64_t O, const uint16_t* b1,
+                                               int act1, int w4, int lane) {
+    const int li = lane & 15, lg = lane >> 4;
+#pragma unroll
+    for (int fo = 0; fo < (kGated ? PC::kFO / 2 : PC::kFO); ++fo) {
+        const int ol = 16 * (w4 + kMulWaves * fo) + 4 * lg;  // first of 4 hidden cols
+        const int64_t og = og0 + ol;
+        float bias[4] = {0.f, 0.f, 0.f, 0.f};
+        const bool colok = og < O;  // O % 8 == 0, so the 4 columns are all in or all out
+        if (!kGated && colok && b1) {
+            uint2 bb = *reinterpret_cast<const uint2*>(b1 + og);
+            bias[0] = bf16_lo(bb.x);
+            bias[1] = bf16_hi(bb.x);
+            bias[2] = bf16_lo(bb.y);
+            bias[3] = bf16_hi(bb.y);
+        }
+        const int slab = ol / 32;
+        const int g = (ol % 32) / 8;
+        const int e = ol % 8;
+#pragma unroll
+        for (int fm = 0; fm < 4; ++fm) {
+            float h[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                if constexpr (kGated)
+                    h[r] = colok ? silu(acc[fo][fm][r]) * acc[fo + PC::kFO / 2][fm][r] : 0.f;
+                else
+                    h[r] = colok ? apply_act(act1, acc[fo][fm][r] + bias[r]) : 0.f;
+            }
+            uint2 pk = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+            *reinterpret_cast<uint2*>(hs + slab * kSub + frag_off(16 * fm + li, g) + 2 * e) = pk;
+        }
+    }
+}
+
+template <int CA, int CB, bool kGrouped, bool kGated>
 __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a) {
-    using Cfg = FusedCfg<C, kGated>;
+    using Cfg = FusedCfg<CA, CB, kGated>;
+    using PA = typename Cfg::PA;
+    using PB = typename Cfg::PB;
     static_assert(!(kGrouped && kGated), "the grouped form is not gated");
     extern __shared__ __attribute__((aligned(16))) char smem[];
 
@@ -154,29 +342,31 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     const int64_t o0 = (int64_t)s * Cfg::kHid;
     const int64_t oc = (O - o0) < Cfg::kHid ? (O - o0) : Cfg::kHid;  // valid hidden columns of this chunk
 
+    G1Ctx c;
+    c.smem = smem;
+    c.N = N;
+    c.O = O;
+    c.w4 = w4;
+    c.lane = lane;
     // ---- X slab loads: loader w fills fragment w (rows 16w..16w+15); lane l
     // brings row 16w + l/4, k-group xc into fragment slot l (see xfrag_slot).
     const int xr = 16 * w4 + (lane >> 2);
-    const int xc = (lane & 3) ^ ((lane >> 3) & 3);
-    int32x4_t rx;
-    uint32_t xrow_off = kOOB;
+    c.xc = (lane & 3) ^ ((lane >> 3) & 3);
+    c.xrow_off = kOOB;
     if constexpr (kGrouped) {
-        rx = make_srd(a.X, a.M * N * 2);
-        if (loader && xr < valid) xrow_off = (uint32_t)((a.g.sorted[row0 + xr] / a.g.k) * N * 2);
+        c.rx = make_srd(a.X, a.M * N * 2);
+        if (loader && xr < valid) c.xrow_off = (uint32_t)((a.g.sorted[row0 + xr] / a.g.k) * N * 2);
     } else {
-        rx = make_srd(a.X + row0 * N, (int64_t)valid * N * 2);
-        if (xr < valid) xrow_off = (uint32_t)(xr * N * 2);
+        c.rx = make_srd(a.X + row0 * N, (int64_t)valid * N * 2);
+        if (xr < valid) c.xrow_off = (uint32_t)(xr * N * 2);
     }
     // ---- weight loads: lane l brings slot l of a block (see wtile_dma_off).
-    // The W1 resource ends at the end of W1, so rows past N read zeros; columns
-    // past this chunk's valid width read finite neighbours whose H columns the
-    // epilogue forces to zero.
-    const int32x4_t rw1 = make_srd(W1 + o0, (N * O - o0) * 2);
-    const int32x4_t rw1u = kGated ? make_srd(a.W1u + o0, (N * O - o0) * 2) : rw1;
-    const uint32_t w1_lane = wtile_dma_off(lane, (uint32_t)(O * 2));
-
-    const int64_t nk = (N + kBK - 1) / kBK;
-    const int64_t nk2 = (nk + 1) & ~(int64_t)1;   // GEMM1 stages walked, padded to even
+    // Each W1 resource ends at the end of its matrix, so rows past N read
+    // zeros; columns past this chunk's valid width read finite neighbours (or
+    // zeros) whose H columns the epilogue forces to zero.
+    c.w1_lane = wtile_dma_off(lane, (uint32_t)(O * 2));
+    c.nk = (N + kBK - 1) / kBK;
+    c.nk2 = (c.nk + 1) & ~(int64_t)1;   // stages walked, padded to even
 
     // W2 stage: 32 hidden rows x 512 output columns.  The W2 resource covers
     // exactly this chunk's rows, so rows past the chunk read zeros; columns
@@ -193,148 +383,29 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     // in step keeps the L2 footprint to one sliding window per expert
     // (measured: 560 -> 530 us on the MoE workload).
     const int64_t jx = kGrouped ? 0 : (blockIdx.x >> 3);
-    const int64_t rot1 = jx % nk;
+    c.rot1 = jx % c.nk;
     const int64_t rotp = jx % np;
     const int rotk = (int)(jx % Cfg::kKS);
-    char* const hreg = smem;
+    char* const hreg = smem + Cfg::kHOff;
 
-    // The two roles run separate loops that execute the same number of
-    // barriers: nk for GEMM1, one between the products, nsteps for GEMM2.
     if (loader) {
-        // =================== loads of GEMM1 (X slab + W1 chunk) =============
-        // loads of the i-th stage in walking order (K stage (i + rot1) mod nk); the
-        // padding stage i == nk of an odd stage count reads zeros
-        auto issue1 = [&](int64_t i, int buf) {
-            const bool real = i < nk;
-            const int64_t kt = !real ? 0 : (i + rot1 < nk ? i + rot1 : i + rot1 - nk);
-            char* st = smem + buf * Cfg::kStage1;
-            const int64_t kx = kt * kBK + 8 * xc;
-            dma16(rx, real && kx < N ? xrow_off + (uint32_t)(kx * 2) : kOOB, st + w4 * kFrag);
-#pragma unroll
-            for (int b = 0; b < Cfg::kNB1; ++b) {
-                const int blk = w4 + kMulWaves * b;
-                const int r = blk / Cfg::kNB1, c = blk % Cfg::kNB1;
-                // gated form: blocks c < kNB1/2 hold gate columns, the rest the up
-                // columns of the same hidden indices
-                const bool up = kGated && c >= Cfg::kNB1 / 2;
-                const int cc = up ? c - Cfg::kNB1 / 2 : c;
-                const uint32_t base = (uint32_t)(((kt * kBK + 8 * r) * O + 64 * cc) * 2);
-                dma16(up ? rw1u : rw1, real ? base + w1_lane : kOOB, st + kSub + blk * kFrag);
-            }
-        };
-#pragma unroll
-        for (int i = 0; i < Cfg::kNS1 - 1; ++i)
-            if (i < nk2) issue1(i, i);
-        // barrier -1 publishes stage 0; barrier kt publishes stage kt + 1 (the
-        // multipliers read one stage ahead of the one they multiply)
-        if (Cfg::kNS1 - 2 < nk2) wait_vmcnt<Cfg::kD1 * (Cfg::kNS1 - 2)>();
-        else wait_vmcnt<0>();
-        __syncthreads();
-        int ibuf = Cfg::kNS1 - 1;
-        for (int64_t kt = 0; kt < nk2; ++kt) {
-            // stages kt+1 .. min(kt + NS1 - 2, nk2 - 1) may be in flight
-            if (kt + Cfg::kNS1 - 2 < nk2) wait_vmcnt<Cfg::kD1 * (Cfg::kNS1 - 3)>();
-            else wait_vmcnt<0>();
-            __syncthreads();
-            if (kt + Cfg::kNS1 - 1 < nk2) issue1(kt + Cfg::kNS1 - 1, ibuf);
-            ibuf = (ibuf + 1 == Cfg::kNS1) ? 0 : ibuf + 1;
+        gemm1_loads<PA, kGated>(c, make_srd(W1 + o0, (N * O - o0) * 2),
+                                kGated ? make_srd(a.W1u + o0, (N * O - o0) * 2) : c.rx);
+        if constexpr (Cfg::kTwoPass) {
+            const int64_t ob = o0 + Cfg::kHidA;
+            gemm1_loads<PB, kGated>(c, make_srd(W1 + ob, (N * O - ob) * 2),
+                                    make_srd(a.W1u + ob, (N * O - ob) * 2));
         }
-        __syncthreads();   // the multipliers are done with the GEMM1 ring
     } else {
-        // ======================= GEMM1: A^T = W1_chunk^T X^T ===================
-        floatx4_t acc[Cfg::kFO][4];
-#pragma unroll
-        for (int i = 0; i < Cfg::kFO; ++i)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
         {
-            const int xoff = 16 * xfrag_slot(li, lg);
-            // multiplier w owns hidden fragments w, w+4, w+8, ...: f % 4 == w
-            const uint32_t trw1 = wtile_tr_base(lane, Cfg::kNB1, w4);
-            // Software pipeline: after barrier kt (which publishes stage kt+1)
-            // the multiplier reads stage kt+1 while it multiplies stage kt from
-            // registers read one iteration earlier.  The reads are spread over
-            // the MFMAs (the X fragments first, then one W fragment ahead of
-            // each group of four MFMAs), so the LDS sees a steady stream and
-            // its latency hides behind the matrix work.  A read past the last
-            // stage fetches a stale buffer that is never multiplied.
-            auto step = [&](int buf, uint4 (&xn)[4], uint4 (&wn)[Cfg::kFO],
-                            const uint4 (&xc)[4], const uint4 (&wc)[Cfg::kFO]) {
-                const char* st = smem + buf * Cfg::kStage1;
-                const char* sw = st + kSub + trw1;
-#pragma unroll
-                for (int fm = 0; fm < 4; ++fm) xn[fm] = ld16(st + fm * kFrag + xoff);
-#pragma unroll
-                for (int fo = 0; fo < Cfg::kFO; ++fo) {
-                    const uint2 lo = lds_read_tr16(sw + 1024 * fo);
-                    const uint2 hi = lds_read_tr16(sw + 1024 * fo + 512);
-                    wn[fo] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-                    for (int fm = 0; fm < 4; ++fm)
-                        acc[fo][fm] = mfma16x16x32(wc[fo], xc[fm], acc[fo][fm]);
-                    __builtin_amdgcn_sched_barrier(0);
-                }
-            };
-            uint4 xa[4], wa[Cfg::kFO], xb[4], wb[Cfg::kFO];
-            __syncthreads();
-            {
-                const char* st = smem;
-#pragma unroll
-                for (int fm = 0; fm < 4; ++fm) xa[fm] = ld16(st + fm * kFrag + xoff);
-#pragma unroll
-                for (int fo = 0; fo < Cfg::kFO; ++fo) {
-                    const uint2 lo = lds_read_tr16(st + kSub + trw1 + 1024 * fo);
-                    const uint2 hi = lds_read_tr16(st + kSub + trw1 + 1024 * fo + 512);
-                    wa[fo] = make_uint4(lo.x, lo.y, hi.x, hi.y);
-                }
-            }
-            int rbuf = 1;
-            for (int64_t kt = 0; kt < nk2; kt += 2) {
-                __syncthreads();
-                step(rbuf, xb, wb, xa, wa);
-                rbuf = (rbuf + 1 == Cfg::kNS1) ? 0 : rbuf + 1;
-                __syncthreads();
-                step(rbuf, xa, wa, xb, wb);
-                rbuf = (rbuf + 1 == Cfg::kNS1) ? 0 : rbuf + 1;
-            }
+            floatx4_t acc[PA::kFO][4];
+            gemm1_mma<PA>(c, acc);
+            gemm1_epilogue<PA, kGated>(acc, hreg + Cfg::kSlabsB * kSub, o0, O, b1, a.act1, w4, lane);
         }
-        __syncthreads();   // every multiplier is done with the GEMM1 ring
-
-        // ---- epilogue 1: H = act(A + b1) -> bf16 -> LDS (GEMM2 operand layout).
-        // Gated form: fragment fo (< kFO/2) holds gate columns and fragment
-        // fo + kFO/2 the up columns of the same hidden indices (block fo of the
-        // W1 stage is fragment fo of every wave), so H = silu(gate) * up.
-        // Both forms round H to bf16 once.
-#pragma unroll
-        for (int fo = 0; fo < (kGated ? Cfg::kFO / 2 : Cfg::kFO); ++fo) {
-            const int ol = 16 * (w4 + kMulWaves * fo) + 4 * lg;  // first of 4 hidden cols
-            const int64_t og = o0 + ol;
-            float bias[4] = {0.f, 0.f, 0.f, 0.f};
-            const bool colok = og < O;  // O % 8 == 0, so the 4 columns are all in or all out
-            if (colok && b1) {
-                uint2 bb = *reinterpret_cast<const uint2*>(b1 + og);
-                bias[0] = bf16_lo(bb.x);
-                bias[1] = bf16_hi(bb.x);
-                bias[2] = bf16_lo(bb.y);
-                bias[3] = bf16_hi(bb.y);
-            }
-            const int slab = ol / 32;
-            const int g = (ol % 32) / 8;
-            const int e = ol % 8;
-#pragma unroll
-            for (int fm = 0; fm < 4; ++fm) {
-                float h[4];
-#pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if constexpr (kGated)
-                        h[r] = colok ? silu(acc[fo][fm][r]) * acc[fo + Cfg::kFO / 2][fm][r] : 0.f;
-                    else
-                        h[r] = colok ? apply_act(a.act1, acc[fo][fm][r] + bias[r]) : 0.f;
-                }
-                uint2 pk = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-                *reinterpret_cast<uint2*>(hreg + slab * kSub + frag_off(16 * fm + li, g) + 2 * e) = pk;
-            }
+        if constexpr (Cfg::kTwoPass) {
+            floatx4_t acc[PB::kFO][4];
+            gemm1_mma<PB>(c, acc);
+            gemm1_epilogue<PB, kGated>(acc, hreg, o0 + Cfg::kHidA, O, b1, a.act1, w4, lane);
         }
     }
     __syncthreads();   // H is complete
@@ -348,10 +419,15 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     // transposed in registers into four k-contiguous operands; operand j,
     // index i stands for column 4i + j.  H is the first MFMA operand, so lane
     // (i, g) ends up with rows 16 fm + 4g + r of the four consecutive columns
-    // 4i..4i+3 and stores them as one 16-byte write.
+    // 4i..4i+3 and stores them as one 16-byte write.  H slab ks holds hidden
+    // rows hrow(ks) .. +31 of the chunk (pass B's slabs first).
     const int wc = wave;
     const __amdgpu_buffer_rsrc_t rw2 = make_rsrc(W2 + o0 * P, oc * P * 2);
     const uint32_t w2_lane = (uint32_t)(8 * lg) * (uint32_t)(P * 2) + (uint32_t)(64 * wc + 4 * li) * 2u;
+    auto hrow = [](int ks) {
+        if constexpr (Cfg::kSlabsB == 0) return kBK * ks;
+        else return ks < Cfg::kSlabsB ? Cfg::kHidA + kBK * ks : kBK * (ks - Cfg::kSlabsB);
+    };
     // loads of stage `step` into R; a step past the end reads zeros (out of
     // range), so that every stage refills its registers unconditionally
     auto load2 = [&](int64_t step, uint2 (&R)[8]) {
@@ -360,7 +436,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
         const int64_t pt = pr + rotp < np ? pr + rotp : pr + rotp - np;
         const int ks = kr + rotk < Cfg::kKS ? kr + rotk : kr + rotk - Cfg::kKS;
         const uint32_t base = step < nsteps
-            ? (uint32_t)(((int64_t)ks * kBK * P + pt * kBN2) * 2) + w2_lane : kOOB;
+            ? (uint32_t)(((int64_t)hrow(ks) * P + pt * kBN2) * 2) + w2_lane : kOOB;
 #pragma unroll
         for (int e = 0; e < 8; ++e) R[e] = bload8(rw2, base + (uint32_t)(e * P * 2));
     };
@@ -472,10 +548,10 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
     }
 }
 
-template <int C, bool G, bool kGated = false>
+template <int CA, int CB, bool G, bool kGated>
 hipError_t launch_fused_impl(const FusedArgs& a, int64_t units, hipStream_t stream) {
-    using Cfg = FusedCfg<C, kGated>;
-    auto kern = fused_ffn_bf16_kernel<C, G, kGated>;
+    using Cfg = FusedCfg<CA, CB, kGated>;
+    auto kern = fused_ffn_bf16_kernel<CA, CB, G, kGated>;
     static bool attr_set = false;
     if (!attr_set) {
         hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
@@ -524,14 +600,27 @@ hipError_t launch_fused_bf16(const uint16_t* X, const uint16_t* W1, const uint16
     const int64_t units = row_blocks * a.splits;
     if (units <= 0) return hipSuccess;
     if (chunk == 448)
-        return grouped ? launch_fused_impl<448, true>(a, units, stream)
-                       : launch_fused_impl<448, false>(a, units, stream);
-    return grouped ? launch_fused_impl<512, true>(a, units, stream)
-                   : launch_fused_impl<512, false>(a, units, stream);
+        return grouped ? launch_fused_impl<448, 0, true, false>(a, units, stream)
+                       : launch_fused_impl<448, 0, false, false>(a, units, stream);
+    return grouped ? launch_fused_impl<512, 0, true, false>(a, units, stream)
+                   : launch_fused_impl<512, 0, false, false>(a, units, stream);
+}
+
+// Hidden columns per workgroup of the gated kernel: 448 (two passes, 256 +
+// 192) or 256 (one pass).  As for the dense chunk: prefer an exact width
+// whose split count divides 8, then any exact width, fewest splits first.
+int fused_swiglu_hid(int64_t O) {
+    constexpr int h2 = FusedCfg<512, 384, true>::kHid, h1 = FusedCfg<512, 0, true>::kHid;
+    for (int h : {h2, h1})
+        if (O % h == 0 && 8 % (O / h) == 0) return h;
+    if (O % h2 == 0) return h2;
+    if (O % h1 == 0) return h1;
+    return O > h1 ? h2 : h1;
 }
 
 int fused_swiglu_splits(int64_t O) {
-    return (int)((O + FusedCfg<kSwigluChunk, true>::kHid - 1) / FusedCfg<kSwigluChunk, true>::kHid);
+    const int h = fused_swiglu_hid(O);
+    return (int)((O + h - 1) / h);
 }
 
 hipError_t launch_fused_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
@@ -554,7 +643,9 @@ hipError_t launch_fused_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, const
     a.act1 = 0;
     const int64_t units = a.row_blocks * a.splits;
     if (units <= 0) return hipSuccess;
-    return launch_fused_impl<kSwigluChunk, false, true>(a, units, stream);
+    if (fused_swiglu_hid(O) == FusedCfg<512, 384, true>::kHid)
+        return launch_fused_impl<512, 384, false, true>(a, units, stream);
+    return launch_fused_impl<512, 0, false, true>(a, units, stream);
 }
 
 hipError_t launch_reduce_splits(const float* part, int splits, const void* b2, int b2_f32,

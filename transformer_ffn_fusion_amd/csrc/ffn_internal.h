@@ -32,10 +32,10 @@ hipError_t launch_fused_bf16(const uint16_t* X, const uint16_t* W1, const uint16
                              int64_t O, int64_t P, int act1, int chunk, int64_t row_blocks,
                              int64_t rows_out, const GroupedRows* grouped, hipStream_t stream);
 
-// SwiGLU form: part[s][row][p] for the hidden chunk s of kSwigluChunk/2
+// SwiGLU form: part[s][row][p] for the hidden chunk s of fused_swiglu_hid(O)
 // columns: H = silu(X Wg) * (X Wu) rounded to bf16, times the rows of Wd.
-constexpr int kSwigluChunk = 512;                // first-product width (gate + up)
-int fused_swiglu_splits(int64_t O);              // ceil(O / (kSwigluChunk / 2))
+int fused_swiglu_hid(int64_t O);                 // 448 or 256
+int fused_swiglu_splits(int64_t O);              // ceil(O / fused_swiglu_hid(O))
 hipError_t launch_fused_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
                                     const uint16_t* Wd, float* part, int64_t M, int64_t N,
                                     int64_t O, int64_t P, hipStream_t stream);
