@@ -70,6 +70,8 @@ def _bind(lib):
     lib.oracle_swiglu.restype = ctypes.c_int
     lib.oracle_silu.argtypes = [ctypes.c_double]
     lib.oracle_silu.restype = ctypes.c_double
+    lib.oracle_router_logits.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i64, dp]
+    lib.oracle_router_logits.restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_act.argtypes = [i32, ctypes.c_double]
@@ -160,6 +162,32 @@ def swiglu(X, Wg, Wu, Wd, rows=None, lib=None):
     if rc != 0:
         raise ValueError("oracle_swiglu rejected its arguments")
     return Y
+
+
+def router_logits(X, Wr, br=None, rows=None, lib=None):
+    """fp64 router logits ``X Wr + br`` (the gate network as one linear layer).
+
+    ``X`` (M x N) and ``Wr`` (N x E): float32 arrays or uint16 bf16 bit patterns;
+    ``br``: E float32 values or None."""
+    lib = lib or load()
+    dt = _dtype_of(X)
+    M, N = X.shape
+    E = Wr.shape[1]
+    assert Wr.shape == (N, E)
+    kx, kw = _as_input(X, dt), _as_input(Wr, dt)
+    b = None if br is None else np.ascontiguousarray(br, dtype=np.float32)
+    assert b is None or b.shape == (E,)
+    if rows is None:
+        rws, rp, nr = None, None, M
+    else:
+        rws = np.ascontiguousarray(np.asarray(rows, dtype=np.int64))
+        rp, nr = rws.ctypes.data, rws.size
+    out = np.empty((nr, E), dtype=np.float64)
+    rc = lib.oracle_router_logits(dt, kx[1], kw[1], None if b is None else b.ctypes.data, rp, nr,
+                                  M, N, E, out.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_router_logits rejected its arguments")
+    return out
 
 
 def moe_route(logits, k=2, lib=None):

@@ -25,6 +25,10 @@
  *    (zhongzhuzhou.org), section 2.1 (Mixture-of-Experts, briefly) and 2.2
  *    (five steps): the router picks the top-k experts per token and the
  *    output is the gate-weighted sum of those experts' FFN outputs.
+ *    Step 1 runs "the gate" (a small router network) on the tokens;
+ *    oracle_router_logits() reads it as one linear layer, the plainest form
+ *    (as in Switch Transformer and GShard, which the section names):
+ *    logits = X Wr + br.
  *
  * Readings where the pages are silent (each also listed in the design doc):
  *  - act1 is ReLU or the tanh form of GELU; GELU-tanh is
@@ -200,6 +204,35 @@ int oracle_swiglu(int dtype, const void* X, const void* Wg, const void* Wu, cons
         free(g);
         free(u);
         free(acc);
+    }
+    return bad ? -1 : 0;
+}
+
+/* Router logits (the gate network read as one linear layer):
+ * logits[t][e] = sum_n X[t][n] Wr[n][e] (ascending n) + br[e].
+ * X: M x N and Wr: N x E in `dtype`; br: E floats or NULL.  rows == NULL: all
+ * M tokens, else the nrows listed tokens; out is nrows x E doubles. */
+int oracle_router_logits(int dtype, const void* X, const void* Wr, const float* br,
+                         const int64_t* rows, int64_t nrows, int64_t M, int64_t N, int64_t E,
+                         double* out) {
+    if (!X || !Wr || !out || M < 0 || N < 1 || E < 1) return -1;
+    if (dtype != OR_F32 && dtype != OR_BF16) return -1;
+    if (!rows) nrows = M;
+    int bad = 0;
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t t = rows ? rows[r] : r;
+        if (t < 0 || t >= M) {
+#pragma omp atomic write
+            bad = 1;
+            continue;
+        }
+        for (int64_t e = 0; e < E; ++e) {
+            double acc = 0.0;
+            for (int64_t n = 0; n < N; ++n)
+                acc += load(dtype, X, t * N + n) * load(dtype, Wr, n * E + e);
+            out[r * E + e] = acc + (br ? (double)br[e] : 0.0);
+        }
     }
     return bad ? -1 : 0;
 }

@@ -425,6 +425,45 @@ def test_swiglu_rows_bit_exact():
 
 
 # ----------------------------------------------------------------------------
+# 7c. router logits (the gate network as one linear layer)
+# ----------------------------------------------------------------------------
+
+def _frac_router(X, Wr, br):
+    M, N = X.shape
+    E = Wr.shape[1]
+    F = lambda v: Fraction(float(v))  # noqa: E731
+    return [[sum(F(X[t, n]) * F(Wr[n, e]) for n in range(N)) + (F(br[e]) if br is not None else 0)
+             for e in range(E)] for t in range(M)]
+
+
+@pytest.mark.parametrize("shape", [(3, 5, 4), (1, 1, 1), (6, 16, 8), (2, 7, 3)])
+@pytest.mark.parametrize("bias", [True, False])
+@pytest.mark.parametrize("as_bf16", [False, True])
+def test_router_logits_exact(shape, bias, as_bf16):
+    M, N, E = shape
+    rng = np.random.default_rng(sum(shape) + 7 * bias + as_bf16)
+    X, Wr = _dyadic(rng, (M, N)), _dyadic(rng, (N, E))
+    br = _dyadic(rng, (E,)) if bias else None
+    exact = _frac_router(X, Wr, br)
+    conv = _to_bf16 if as_bf16 else (lambda a: a)
+    got = oracle.router_logits(conv(X), conv(Wr), br)
+    for t in range(M):
+        for e in range(E):
+            assert got[t, e] == float(exact[t][e]), (t, e)
+
+
+def test_router_identity_and_rows():
+    """N = E, Wr = I: logits = X + br exactly; a row subset is bit-exact."""
+    rng = np.random.default_rng(12)
+    X = rng.standard_normal((9, 8)).astype(np.float32)
+    br = rng.standard_normal(8).astype(np.float32)
+    L = oracle.router_logits(X, np.eye(8, dtype=np.float32), br)
+    assert np.array_equal(L, X.astype(np.float64) + br.astype(np.float64))
+    assert np.array_equal(oracle.router_logits(X, np.eye(8, dtype=np.float32), br, rows=[8, 2]),
+                          L[[8, 2]])
+
+
+# ----------------------------------------------------------------------------
 # 8. planted mistakes in the oracle must be caught (CPU only)
 # ----------------------------------------------------------------------------
 
@@ -449,6 +488,10 @@ MUTANTS = {
     "swiglu_wg_cols_reversed": ("load(dtype, Wg, n * O + o)", "load(dtype, Wg, n * O + (O - 1 - o))"),
     "swiglu_wu_cols_reversed": ("load(dtype, Wu, n * O + o)", "load(dtype, Wu, n * O + (O - 1 - o))"),
     "swiglu_wd_cols_reversed": ("load(dtype, Wd, o * P + p)", "load(dtype, Wd, o * P + (P - 1 - p))"),
+    "router_wr_cols_reversed": ("load(dtype, Wr, n * E + e)", "load(dtype, Wr, n * E + (E - 1 - e))"),
+    "router_bias_dropped": ("acc + (br ? (double)br[e] : 0.0)", "acc"),
+    "router_skip_first_n": ("for (int64_t n = 0; n < N; ++n)\n                acc +=",
+                            "for (int64_t n = 1; n < N; ++n)\n                acc +="),
     "swiglu_skip_first_n": ("x = load(dtype, X, m * N + n);\n        for (int64_t o = 0; o < O; ++o) {\n            g[o]",
                             "x = n ? load(dtype, X, m * N + n) : 0.0;\n        for (int64_t o = 0; o < O; ++o) {\n            g[o]"),
 }
@@ -516,8 +559,15 @@ def _pin_suite(lib):
         xd = x.astype(np.float64)
         assert np.allclose(Y, 2 * xd * xd * _sigmoid_tanh_form(2 * xd), rtol=1e-13, atol=0)
 
+    def router():
+        rng = np.random.default_rng(13)
+        X, Wr, br = _dyadic(rng, (3, 6)), _dyadic(rng, (6, 4)), _dyadic(rng, (4,))
+        exact = _frac_router(X, Wr, br)
+        got = oracle.router_logits(X, Wr, br, lib=lib)
+        assert all(got[t, e] == float(exact[t][e]) for t in range(3) for e in range(4))
+
     for name, fn in [("brute", brute), ("act2", act2), ("gelu", gelu), ("routing", routing),
-                     ("moe_combine", moe_combine), ("swiglu", swiglu)]:
+                     ("moe_combine", moe_combine), ("swiglu", swiglu), ("router", router)]:
         check(name, fn)
     return failures
 

@@ -1,19 +1,24 @@
 """Seeded synthetic inputs shared by the tests, the bench and the smoke check.
 
 This module generates inputs only.  It holds none of the feed-forward
-arithmetic: no activation, no bias addition, no FFN product and no routing.
+arithmetic: no activation, no bias addition, no FFN or router product and no
+routing.
 Both sides of every parity check (the HIP library and the fp64 oracle) receive
 the arrays produced here, bit for bit.
 
 Recipe (the reading is recorded in the design doc):
 * ``numpy.random.default_rng(seed)`` (PCG64), ``standard_normal(dtype=float32)``
   scaled by the standard deviation, in the order X, W1, b1, W2, b2
-  (MoE: X, Wr, then per expert W1_e, b1_e, W2_e, b2_e);
+  (MoE with logits as input: X, the logit draws, then per expert W1_e, b1_e,
+  W2_e, b2_e; MoE with the router: X, Wr, then the experts);
 * standard deviations: X 1, W1 1/sqrt(N), W2 1/sqrt(O), Wr 1/sqrt(N), biases
   sqrt(v) with v read as a variance (0.1 for the tiny fp32 case, 0.02 else);
 * bf16 tensors are the fp32 draws rounded once to nearest, ties to even;
-* MoE gate logits are an input of the layer: ``fp32(sum_n X[t,n] Wr[n,e] + off[e])``
-  accumulated in float64 from the bf16 values of X and the fp32 Wr.
+* MoE gate logits, where they are an input of the layer, are drawn directly:
+  a standard normal draw (the spread of a unit-variance token through a
+  1/sqrt(N)-scaled router) plus the per-expert offset, rounded once to fp32;
+  where the router runs on the GPU its weights Wr (bf16) and the offsets as
+  its bias br (fp32) are the inputs instead.
 """
 from __future__ import annotations
 
@@ -80,11 +85,12 @@ def swiglu_inputs(M, N, O, P, *, dtype="bf16", seed=0):
     return out
 
 
-def moe_inputs(M, E, N, O, P, *, offsets=MOE_SKEW_OFFSETS, bias_var=0.02, seed=0):
-    """bf16 MoE inputs: X (MxN), logits (MxE, fp32), W1 (ExNxO), b1 (ExO), W2 (ExOxP), b2 (ExP)."""
-    rng = np.random.default_rng(seed)
-    X = f32_to_bf16_bits(_draw(rng, (M, N), 1.0))
-    Wr = _draw(rng, (N, E), 1.0 / np.sqrt(N))
+def _offsets(offsets, E):
+    return np.asarray(offsets[:E] if len(offsets) >= E else list(offsets) + [0.0] * (E - len(offsets)),
+                      dtype=np.float64)
+
+
+def _experts(rng, E, N, O, P, bias_var):
     W1 = np.empty((E, N, O), np.uint16)
     b1 = np.empty((E, O), np.uint16)
     W2 = np.empty((E, O, P), np.uint16)
@@ -94,10 +100,29 @@ def moe_inputs(M, E, N, O, P, *, offsets=MOE_SKEW_OFFSETS, bias_var=0.02, seed=0
         b1[e] = f32_to_bf16_bits(_draw(rng, (O,), np.sqrt(bias_var)))
         W2[e] = f32_to_bf16_bits(_draw(rng, (O, P), 1.0 / np.sqrt(O)))
         b2[e] = f32_to_bf16_bits(_draw(rng, (P,), np.sqrt(bias_var)))
-    off = np.asarray(offsets[:E] if len(offsets) >= E else list(offsets) + [0.0] * (E - len(offsets)),
-                     dtype=np.float64)
-    logits = (bf16_bits_to_f32(X).astype(np.float64) @ Wr.astype(np.float64) + off).astype(np.float32)
+    return W1, b1, W2, b2
+
+
+def moe_inputs(M, E, N, O, P, *, offsets=MOE_SKEW_OFFSETS, bias_var=0.02, seed=0):
+    """bf16 MoE inputs with the gate logits given: X (MxN), logits (MxE, fp32), W1 (ExNxO),
+    b1 (ExO), W2 (ExOxP), b2 (ExP)."""
+    rng = np.random.default_rng(seed)
+    X = f32_to_bf16_bits(_draw(rng, (M, N), 1.0))
+    noise = _draw(rng, (M, E), 1.0)
+    W1, b1, W2, b2 = _experts(rng, E, N, O, P, bias_var)
+    logits = (noise.astype(np.float64) + _offsets(offsets, E)).astype(np.float32)
     return X, logits, W1, b1, W2, b2
+
+
+def moe_router_inputs(M, E, N, O, P, *, offsets=MOE_SKEW_OFFSETS, bias_var=0.02, seed=0):
+    """bf16 MoE inputs with the router on the GPU: X (MxN), Wr (NxE bf16, std 1/sqrt(N)),
+    br (E fp32: the per-expert offsets), W1, b1, W2, b2 as in moe_inputs."""
+    rng = np.random.default_rng(seed)
+    X = f32_to_bf16_bits(_draw(rng, (M, N), 1.0))
+    Wr = f32_to_bf16_bits(_draw(rng, (N, E), 1.0 / np.sqrt(N)))
+    W1, b1, W2, b2 = _experts(rng, E, N, O, P, bias_var)
+    br = _offsets(offsets, E).astype(np.float32)
+    return X, Wr, br, W1, b1, W2, b2
 
 
 def check_rows(M, block=64, n_random=249, seed=1):
