@@ -229,6 +229,57 @@ def run_dense(cfg, steps, warmup, hip, torch, ffn, synth, workload):
                 rotate=R, inputs=(X, W1, b1, W2, b2))
 
 
+def run_moe_router(cfg, steps, warmup, hip, torch, ffn, synth, workload):
+    """The MoE layer with the router on the GPU (logits = X Wr + br): region 1 times
+    the whole layer, region 2 the router + routing alone."""
+    X, Wr, br, W1, b1, W2, b2 = synth.moe_router_inputs(cfg.M, cfg.E, cfg.N, cfg.O, cfg.P, seed=0)
+    set_bytes = workload.moe_bytes(cfg.M, cfg.E, cfg.N, cfg.O, cfg.P) + 2 * cfg.N * cfg.E
+    R = max(1, min(8, math.ceil(MALL_DEFEAT_BYTES / set_bytes)))
+    base = [to_dev(a, torch) for a in (X, Wr, br, W1, b1, W2, b2)]
+    sets = [[t.clone() for t in base] +
+            [torch.empty((cfg.M, cfg.P), dtype=torch.bfloat16, device="cuda")] for _ in range(R)]
+    del base
+    ws = ffn.workspace(ffn.moe_workspace_size(cfg.M, cfg.E, cfg.k, cfg.N, cfg.O, cfg.P))
+    L = ffn.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    p = lambda t: t.data_ptr()  # noqa: E731
+
+    def layer(i):
+        x, wr, c, w1, c1, w2, c2, y = sets[i % R]
+        rc = L.moe_ffn_forward_router(p(x), p(wr), p(c), cfg.M, cfg.E, cfg.k, p(w1), p(c1), p(w2),
+                                      p(c2), p(y), cfg.N, cfg.O, cfg.P, ffn.BF16, 2, 0, None, None,
+                                      None, None, None, p(ws), ws.numel(), stream)
+        if rc != 0:
+            raise RuntimeError(ffn.ffn_last_error())
+
+    def route(i):
+        x, wr, c = sets[i % R][:3]
+        rc = L.moe_router(p(x), p(wr), p(c), cfg.M, cfg.N, cfg.E, cfg.k, None, None, None, None,
+                          None, p(ws), ws.numel(), stream)
+        if rc != 0:
+            raise RuntimeError(ffn.ffn_last_error())
+
+    for i in range(warmup):
+        layer(i)
+    torch.cuda.synchronize()
+    t0, t1, t2, t3 = hip.event(), hip.event(), hip.event(), hip.event()
+    hip.record(t0, stream)
+    for s_ in range(steps):
+        layer(s_)
+    hip.record(t1, stream)
+    torch.cuda.synchronize()
+    hip.record(t2, stream)
+    for s_ in range(steps):
+        route(steps + s_)
+    hip.record(t3, stream)
+    torch.cuda.synchronize()
+    total_ms, route_ms = hip.ms(t0, t1), hip.ms(t2, t3)
+    hip.destroy([t0, t1, t2, t3])
+    flops = workload.moe_flops(cfg.M * cfg.k, cfg.N, cfg.O, cfg.P) + 2 * cfg.M * cfg.N * cfg.E
+    return dict(ms_per_step=total_ms / steps, router_ms=route_ms / steps, flops=flops,
+                bytes=set_bytes, rotate=R)
+
+
 def run_moe(cfg, steps, warmup, hip, torch, ffn, synth, workload):
     X, logits, W1, b1, W2, b2 = synth.moe_inputs(cfg.M, cfg.E, cfg.N, cfg.O, cfg.P, seed=0)
     set_bytes = workload.moe_bytes(cfg.M, cfg.E, cfg.N, cfg.O, cfg.P)
@@ -346,7 +397,8 @@ def main():
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill",
-                    choices=["prefill", "decode", "large", "moe", "tiny", "swiglu", "swiglu_decode"])
+                    choices=["prefill", "decode", "large", "moe", "tiny", "swiglu", "swiglu_decode",
+                             "moe_shard"])
     ap.add_argument("--all", action="store_true", help="also time the large and MoE workloads")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle sample rows (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -371,18 +423,19 @@ def main():
     hip = Hip()
     cfgs = {"prefill": workload.PREFILL, "decode": workload.DECODE, "large": workload.LARGE,
             "tiny": workload.TINY_F32, "moe": workload.MOE, "swiglu": workload.SWIGLU_PREFILL,
-            "swiglu_decode": workload.SWIGLU_DECODE}
+            "swiglu_decode": workload.SWIGLU_DECODE, "moe_shard": workload.MOE_SHARD}
     head = cfgs[args.workload]
     log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {head.name}")
 
     secondary = {}
-    if args.workload == "moe":
+    if args.workload in ("moe", "moe_shard"):
         r = run_moe(head, args.steps, args.warmup, hip, torch, ffn, synth, workload)
         value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
         kern_tflops = r["flops"] / (r["k1_ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": "grouped fused FFN", "achieved": kern_tflops,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": kern_tflops / PEAK_BF16_TFLOPS,
-                "traffic": recorded_traffic(head.name), "kernel_us": 1e3 * r["k1_ms"]}
+                "traffic": recorded_traffic(head.name), "kernel_us": 1e3 * r["k1_ms"],
+                "route_us": 1e3 * r["route_ms"], "combine_us": 1e3 * r["combine_ms"]}
         unit = "TFLOP/s"
         dense = None
     else:
@@ -422,11 +475,11 @@ def main():
             "kernels_GB_per_s": d["bytes"] / ((d["k1_ms"] + d["k2_ms"]) * 1e-3) / 1e9,
             "rotate": d["rotate"]}
     if args.all:
-        for name in ("large", "moe", "tiny", "swiglu", "swiglu_decode"):
+        for name in ("large", "moe", "moe_shard", "tiny", "swiglu", "swiglu_decode"):
             c = cfgs[name]
             if c is head:
                 continue
-            if name == "moe":
+            if name in ("moe", "moe_shard"):
                 m = run_moe(c, args.steps, args.warmup, hip, torch, ffn, synth, workload)
                 secondary[c.name] = {"TFLOP_per_s": m["flops"] / (m["ms_per_step"] * 1e-3) / 1e12,
                                      "us_per_call": 1e3 * m["ms_per_step"],
@@ -439,6 +492,12 @@ def main():
                                      "GB_per_s": m["bytes"] / (m["ms_per_step"] * 1e-3) / 1e9,
                                      "us_per_call": 1e3 * m["ms_per_step"],
                                      "kernel1_us": 1e3 * m["k1_ms"], "kernel2_us": 1e3 * m["k2_ms"]}
+
+    if args.all:
+        m = run_moe_router(workload.MOE, args.steps, args.warmup, hip, torch, ffn, synth, workload)
+        secondary["moe_router_" + workload.MOE.name] = {
+            "TFLOP_per_s": m["flops"] / (m["ms_per_step"] * 1e-3) / 1e12,
+            "us_per_call": 1e3 * m["ms_per_step"], "router_and_routing_us": 1e3 * m["router_ms"]}
 
     ceil = box_ceilings(hip, torch, ffn)
     if roof["unit"] == "TFLOP/s" and head.dtype == "bf16":

@@ -175,6 +175,32 @@ int moe_ffn_forward_traced(const void* X, const float* logits, int64_t M, int64_
                            int act2, void* workspace, size_t workspace_bytes, void* stream,
                            void** events, int n_events);
 
+/* ---------------------------------------------------------------- MoE with the router
+ * The same layer with the gate network on the GPU (the review, section 2.2,
+ * step 1: the gate runs on the tokens and yields the assignments and gate
+ * weights), read as one linear layer:
+ *
+ *     logits = X Wr + br           Wr: N x E bf16, br: E fp32 or NULL
+ *
+ * accumulated in fp32 (bf16 products, one fixed summation order), then routed
+ * exactly as moe_route does.  The router form needs E % 8 == 0; Wr must be
+ * 16-byte aligned.  logits_out (M x E fp32, may be NULL) receives the logits
+ * the routing used.  Workspace: as for moe_workspace_size. */
+
+/* Router + routing alone (the outputs as in moe_route, plus logits_out). */
+int moe_router(const void* X, const void* Wr, const float* br, int64_t M, int64_t N, int64_t E,
+               int k, float* logits_out, int32_t* topk_ids, float* topk_w,
+               int32_t* expert_offsets, int32_t* sorted_entries, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/* As moe_ffn_forward with the logits computed from X, Wr and br. */
+int moe_ffn_forward_router(const void* X, const void* Wr, const float* br, int64_t M, int64_t E,
+                           int k, const void* W1, const void* b1, const void* W2, const void* b2,
+                           void* Y, int64_t N, int64_t O, int64_t P, int dtype, int act1,
+                           int act2, float* logits_out, int32_t* topk_ids, float* topk_w,
+                           int32_t* expert_offsets, int32_t* sorted_entries, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
 /* Text describing the last non-zero return on this host thread ("" if none). */
 const char* ffn_last_error(void);
 

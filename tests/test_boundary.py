@@ -164,6 +164,26 @@ def test_moe_rejects(kw, code):
     assert rc == code, (rc, ffn.ffn_last_error())
 
 
+def test_router_rejects():
+    L = ffn.lib()
+    ws = 1 << 24
+    # X, Wr, br, M, N, E, k, logits_out, ids, w, offsets, sorted, ws, bytes, stream
+    assert L.moe_router(FAKE, None, None, 64, 64, 8, 2, None, None, None, None, None, FAKE, ws, None) == E_INVAL
+    assert L.moe_router(FAKE, FAKE, None, 64, 64, 12, 2, None, None, None, None, None, FAKE, ws, None) == E_UNSUP
+    assert L.moe_router(FAKE, FAKE + 8, None, 64, 64, 8, 2, None, None, None, None, None, FAKE, ws, None) == E_ALIGN
+    assert L.moe_router(FAKE, FAKE, FAKE + 2, 64, 64, 8, 2, None, None, None, None, None, FAKE, ws, None) == E_ALIGN
+    assert L.moe_router(FAKE, FAKE, None, 64, 60, 8, 2, None, None, None, None, None, FAKE, ws, None) == E_UNSUP
+    assert L.moe_router(FAKE, FAKE, None, 64, 64, 8, 9, None, None, None, None, None, FAKE, ws, None) == E_UNSUP
+    assert L.moe_router(FAKE, FAKE, None, 64, 64, 8, 2, None, None, None, None, None, FAKE, 16, None) == E_WS
+    # the full layer: logits come from the router; no Wr is an error
+    rc = L.moe_ffn_forward_router(FAKE, None, None, 64, 8, 2, FAKE, None, FAKE, None, FAKE2, 64, 448,
+                                  64, ffn.BF16, 2, 0, None, None, None, None, None, FAKE, ws, None)
+    assert rc == E_INVAL
+    rc = L.moe_ffn_forward_router(FAKE, FAKE, None, 64, 8, 2, FAKE, None, FAKE, None, FAKE2, 64, 448,
+                                  64, ffn.BF16, 2, 0, None, None, None, None, None, FAKE, 16, None)
+    assert rc == E_WS
+
+
 def test_route_rejects():
     L = ffn.lib()
     assert L.moe_route(None, 8, 8, 2, None, None, None, None, FAKE, 1 << 20, None) == E_INVAL

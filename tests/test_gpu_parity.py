@@ -209,6 +209,24 @@ def test_moe_shapes(M, E, k, N, O, P):
     compare(got, ref, BF16_TOL, "moe")
 
 
+def test_moe_expert_shard_workload():
+    """One GPU's share of an 8-way expert-sharded layer: every expert at O = 256."""
+    c = workload.MOE_SHARD
+    log(f"case {c.name}")
+    got, ref, counts = _run_moe(c.M, c.E, c.k, c.N, c.O, c.P)
+    log(f"  expert loads {counts.tolist()}")
+    compare(got, ref, BF16_TOL, c.name)
+
+
+@pytest.mark.parametrize("shape", [(100, 256, 256, 520), (70, 64, 136, 64)])
+def test_fused_narrow_hidden(shape):
+    """Hidden widths of at most 256 run the 256-wide chunk."""
+    M, N, O, P = shape
+    log(f"case fused narrow {shape}")
+    got, ref, _ = _run_dense(M, N, O, P, variant=ffn.VARIANT_FUSED, seed=O)
+    compare(got, ref, BF16_TOL, f"fused {shape}")
+
+
 @pytest.mark.parametrize("M,E,k", [
     (1000, 8, 2),
     (3000, 64, 8),    # several staged logit blocks (128 tokens each), k at its maximum

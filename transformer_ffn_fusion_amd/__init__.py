@@ -76,6 +76,11 @@ def lib():
         L.ffn_swiglu_forward_traced.argtypes = [vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, vp,
                                                 sz, vp, ctypes.POINTER(vp), i32]
         L.ffn_swiglu_forward_traced.restype = i32
+        L.moe_router.argtypes = [vp, vp, vp, i64, i64, i64, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_router.restype = i32
+        L.moe_ffn_forward_router.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, i64, i64,
+                                             i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_ffn_forward_router.restype = i32
         L.ffn_last_error.argtypes = []
         L.ffn_last_error.restype = ctypes.c_char_p
         L.ffn_version.restype = i32
@@ -201,6 +206,36 @@ def moe_ffn_forward(X, logits, k, W1, b1, W2, b2, Y, act1="gelu_tanh", act2="non
                                  _ptr(b2), _ptr(Y), N, O, P, dt, _act(act1), _act(act2),
                                  _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets),
                                  _ptr(sorted_entries), _ptr(ws), ws.numel(), _stream(stream)))
+    return Y
+
+
+def moe_router(X, Wr, br, k, logits_out=None, topk_ids=None, topk_w=None, expert_offsets=None,
+               sorted_entries=None, ws=None, stream=None):
+    """Router logits X Wr + br and top-k routing on the GPU; fills the given outputs."""
+    M, N = X.shape
+    E = Wr.shape[1]
+    if ws is None:
+        ws = workspace(moe_workspace_size(M, E, k, N, 8, 8), X.device)
+    _check(lib().moe_router(_ptr(X), _ptr(Wr), _ptr(br), M, N, E, k, _ptr(logits_out),
+                            _ptr(topk_ids), _ptr(topk_w), _ptr(expert_offsets),
+                            _ptr(sorted_entries), _ptr(ws), ws.numel(), _stream(stream)))
+
+
+def moe_ffn_forward_router(X, Wr, br, k, W1, b1, W2, b2, Y, act1="gelu_tanh", act2="none",
+                           logits_out=None, topk_ids=None, topk_w=None, expert_offsets=None,
+                           sorted_entries=None, ws=None, stream=None):
+    """The MoE layer with the router on the GPU; ``Y`` written in place."""
+    M, N = X.shape
+    E, _, O = W1.shape
+    P = W2.shape[2]
+    dt = _dtype_code(X)
+    if ws is None:
+        ws = workspace(moe_workspace_size(M, E, k, N, O, P, dt), X.device)
+    _check(lib().moe_ffn_forward_router(_ptr(X), _ptr(Wr), _ptr(br), M, E, k, _ptr(W1), _ptr(b1),
+                                        _ptr(W2), _ptr(b2), _ptr(Y), N, O, P, dt, _act(act1),
+                                        _act(act2), _ptr(logits_out), _ptr(topk_ids), _ptr(topk_w),
+                                        _ptr(expert_offsets), _ptr(sorted_entries), _ptr(ws),
+                                        ws.numel(), _stream(stream)))
     return Y
 
 

@@ -127,7 +127,8 @@ SwigluLayout swiglu_layout(int64_t M, int64_t N, int64_t O, int64_t P, int varia
 
 // ---- MoE workspace layout
 struct MoeLayout {
-    size_t ids, w, counts, offsets, sorted, pos, tiles, tile_count, part, total;
+    size_t ids, w, counts, offsets, sorted, pos, tiles, tile_count, blk_counts, blk_base, part,
+        total;
     int splits, chunk;
     int64_t max_tiles;
 };
@@ -147,6 +148,9 @@ MoeLayout moe_layout(int64_t M, int64_t E, int k, int64_t O, int64_t P) {
     L.pos = off;        off += align_up(sizeof(int32_t) * mk);
     L.tiles = off;      off += align_up(sizeof(int32_t) * 3 * (L.max_tiles + 1));
     L.tile_count = off; off += kAlign;
+    // block histograms sized for the router form's 16-token blocks (the most blocks)
+    L.blk_counts = off; off += align_up(sizeof(int32_t) * E * ffn::moe_route_blocks_a(M, E, true));
+    L.blk_base = off;   off += align_up(sizeof(int32_t) * E * ffn::moe_route_blocks_b(M));
     L.part = off;       off += align_up(sizeof(float) * (size_t)L.splits * mk * P);
     L.total = off;
     return L;
@@ -415,18 +419,34 @@ size_t moe_workspace_size(int64_t M, int64_t E, int k, int64_t N, int64_t O, int
     return moe_layout(M, E, k, O, P).total;
 }
 
-static int route_into(const float* logits, int64_t M, int64_t E, int k, const MoeLayout& L,
-                      char* ws, int32_t** ids, float** w, hipStream_t st) {
+// Routing into the workspace: from `logits`, or (logits == NULL) from the
+// router X Wr + br, whose logits go to logits_out when it is not NULL.
+static int route_into(const float* logits, const void* X, const void* Wr, const float* br,
+                      float* logits_out, int64_t M, int64_t N, int64_t E, int k,
+                      const MoeLayout& L, char* ws, int32_t** ids, float** w, hipStream_t st) {
     *ids = reinterpret_cast<int32_t*>(ws + L.ids);
     *w = reinterpret_cast<float*>(ws + L.w);
-    return launched(ffn::launch_moe_route(logits, M, E, k, *ids, *w,
-                                          reinterpret_cast<int32_t*>(ws + L.counts),
-                                          reinterpret_cast<int32_t*>(ws + L.offsets),
-                                          reinterpret_cast<int32_t*>(ws + L.sorted),
-                                          reinterpret_cast<int32_t*>(ws + L.pos),
-                                          reinterpret_cast<int32_t*>(ws + L.tiles),
-                                          reinterpret_cast<int32_t*>(ws + L.tile_count), st),
-                    "routing kernel");
+    ffn::RouteIO io;
+    io.logits = logits;
+    io.X = static_cast<const uint16_t*>(X);
+    io.Wr = static_cast<const uint16_t*>(Wr);
+    io.br = br;
+    io.logits_out = logits ? nullptr : logits_out;
+    io.M = M;
+    io.N = N;
+    io.E = E;
+    io.k = k;
+    io.ids = *ids;
+    io.w = *w;
+    io.counts = reinterpret_cast<int32_t*>(ws + L.counts);
+    io.offsets = reinterpret_cast<int32_t*>(ws + L.offsets);
+    io.sorted = reinterpret_cast<int32_t*>(ws + L.sorted);
+    io.pos = reinterpret_cast<int32_t*>(ws + L.pos);
+    io.tiles = reinterpret_cast<int32_t*>(ws + L.tiles);
+    io.tile_count = reinterpret_cast<int32_t*>(ws + L.tile_count);
+    io.blk_counts = reinterpret_cast<int32_t*>(ws + L.blk_counts);
+    io.blk_base = reinterpret_cast<int32_t*>(ws + L.blk_base);
+    return launched(ffn::launch_moe_route(io, st), "routing kernels");
 }
 
 static int copy_route_outputs(int64_t M, int64_t E, int k, const MoeLayout& L, const char* ws,
@@ -463,19 +483,33 @@ int moe_route(const float* logits, int64_t M, int64_t E, int k, int32_t* topk_id
     char* ws = static_cast<char*>(workspace);
     int32_t* ids;
     float* w;
-    rc = route_into(logits, M, E, k, L, ws, &ids, &w, st);
+    rc = route_into(logits, nullptr, nullptr, nullptr, nullptr, M, 0, E, k, L, ws, &ids, &w, st);
     if (rc) return rc;
     rc = copy_route_outputs(M, E, k, L, ws, topk_ids, topk_w, expert_offsets, sorted_entries, st);
     if (rc) return rc;
     return ok();
 }
 
-static int moe_forward(const void* X, const float* logits, int64_t M, int64_t E, int k,
-                       const void* W1, const void* b1, const void* W2, const void* b2, void* Y,
-                       int64_t N, int64_t O, int64_t P, int dtype, int act1, int act2,
-                       int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
-                       int32_t* sorted_entries, void* workspace, size_t workspace_bytes,
-                       void* stream, void** events, int n_events) {
+// Host checks of the router form's own arguments (X itself is checked by the caller).
+static int check_router_args(const void* Wr, const float* br, const float* logits_out, int64_t E) {
+    if (!Wr) return fail(FFN_EINVAL, "Wr must not be NULL");
+    if (!aligned16(Wr)) return fail(FFN_EALIGN, "Wr is not 16-byte aligned");
+    if (E % 8 != 0) return fail(FFN_EUNSUPPORTED, "the router form takes E % 8 == 0 (got %lld)", (long long)E);
+    if (reinterpret_cast<uintptr_t>(br) & 3u) return fail(FFN_EALIGN, "br not 4-byte aligned");
+    if (reinterpret_cast<uintptr_t>(logits_out) & 3u)
+        return fail(FFN_EALIGN, "logits_out not 4-byte aligned");
+    return FFN_OK;
+}
+
+// logits != NULL: routing from the given logits (Wr, br, logits_out unused);
+// logits == NULL: the router form (logits = X Wr + br on the GPU).
+static int moe_forward(const void* X, const float* logits, const void* Wr, const float* br,
+                       float* logits_out, int64_t M, int64_t E, int k, const void* W1,
+                       const void* b1, const void* W2, const void* b2, void* Y, int64_t N,
+                       int64_t O, int64_t P, int dtype, int act1, int act2, int32_t* topk_ids,
+                       float* topk_w, int32_t* expert_offsets, int32_t* sorted_entries,
+                       void* workspace, size_t workspace_bytes, void* stream, void** events,
+                       int n_events) {
     if (events && n_events < 4) return fail(FFN_EINVAL, "traced MoE calls take at least 4 events");
     int rc = check_moe_dims(M, E, k);
     if (rc) return rc;
@@ -484,8 +518,12 @@ static int moe_forward(const void* X, const float* logits, int64_t M, int64_t E,
     if (dtype != FFN_BF16) return fail(FFN_EUNSUPPORTED, "the grouped form takes bf16 only");
     if (!valid_act(act1) || !valid_act(act2))
         return fail(FFN_EINVAL, "unknown activation (act1=%d, act2=%d)", act1, act2);
-    if (!logits) return fail(FFN_EINVAL, "logits must not be NULL");
-    if (reinterpret_cast<uintptr_t>(logits) & 3u) return fail(FFN_EALIGN, "logits not 4-byte aligned");
+    if (logits) {
+        if (reinterpret_cast<uintptr_t>(logits) & 3u) return fail(FFN_EALIGN, "logits not 4-byte aligned");
+    } else {
+        rc = check_router_args(Wr, br, logits_out, E);
+        if (rc) return rc;
+    }
     rc = check_common_ptrs(X, W1, b1, W2, b2, Y, workspace, M);
     if (rc) return rc;
     if (M * N >= ((int64_t)1 << 30))
@@ -500,7 +538,7 @@ static int moe_forward(const void* X, const float* logits, int64_t M, int64_t E,
     int32_t* ids;
     float* w;
     if ((rc = mark(events, n_events, 0, st))) return rc;
-    rc = route_into(logits, M, E, k, L, ws, &ids, &w, st);
+    rc = route_into(logits, X, Wr, br, logits_out, M, N, E, k, L, ws, &ids, &w, st);
     if (rc) return rc;
     if ((rc = mark(events, n_events, 1, st))) return rc;
 
@@ -537,9 +575,49 @@ int moe_ffn_forward(const void* X, const float* logits, int64_t M, int64_t E, in
                     int32_t* topk_ids, float* topk_w, int32_t* expert_offsets,
                     int32_t* sorted_entries, void* workspace, size_t workspace_bytes,
                     void* stream) {
-    return moe_forward(X, logits, M, E, k, W1, b1, W2, b2, Y, N, O, P, dtype, act1, act2,
-                       topk_ids, topk_w, expert_offsets, sorted_entries, workspace,
+    if (!logits) return fail(FFN_EINVAL, "logits must not be NULL");
+    return moe_forward(X, logits, nullptr, nullptr, nullptr, M, E, k, W1, b1, W2, b2, Y, N, O, P,
+                       dtype, act1, act2, topk_ids, topk_w, expert_offsets, sorted_entries,
+                       workspace, workspace_bytes, stream, nullptr, 0);
+}
+
+int moe_ffn_forward_router(const void* X, const void* Wr, const float* br, int64_t M, int64_t E,
+                           int k, const void* W1, const void* b1, const void* W2, const void* b2,
+                           void* Y, int64_t N, int64_t O, int64_t P, int dtype, int act1,
+                           int act2, float* logits_out, int32_t* topk_ids, float* topk_w,
+                           int32_t* expert_offsets, int32_t* sorted_entries, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+    return moe_forward(X, nullptr, Wr, br, logits_out, M, E, k, W1, b1, W2, b2, Y, N, O, P, dtype,
+                       act1, act2, topk_ids, topk_w, expert_offsets, sorted_entries, workspace,
                        workspace_bytes, stream, nullptr, 0);
+}
+
+int moe_router(const void* X, const void* Wr, const float* br, int64_t M, int64_t N, int64_t E,
+               int k, float* logits_out, int32_t* topk_ids, float* topk_w,
+               int32_t* expert_offsets, int32_t* sorted_entries, void* workspace,
+               size_t workspace_bytes, void* stream) {
+    int rc = check_moe_dims(M, E, k);
+    if (rc) return rc;
+    if (N < 8 || N % 8 != 0) return fail(FFN_EUNSUPPORTED, "N must be a positive multiple of 8");
+    if ((M > 0 && !X) || !workspace) return fail(FFN_EINVAL, "X and workspace must not be NULL");
+    if (X && !aligned16(X)) return fail(FFN_EALIGN, "X is not 16-byte aligned");
+    rc = check_router_args(Wr, br, logits_out, E);
+    if (rc) return rc;
+    if (reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1))
+        return fail(FFN_EALIGN, "workspace is not 256-byte aligned");
+    const MoeLayout L = moe_layout(M, E, k, 8, 8);
+    if (workspace_bytes < L.part) return fail(FFN_EWORKSPACE, "workspace has %zu bytes, needs %zu",
+                                              workspace_bytes, L.part);
+    if (M == 0) return ok();
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(workspace);
+    int32_t* ids;
+    float* w;
+    rc = route_into(nullptr, X, Wr, br, logits_out, M, N, E, k, L, ws, &ids, &w, st);
+    if (rc) return rc;
+    rc = copy_route_outputs(M, E, k, L, ws, topk_ids, topk_w, expert_offsets, sorted_entries, st);
+    if (rc) return rc;
+    return ok();
 }
 
 int moe_ffn_forward_traced(const void* X, const float* logits, int64_t M, int64_t E, int k,
@@ -548,9 +626,10 @@ int moe_ffn_forward_traced(const void* X, const float* logits, int64_t M, int64_
                            int act2, void* workspace, size_t workspace_bytes, void* stream,
                            void** events, int n_events) {
     if (!events) return fail(FFN_EINVAL, "events must not be NULL");
-    return moe_forward(X, logits, M, E, k, W1, b1, W2, b2, Y, N, O, P, dtype, act1, act2,
-                       nullptr, nullptr, nullptr, nullptr, workspace, workspace_bytes, stream,
-                       events, n_events);
+    if (!logits) return fail(FFN_EINVAL, "logits must not be NULL");
+    return moe_forward(X, logits, nullptr, nullptr, nullptr, M, E, k, W1, b1, W2, b2, Y, N, O, P,
+                       dtype, act1, act2, nullptr, nullptr, nullptr, nullptr, workspace,
+                       workspace_bytes, stream, events, n_events);
 }
 
 // ---------------------------------------------------------------- self-check

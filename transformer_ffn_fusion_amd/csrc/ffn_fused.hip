@@ -9,8 +9,8 @@
 //
 // gfx950 design (differs from the page's, which targets a GPU with
 // asynchronous tile reductions into global memory):
-//  * one workgroup = 64 token rows x one hidden chunk of C columns (C = 448
-//    or 512).  GEMM1 (K = N) runs on bf16 MFMA with fp32 accumulators; the
+//  * one workgroup = 64 token rows x one hidden chunk of C columns (C = 256,
+//    448 or 512).  GEMM1 (K = N) runs on bf16 MFMA with fp32 accumulators; the
 //    epilogue adds b1, applies the activation, rounds once to bf16 and writes
 //    the 64 x C tile of H into LDS in the operand layout GEMM2 reads;
 //  * GEMM2 sweeps the output columns in passes of 512, reading H from LDS and
@@ -567,12 +567,14 @@ hipError_t launch_fused_impl(const FusedArgs& a, int64_t units, hipStream_t stre
 
 int fused_pick_chunk(int64_t O) {
     // prefer an exact chunk whose split count lets every XCD own one chunk
-    // (the split count divides 8), then any exact chunk, fewest splits first
-    for (int c : {512, 448})
+    // (the split count divides 8), then any exact chunk, fewest splits first;
+    // a hidden width of at most 256 (an expert's share of a sharded layer)
+    // takes the 256-wide chunk instead of half-empty wider ones
+    for (int c : {512, 448, 256})
         if (O % c == 0 && 8 % (O / c) == 0) return c;
     if (O % 512 == 0) return 512;
     if (O % 448 == 0) return 448;
-    return 512;
+    return O <= 256 ? 256 : 512;
 }
 
 int fused_num_splits(int64_t O, int chunk) { return (int)((O + chunk - 1) / chunk); }
@@ -602,6 +604,9 @@ hipError_t launch_fused_bf16(const uint16_t* X, const uint16_t* W1, const uint16
     if (chunk == 448)
         return grouped ? launch_fused_impl<448, 0, true, false>(a, units, stream)
                        : launch_fused_impl<448, 0, false, false>(a, units, stream);
+    if (chunk == 256)
+        return grouped ? launch_fused_impl<256, 0, true, false>(a, units, stream)
+                       : launch_fused_impl<256, 0, false, false>(a, units, stream);
     return grouped ? launch_fused_impl<512, 0, true, false>(a, units, stream)
                    : launch_fused_impl<512, 0, false, false>(a, units, stream);
 }

@@ -15,7 +15,7 @@ constexpr int kBM = 64;     // token rows per workgroup tile
 constexpr int kBN2 = 512;   // output columns per second-layer pass
 
 // Hidden-chunk widths the fused kernel is instantiated for.
-int fused_pick_chunk(int64_t O);                 // 448 or 512
+int fused_pick_chunk(int64_t O);                 // 256, 448 or 512
 int fused_num_splits(int64_t O, int chunk);      // ceil(O / chunk)
 
 struct GroupedRows {
@@ -78,10 +78,32 @@ hipError_t launch_fused_swiglu_f32(const float* X, const float* Wg, const float*
 // ---- Mixture-of-Experts
 
 int64_t moe_max_tiles(int64_t M, int64_t E, int k);
-hipError_t launch_moe_route(const float* logits, int64_t M, int64_t E, int k, int32_t* ids,
-                            float* w, int32_t* counts, int32_t* offsets, int32_t* sorted,
-                            int32_t* pos, int32_t* tiles, int32_t* tile_count,
-                            hipStream_t stream);
+
+// Routing: top-k per token block (from the logits, or from X Wr + br when
+// `logits` is null), then a one-workgroup scan (counts, offsets, block bases,
+// tile table), then a parallel stable scatter into the per-expert lists.
+struct RouteIO {
+    const float* logits = nullptr;     // M x E fp32 gate logits, or null for the router form
+    const uint16_t* X = nullptr;       // router form: M x N bf16
+    const uint16_t* Wr = nullptr;      // router form: N x E bf16, E % 8 == 0
+    const float* br = nullptr;         // router form: E fp32 or null
+    float* logits_out = nullptr;       // router form: M x E fp32 or null
+    int64_t M = 0, N = 0, E = 0;
+    int k = 1;
+    int32_t* ids = nullptr;            // M x k
+    float* w = nullptr;                // M x k
+    int32_t* counts = nullptr;         // E
+    int32_t* offsets = nullptr;        // E + 1
+    int32_t* sorted = nullptr;         // M x k
+    int32_t* pos = nullptr;            // M x k
+    int32_t* tiles = nullptr;          // moe_max_tiles x 3
+    int32_t* tile_count = nullptr;     // 1
+    int32_t* blk_counts = nullptr;     // moe_route_blocks_a x E
+    int32_t* blk_base = nullptr;       // moe_route_blocks_b x E
+};
+int64_t moe_route_blocks_a(int64_t M, int64_t E, bool router);
+int64_t moe_route_blocks_b(int64_t M);
+hipError_t launch_moe_route(const RouteIO& io, hipStream_t stream);
 hipError_t launch_moe_combine(const float* part, int splits, int64_t rows_total,
                               const int32_t* pos, const int32_t* ids, const float* w,
                               const uint16_t* b2, uint16_t* Y, int64_t M, int k, int64_t P,

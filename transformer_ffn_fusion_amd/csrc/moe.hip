@@ -21,179 +21,300 @@ namespace ffn {
 
 namespace {
 
-constexpr int kRouteThreads = 1024;
-constexpr int kRouteWaves = kRouteThreads / 64;
+constexpr int kTopkThreads = 256;
+constexpr int kScanThreads = 1024;
+constexpr int kScatterTokens = 256;   // tokens per workgroup of the scatter
+constexpr int kRouterTokens = 16;     // tokens per workgroup of the router form
 constexpr int kMaxE = 256;
-constexpr int kLogitStage = 8192;   // floats of router logits staged in LDS per token block
+constexpr int kLogitStage = 8192;     // floats of logits held in LDS per workgroup
 
-// One workgroup.  Pass 1 stages a block of router logits in LDS with coalesced
-// loads and gives each token to one thread (top-k by insertion into a list
-// sorted by decreasing logit, an equal logit staying behind the earlier
-// expert, which is the repeated strict arg-max order), then the gate weights
-// and the expert histogram.  Pass 2 scatters the entries into the per-expert
-// lists in token order: inside a block every wave ranks its entries per
-// expert with ballots, one barrier publishes the per-wave counts, and each
-// entry's position is the expert's running offset plus the counts of earlier
-// waves plus its rank.
+// Tokens per top-k workgroup: 16 with the router GEMM; with logits as input,
+// the largest power of two <= 256 whose logits fit the LDS stage.
+int topk_block_tokens(int64_t E, bool router) {
+    if (router) return kRouterTokens;
+    int tb = kScatterTokens;
+    while (tb > 1 && (int64_t)tb * E > kLogitStage) tb >>= 1;
+    return tb;
+}
+
+// The k largest logits of one row, in decreasing order.  Insertion into a
+// sorted list where an equal logit stays behind the earlier expert: the order
+// of repeated strict arg-max (ties to the smaller expert index).
 template <int k>
-__global__ __launch_bounds__(kRouteThreads) void moe_route_kernel(
-    const float* __restrict__ logits, int64_t M, int E, int32_t* ids, float* w,
-    int32_t* counts, int32_t* offsets, int32_t* sorted, int32_t* pos, int32_t* tiles,
-    int32_t* tile_count) {
+__device__ __forceinline__ void topk_row(const float* row, int E, float (&bv)[k], int (&be)[k]) {
+#pragma unroll
+    for (int j = 0; j < k; ++j) { bv[j] = 0.f; be[j] = 0; }
+    int nf = 0;
+    for (int e = 0; e < E; ++e) {
+        const float v = row[e];
+        int p = 0;   // entries that stay ahead: larger or equal logit
+#pragma unroll
+        for (int j = 0; j < k; ++j) p += (j < nf && bv[j] >= v) ? 1 : 0;
+        if (p >= k) continue;
+#pragma unroll
+        for (int j = k - 1; j > 0; --j)
+            if (j > p) { bv[j] = bv[j - 1]; be[j] = be[j - 1]; }
+#pragma unroll
+        for (int j = 0; j < k; ++j)
+            if (j == p) { bv[j] = v; be[j] = e; }
+        nf = nf + 1 < k ? nf + 1 : k;
+    }
+}
+
+struct TopkArgs {
+    const float* logits;    // input form: M x E
+    const uint16_t* X;      // router form: M x N bf16
+    const uint16_t* Wr;     //              N x E bf16 (E % 8 == 0)
+    const float* br;        //              E, or null
+    float* logits_out;      //              M x E, or null
+    int64_t M, N;
+    int E;
+    int tb;                 // tokens per workgroup
+    int32_t* ids;
+    float* w;
+    int32_t* blk_counts;    // [blocks][E]
+};
+
+// Routing step 1 (the review, section 2.2: the gate gives every token its
+// expert assignments and gate weights), one block of tokens per workgroup:
+// the block's logits into LDS -- read, or computed as X Wr + br (the gate
+// read as one linear layer) -- then per token the top-k and the softmax over
+// the k selected logits, and the block's expert histogram.
+//
+// Router form: wave v owns tokens 4v..4v+3 of the block, lane l the k-slices
+// 8l + 512i (16-byte loads of X: one wave reads 1 KiB of a row at once), for
+// 8 experts at a time; the 64 lanes' partial sums are then added in lane
+// order through LDS, so every logit has one fixed summation order.
+template <int k, bool kRouter>
+__global__ __launch_bounds__(kTopkThreads) void moe_topk_kernel(TopkArgs a) {
     __shared__ float s_log[kLogitStage];
     __shared__ int s_cnt[kMaxE];
-    __shared__ int s_run[kMaxE];
-    __shared__ int s_off[kMaxE];
-    __shared__ int s_wcnt[kRouteWaves][kMaxE];
-
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
-    for (int e = tid; e < E; e += kRouteThreads) s_cnt[e] = 0;
+    const int E = a.E;
+    const int64_t base = (int64_t)blockIdx.x * a.tb;
+    const int nb = (a.M - base) < a.tb ? (int)(a.M - base) : a.tb;
+    for (int e = tid; e < E; e += kTopkThreads) s_cnt[e] = 0;
 
-    // ---- pass 1: top-k and gate weights per token, expert histogram
-    const int tb = (kLogitStage / E) < kRouteThreads ? (kLogitStage / E) : kRouteThreads;
-    for (int64_t base = 0; base < M; base += tb) {
-        const int nb = (M - base) < tb ? (int)(M - base) : tb;
-        __syncthreads();   // the previous block's logits are no longer read
-        for (int i0 = tid; i0 < nb * E; i0 += 8 * kRouteThreads) {   // 8 loads in flight
+    if constexpr (kRouter) {
+        __shared__ float s_red[4][32][65];   // [wave][token*8 + expert][lane], padded rows
+        const int wv = tid >> 6, kl = tid & 63;
+        for (int e0 = 0; e0 < E; e0 += 8) {
+            float acc[4][8];
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) acc[i][e] = 0.f;
+            for (int64_t k0 = 8 * kl; k0 < a.N; k0 += 512) {
+                uint4 xr[4], wr[8];
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    xr[i] = (4 * wv + i < nb) ? ld16(a.X + (base + 4 * wv + i) * a.N + k0)
+                                              : make_uint4(0u, 0u, 0u, 0u);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) wr[j] = ld16(a.Wr + (k0 + j) * E + e0);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const uint32_t ww[4] = {wr[j].x, wr[j].y, wr[j].z, wr[j].w};
+                    float wf[8];
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) { wf[2 * q] = bf16_lo(ww[q]); wf[2 * q + 1] = bf16_hi(ww[q]); }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const uint32_t xw[4] = {xr[i].x, xr[i].y, xr[i].z, xr[i].w};
+                        const float x = (j & 1) ? bf16_hi(xw[j >> 1]) : bf16_lo(xw[j >> 1]);
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) acc[i][e] = fmaf(x, wf[e], acc[i][e]);
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) s_red[wv][8 * i + e][kl] = acc[i][e];
+            __syncthreads();
+            if (kl < 32) {
+                float sum = 0.f;
+                for (int l = 0; l < 64; ++l) sum += s_red[wv][kl][l];
+                const int e = e0 + (kl & 7);
+                s_log[(4 * wv + (kl >> 3)) * E + e] = sum + (a.br ? a.br[e] : 0.f);
+            }
+            __syncthreads();
+        }
+    } else {
+        // stage the block's logits with coalesced loads, 8 in flight per thread
+        const int n = nb * E;
+        const float* src = a.logits + base * E;
+        for (int i0 = tid; i0 < n; i0 += 8 * kTopkThreads) {
             float v[8];
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const int i = i0 + u * kRouteThreads;
-                v[u] = i < nb * E ? logits[base * E + i] : 0.f;
+                const int i = i0 + u * kTopkThreads;
+                v[u] = i < n ? src[i] : 0.f;
             }
 #pragma unroll
             for (int u = 0; u < 8; ++u) {
-                const int i = i0 + u * kRouteThreads;
-                if (i < nb * E) s_log[i] = v[u];
+                const int i = i0 + u * kTopkThreads;
+                if (i < n) s_log[i] = v[u];
             }
         }
         __syncthreads();
-        const bool act = tid < nb;
+    }
+
+    if (tid < nb) {
         const int64_t t = base + tid;
-        const float* row = s_log + tid * E;
         float bv[k];
         int be[k];
-#pragma unroll
-        for (int j = 0; j < k; ++j) { bv[j] = 0.f; be[j] = 0; }
-        int nf = 0;
-        for (int e = 0; act && e < E; ++e) {
-            const float v = row[e];
-            int p = 0;   // entries that stay ahead: larger or equal logit
-#pragma unroll
-            for (int j = 0; j < k; ++j) p += (j < nf && bv[j] >= v) ? 1 : 0;
-            if (p >= k) continue;
-#pragma unroll
-            for (int j = k - 1; j > 0; --j)
-                if (j > p && j < k) { bv[j] = bv[j - 1]; be[j] = be[j - 1]; }
-#pragma unroll
-            for (int j = 0; j < k; ++j)
-                if (j == p) { bv[j] = v; be[j] = e; }
-            nf = nf + 1 < k ? nf + 1 : k;
-        }
+        topk_row<k>(s_log + tid * E, E, bv, be);
         float ex[k];
         float den = 0.f;
 #pragma unroll
         for (int s = 0; s < k; ++s) {
-            if (s < k) {
-                ex[s] = expf(bv[s] - bv[0]);
-                den += ex[s];
-            }
+            ex[s] = expf(bv[s] - bv[0]);
+            den += ex[s];
         }
 #pragma unroll
         for (int s = 0; s < k; ++s) {
-            if (act && s < k) {
-                ids[t * k + s] = be[s];
-                w[t * k + s] = ex[s] / den;
-            }
-        }
-        // expert histogram: one LDS add per wave and expert (ballot counts), not
-        // one contended add per entry
-        for (int e = 0; e < E; ++e) {
-            int c = 0;
-#pragma unroll
-            for (int s = 0; s < k; ++s) c += __popcll(__ballot(act && s < k && be[s] == e));
-            if (lane == 0 && c) atomicAdd(&s_cnt[e], c);
+            a.ids[t * k + s] = be[s];
+            a.w[t * k + s] = ex[s] / den;
+            atomicAdd(&s_cnt[be[s]], 1);   // a count: the order of the adds does not matter
         }
     }
     __syncthreads();
+    for (int e = tid; e < E; e += kTopkThreads) a.blk_counts[(int64_t)blockIdx.x * E + e] = s_cnt[e];
+    if (kRouter && a.logits_out)
+        for (int i = tid; i < nb * E; i += kTopkThreads) a.logits_out[base * E + i] = s_log[i];
+}
 
-    // ---- per-expert counts and exclusive offsets
+// Per-expert totals and exclusive offsets, the base position of every
+// scatter block in every expert's list, and the tile table (heaviest expert
+// first, ties to the smaller index; tiles of at most 64 rows).  One
+// workgroup: for each expert, tpe threads each own a contiguous run of
+// scatter blocks; integer sums only.
+__global__ __launch_bounds__(kScanThreads) void moe_scan_kernel(
+    const int32_t* __restrict__ blk_counts, int64_t nblk_a, int group, int64_t nblk_b, int E,
+    int32_t* counts, int32_t* offsets, int32_t* blk_base, int32_t* tiles, int32_t* tile_count) {
+    __shared__ int s_part[kScanThreads];
+    __shared__ int s_tot[kMaxE];
+    __shared__ int s_off[kMaxE];
+    __shared__ int s_order[kMaxE];
+    __shared__ int s_done[kMaxE];
+    __shared__ int s_tstart[kMaxE + 1];
+    const int tid = threadIdx.x;
+    int epow = 1;
+    while (epow < E) epow <<= 1;
+    const int tpe = kScanThreads / epow;
+    const int e = tid / tpe, r = tid % tpe;
+    const bool act = e < E;
+    const int64_t per = (nblk_b + tpe - 1) / tpe;
+    const int64_t b0 = r * per;
+    const int64_t b1 = (b0 + per) < nblk_b ? (b0 + per) : nblk_b;
+    auto bcount = [&](int64_t bb) {
+        int c = 0;
+        for (int q = 0; q < group; ++q) {
+            const int64_t ba = bb * group + q;
+            if (ba < nblk_a) c += blk_counts[ba * E + e];
+        }
+        return c;
+    };
+    int sum = 0;
+    if (act)
+        for (int64_t bb = b0; bb < b1; ++bb) sum += bcount(bb);
+    s_part[tid] = sum;
+    __syncthreads();
+    int pre = 0;
+    if (act) {
+        for (int q = 0; q < r; ++q) pre += s_part[e * tpe + q];
+        if (r == 0) {
+            int tot = 0;
+            for (int q = 0; q < tpe; ++q) tot += s_part[e * tpe + q];
+            s_tot[e] = tot;
+        }
+    }
+    __syncthreads();
     if (tid == 0) {
         int run = 0;
-        for (int e = 0; e < E; ++e) {
-            counts[e] = s_cnt[e];
-            offsets[e] = run;
-            s_run[e] = run;
-            s_off[e] = run;
-            run += s_cnt[e];
+        for (int x = 0; x < E; ++x) {
+            s_off[x] = run;
+            counts[x] = s_tot[x];
+            offsets[x] = run;
+            run += s_tot[x];
+            s_done[x] = 0;
         }
         offsets[E] = run;
+        s_tstart[0] = 0;
+        for (int p = 0; p < E; ++p) {
+            int best = -1;
+            for (int x = 0; x < E; ++x)
+                if (!s_done[x] && (best < 0 || s_tot[x] > s_tot[best])) best = x;
+            s_done[best] = 1;
+            s_order[p] = best;
+            s_tstart[p + 1] = s_tstart[p] + (s_tot[best] + kBM - 1) / kBM;
+        }
+        *tile_count = s_tstart[E];
     }
     __syncthreads();
-
-    // ---- pass 2: stable scatter, entry t*k+s into its expert's list in token order
-    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
-    for (int64_t base = 0; base < M; base += kRouteThreads) {
-        const int64_t t = base + tid;
-        const bool have = t < M;
-        int mine[k], rank[k];
-#pragma unroll
-        for (int s = 0; s < k; ++s) {
-            mine[s] = (have && s < k) ? ids[t * k + s] : -1;
-            rank[s] = 0;
+    if (act) {
+        int run = s_off[e] + pre;
+        for (int64_t bb = b0; bb < b1; ++bb) {
+            blk_base[bb * E + e] = run;
+            run += bcount(bb);
         }
-        for (int e = 0; e < E; ++e) {
-            bool hit = false;   // the k picks of a token are distinct experts
-#pragma unroll
-            for (int s = 0; s < k; ++s) hit |= (mine[s] == e);
-            const uint64_t mask = __ballot(hit);
-            const int r = __popcll(mask & lt_mask);
-#pragma unroll
-            for (int s = 0; s < k; ++s)
-                if (mine[s] == e) rank[s] = r;
-            if (lane == 0) s_wcnt[wave][e] = __popcll(mask);
-        }
-        __syncthreads();
-#pragma unroll
-        for (int s = 0; s < k; ++s) {
-            const int e = mine[s];
-            if (e < 0) continue;
-            int before = 0;
-            for (int q = 0; q < wave; ++q) before += s_wcnt[q][e];
-            const int p = s_run[e] + before + rank[s];
-            sorted[p] = (int32_t)(t * k + s);
-            pos[t * k + s] = p;
-        }
-        __syncthreads();
-        for (int e = tid; e < E; e += kRouteThreads) {
-            int tot = 0;
-            for (int q = 0; q < kRouteWaves; ++q) tot += s_wcnt[q][e];
-            s_run[e] += tot;
-        }
-        __syncthreads();
     }
+    const int ntiles = s_tstart[E];
+    for (int i = tid; i < ntiles; i += kScanThreads) {
+        int p = 0;
+        while (s_tstart[p + 1] <= i) ++p;   // i < s_tstart[E]: stops at p < E
+        const int x = s_order[p];
+        const int r0 = (i - s_tstart[p]) * kBM;
+        tiles[3 * i + 0] = x;
+        tiles[3 * i + 1] = s_off[x] + r0;
+        tiles[3 * i + 2] = (s_tot[x] - r0) < kBM ? (s_tot[x] - r0) : kBM;
+    }
+}
 
-    // ---- tile table, heaviest expert first (ties: smaller index first)
-    if (tid == 0) {
-        int n = 0;
-        int* done = &s_wcnt[0][0];   // the per-wave counts are no longer needed
-        for (int e = 0; e < E; ++e) done[e] = 0;
-        for (int it = 0; it < E; ++it) {
-            int best = -1;
-            for (int e = 0; e < E; ++e)
-                if (!done[e] && (best < 0 || s_cnt[e] > s_cnt[best])) best = e;
-            done[best] = 1;
-            for (int r0 = 0; r0 < s_cnt[best]; r0 += kBM) {
-                const int v = (s_cnt[best] - r0) < kBM ? (s_cnt[best] - r0) : kBM;
-                tiles[3 * n + 0] = best;
-                tiles[3 * n + 1] = s_off[best] + r0;
-                tiles[3 * n + 2] = v;
-                ++n;
-            }
-        }
-        *tile_count = n;
+// Stable scatter of the entries t*k+s into their experts' lists, in token
+// order, one block of 256 tokens per workgroup: inside a wave each entry is
+// ranked among the wave's entries of the same expert with a ballot; one
+// barrier publishes the per-wave counts; the position is the block's base
+// for the expert plus the counts of earlier waves plus the rank.
+template <int k>
+__global__ __launch_bounds__(kScatterTokens) void moe_scatter_kernel(
+    const int32_t* __restrict__ ids, int64_t M, int E, const int32_t* __restrict__ blk_base,
+    int32_t* sorted, int32_t* pos) {
+    __shared__ int s_wcnt[kScatterTokens / 64][kMaxE];
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = tid >> 6;
+    const int64_t t = (int64_t)blockIdx.x * kScatterTokens + tid;
+    const bool have = t < M;
+    const uint64_t lt_mask = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+    int mine[k], rank[k];
+#pragma unroll
+    for (int s = 0; s < k; ++s) {
+        mine[s] = have ? ids[t * k + s] : -1;
+        rank[s] = 0;
+    }
+    for (int e = 0; e < E; ++e) {
+        bool hit = false;   // the k picks of a token are distinct experts
+#pragma unroll
+        for (int s = 0; s < k; ++s) hit |= (mine[s] == e);
+        const uint64_t mask = __ballot(hit);
+        const int r = __popcll(mask & lt_mask);
+#pragma unroll
+        for (int s = 0; s < k; ++s)
+            if (mine[s] == e) rank[s] = r;
+        if (lane == 0) s_wcnt[wave][e] = __popcll(mask);
+    }
+    __syncthreads();
+#pragma unroll
+    for (int s = 0; s < k; ++s) {
+        const int e = mine[s];
+        if (e < 0) continue;
+        int before = 0;
+        for (int q = 0; q < wave; ++q) before += s_wcnt[q][e];
+        const int p = blk_base[(int64_t)blockIdx.x * E + e] + before + rank[s];
+        sorted[p] = (int32_t)(t * k + s);
+        pos[t * k + s] = p;
     }
 }
 
@@ -247,19 +368,62 @@ int64_t moe_max_tiles(int64_t M, int64_t E, int k) {
     return (M * k + E * (kBM - 1)) / kBM;
 }
 
-hipError_t launch_moe_route(const float* logits, int64_t M, int64_t E, int k, int32_t* ids,
-                            float* w, int32_t* counts, int32_t* offsets, int32_t* sorted,
-                            int32_t* pos, int32_t* tiles, int32_t* tile_count,
-                            hipStream_t stream) {
-    switch (k) {
-#define FFN_ROUTE_K(K)                                                                          \
-    case K:                                                                                      \
-        hipLaunchKernelGGL(moe_route_kernel<K>, dim3(1), dim3(kRouteThreads), 0, stream, logits, \
-                           M, (int)E, ids, w, counts, offsets, sorted, pos, tiles, tile_count);  \
+int64_t moe_route_blocks_a(int64_t M, int64_t E, bool router) {
+    const int tb = topk_block_tokens(E, router);
+    return (M + tb - 1) / tb;
+}
+
+int64_t moe_route_blocks_b(int64_t M) { return (M + kScatterTokens - 1) / kScatterTokens; }
+
+hipError_t launch_moe_route(const RouteIO& io, hipStream_t stream) {
+    const bool router = io.logits == nullptr;
+    TopkArgs a;
+    a.logits = io.logits;
+    a.X = io.X;
+    a.Wr = io.Wr;
+    a.br = io.br;
+    a.logits_out = io.logits_out;
+    a.M = io.M;
+    a.N = io.N;
+    a.E = (int)io.E;
+    a.tb = topk_block_tokens(io.E, router);
+    a.ids = io.ids;
+    a.w = io.w;
+    a.blk_counts = io.blk_counts;
+    const int64_t na = moe_route_blocks_a(io.M, io.E, router);
+    const int64_t nbk = moe_route_blocks_b(io.M);
+    if (na <= 0) return hipSuccess;
+    switch (io.k) {
+#define FFN_TOPK_K(K)                                                                             \
+    case K:                                                                                       \
+        if (router)                                                                               \
+            hipLaunchKernelGGL((moe_topk_kernel<K, true>), dim3((unsigned)na), dim3(kTopkThreads), \
+                               0, stream, a);                                                     \
+        else                                                                                      \
+            hipLaunchKernelGGL((moe_topk_kernel<K, false>), dim3((unsigned)na),                   \
+                               dim3(kTopkThreads), 0, stream, a);                                 \
         break;
-        FFN_ROUTE_K(1) FFN_ROUTE_K(2) FFN_ROUTE_K(3) FFN_ROUTE_K(4)
-        FFN_ROUTE_K(5) FFN_ROUTE_K(6) FFN_ROUTE_K(7) FFN_ROUTE_K(8)
-#undef FFN_ROUTE_K
+        FFN_TOPK_K(1) FFN_TOPK_K(2) FFN_TOPK_K(3) FFN_TOPK_K(4)
+        FFN_TOPK_K(5) FFN_TOPK_K(6) FFN_TOPK_K(7) FFN_TOPK_K(8)
+#undef FFN_TOPK_K
+        default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(moe_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, io.blk_counts, na,
+                       kScatterTokens / a.tb, nbk, a.E, io.counts, io.offsets, io.blk_base,
+                       io.tiles, io.tile_count);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    switch (io.k) {
+#define FFN_SCATTER_K(K)                                                                        \
+    case K:                                                                                     \
+        hipLaunchKernelGGL(moe_scatter_kernel<K>, dim3((unsigned)nbk), dim3(kScatterTokens), 0, \
+                           stream, io.ids, io.M, a.E, io.blk_base, io.sorted, io.pos);          \
+        break;
+        FFN_SCATTER_K(1) FFN_SCATTER_K(2) FFN_SCATTER_K(3) FFN_SCATTER_K(4)
+        FFN_SCATTER_K(5) FFN_SCATTER_K(6) FFN_SCATTER_K(7) FFN_SCATTER_K(8)
+#undef FFN_SCATTER_K
         default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -54,6 +54,12 @@ MOE = MoE("moe_top2_4096tok_8x4096x2048x4096", 4096, 8, 2, 4096, 2048, 4096, "bf
 
 ALL = (TINY_F32, DECODE, PREFILL, LARGE, MOE)
 
+# One GPU's share of the same MoE layer sharded 8 ways over the hidden width of
+# every expert (2048 / 8 = 256 per expert; the kernel-fusion post, section
+# "Results": expert sharding keeps all experts on every GPU with O/G columns).
+MOE_SHARD = MoE("moe_top2_4096tok_8x4096x256x4096_expert_shard", 4096, 8, 2, 4096, 256, 4096,
+                "bf16", "gelu_tanh", 0.02)
+
 
 @dataclass(frozen=True)
 class Gated:
