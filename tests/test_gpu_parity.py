@@ -201,6 +201,8 @@ def test_moe_workload():
     (130, 8, 2, 128, 512, 264),
     (257, 5, 3, 64, 904, 72),
     (64, 1, 1, 256, 448, 512),
+    (100, 4, 2, 128, 512, 4096),   # a short round: each unit cut into 8 pass ranges
+    (300, 8, 2, 64, 1024, 2048),   # 2 chunks, pass ranges of a 4-pass output
 ])
 def test_moe_shapes(M, E, k, N, O, P):
     log(f"case moe M={M} E={E} k={k} N={N} O={O} P={P}")
