@@ -72,6 +72,11 @@ def _bind(lib):
     lib.oracle_silu.restype = ctypes.c_double
     lib.oracle_router_logits.argtypes = [i32, vp, vp, vp, vp, i64, i64, i64, i64, dp]
     lib.oracle_router_logits.restype = ctypes.c_int
+    lib.oracle_act_grad.argtypes = [i32, ctypes.c_double]
+    lib.oracle_act_grad.restype = ctypes.c_double
+    lib.oracle_ffn_backward.argtypes = [i32, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32,
+                                        vp, i64, dp, vp, i64, dp, dp, dp, dp]
+    lib.oracle_ffn_backward.restype = ctypes.c_int
     lib.oracle_threads.argtypes = []
     lib.oracle_threads.restype = ctypes.c_int
     lib.oracle_act.argtypes = [i32, ctypes.c_double]
@@ -132,6 +137,44 @@ def ffn(X, W1, b1, W2, b2, act1=ACT_GELU_TANH, act2=ACT_NONE, rows=None, lib=Non
     if rc != 0:
         raise ValueError("oracle_ffn rejected its arguments")
     return Y
+
+
+def act_grad(kind: int, x: float, lib=None) -> float:
+    """The oracle's act1 derivative at one double."""
+    return (lib or load()).oracle_act_grad(kind, float(x))
+
+
+def ffn_backward(X, W1, b1, W2, dY, act1=ACT_GELU_TANH, rows=None, cols=None, lib=None):
+    """fp64 gradients of the FFN (act2 none) for the output gradient dY.
+
+    Returns (dX[rows], dW1[:, cols], db1[cols], dW2[cols, :], db2) with rows/cols
+    None meaning all; inputs as for ``ffn`` (dY in the same dtype as X)."""
+    lib = lib or load()
+    dt = _dtype_of(X)
+    M, N = X.shape
+    O = W1.shape[1]
+    P = W2.shape[1]
+    assert W1.shape == (N, O) and W2.shape == (O, P) and dY.shape == (M, P)
+    keep = [None if a is None else _as_input(a, dt) for a in (X, W1, b1, W2, dY)]
+    ptr = [None if k is None else k[1] for k in keep]
+    def idx(v, n):
+        if v is None:
+            return None, None, n
+        a = np.ascontiguousarray(np.asarray(v, dtype=np.int64))
+        return a, a.ctypes.data, a.size
+    rk, rp, nr = idx(rows, M)
+    ck, cp, nc = idx(cols, O)
+    dX = np.empty((nr, N), np.float64)
+    dW1 = np.empty((N, nc), np.float64)
+    db1 = np.empty(nc, np.float64)
+    dW2 = np.empty((nc, P), np.float64)
+    db2 = np.empty(P, np.float64)
+    rc = lib.oracle_ffn_backward(dt, ptr[0], ptr[1], ptr[2], ptr[3], ptr[4], M, N, O, P, int(act1),
+                                 rp, nr, dX.ctypes.data, cp, nc, dW1.ctypes.data, db1.ctypes.data,
+                                 dW2.ctypes.data, db2.ctypes.data)
+    if rc != 0:
+        raise ValueError("oracle_ffn_backward rejected its arguments")
+    return dX, dW1, db1, dW2, db2
 
 
 def silu(x: float, lib=None) -> float:

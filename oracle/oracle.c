@@ -21,6 +21,11 @@
  *    Y = H Wd, with silu(x) = x / (1 + exp(-x)) (the Swish-1 / SiLU unit of
  *    Ramachandran et al. and Elfwing et al.; the page names the activation
  *    but does not write it out).
+ *  - Same post, closing section: a fused backward pass is named as the next
+ *    step.  oracle_ffn_backward() is the plain chain rule of the two layers
+ *    (act2 none): with a = X W1 + b1, h = act1(a), Y = h W2 + b2 and the
+ *    output gradient dY: dh = dY W2^T, da = dh * act1'(a), dX = da W1^T,
+ *    dW1 = X^T da, db1 = sum_m da, dW2 = h^T dY, db2 = sum_m dY.
  *  - "Fine-Grained Compute-Communication Overlap for MoE" review
  *    (zhongzhuzhou.org), section 2.1 (Mixture-of-Experts, briefly) and 2.2
  *    (five steps): the router picks the top-k experts per token and the
@@ -75,6 +80,19 @@ double oracle_act(int act, double x) {
         return 0.5 * x * (1.0 + tanh(c * (x + 0.044715 * x * x * x)));
     }
     return x;
+}
+
+/* Derivative of act1: ReLU' = 1 for x > 0, else 0 (0 at the kink); GELU-tanh'
+ * = 0.5 (1 + tanh u) + 0.5 x (1 - tanh^2 u) u'(x), u = sqrt(2/pi) (x + 0.044715 x^3),
+ * u' = sqrt(2/pi) (1 + 3 * 0.044715 x^2); none: 1. */
+double oracle_act_grad(int act, double x) {
+    if (act == OR_ACT_RELU) return x > 0.0 ? 1.0 : 0.0;
+    if (act == OR_ACT_GELU_TANH) {
+        const double c = sqrt(2.0 / M_PI);
+        const double t = tanh(c * (x + 0.044715 * x * x * x));
+        return 0.5 * (1.0 + t) + 0.5 * x * (1.0 - t * t) * c * (1.0 + 3.0 * 0.044715 * x * x);
+    }
+    return 1.0;
 }
 
 /* One output row of the two-layer FFN, straight from the definition.
@@ -205,6 +223,118 @@ int oracle_swiglu(int dtype, const void* X, const void* Wg, const void* Wu, cons
         free(u);
         free(acc);
     }
+    return bad ? -1 : 0;
+}
+
+/* a[m][o] (pre-activation, with b1) and dh[m][o] = sum_p dY[m][p] W2[o][p]
+ * for one row m and one hidden column o. */
+static double bwd_a(int dtype, const void* X, const void* W1, const void* b1, int64_t m,
+                    int64_t o, int64_t N, int64_t O) {
+    double acc = 0.0;
+    for (int64_t n = 0; n < N; ++n) acc += load(dtype, X, m * N + n) * load(dtype, W1, n * O + o);
+    return acc + (b1 ? load(dtype, b1, o) : 0.0);
+}
+static double bwd_dh(int dtype, const void* W2, const void* dY, int64_t m, int64_t o, int64_t P) {
+    double acc = 0.0;
+    for (int64_t p = 0; p < P; ++p) acc += load(dtype, dY, m * P + p) * load(dtype, W2, o * P + p);
+    return acc;
+}
+
+/* Gradients of the two-layer FFN (act2 none) for the output gradient dY (M x P).
+ * dX for the nrows listed rows (rows == NULL: all M; dX nrows x N); for the
+ * ncols listed hidden columns (cols == NULL: all O) dW1 (N x ncols, column c
+ * for hidden column cols[c]), db1 (ncols) and dW2 (ncols x P); db2 (P).
+ * Any output may be NULL.  Sums run in ascending index order. */
+int oracle_ffn_backward(int dtype, const void* X, const void* W1, const void* b1, const void* W2,
+                        const void* dY, int64_t M, int64_t N, int64_t O, int64_t P, int act1,
+                        const int64_t* rows, int64_t nrows, double* dX, const int64_t* cols,
+                        int64_t ncols, double* dW1, double* db1, double* dW2, double* db2) {
+    if (!X || !W1 || !W2 || !dY || M < 0 || N < 1 || O < 1 || P < 1) return -1;
+    if (dtype != OR_F32 && dtype != OR_BF16) return -1;
+    if (act1 < OR_ACT_NONE || act1 > OR_ACT_GELU_TANH) return -1;
+    if (!rows) nrows = M;
+    if (!cols) ncols = O;
+    int bad = 0;
+    if (dX) {
+#pragma omp parallel
+        {
+            double* da = (double*)malloc(sizeof(double) * (size_t)O);
+            if (!da) {
+#pragma omp atomic write
+                bad = 1;
+            } else {
+#pragma omp for schedule(dynamic, 1)
+                for (int64_t r = 0; r < nrows; ++r) {
+                    const int64_t m = rows ? rows[r] : r;
+                    if (m < 0 || m >= M) {
+#pragma omp atomic write
+                        bad = 1;
+                        continue;
+                    }
+                    for (int64_t o = 0; o < O; ++o)
+                        da[o] = bwd_dh(dtype, W2, dY, m, o, P) *
+                                oracle_act_grad(act1, bwd_a(dtype, X, W1, b1, m, o, N, O));
+                    for (int64_t n = 0; n < N; ++n) {
+                        double acc = 0.0;
+                        for (int64_t o = 0; o < O; ++o) acc += da[o] * load(dtype, W1, n * O + o);
+                        dX[r * N + n] = acc;
+                    }
+                }
+            }
+            free(da);
+        }
+    }
+    if (dW1 || db1 || dW2) {
+#pragma omp parallel
+        {
+            double* da = (double*)malloc(sizeof(double) * (size_t)(M + 1));
+            double* h = (double*)malloc(sizeof(double) * (size_t)(M + 1));
+            if (!da || !h) {
+#pragma omp atomic write
+                bad = 1;
+            } else {
+#pragma omp for schedule(dynamic, 1)
+                for (int64_t c = 0; c < ncols; ++c) {
+                    const int64_t o = cols ? cols[c] : c;
+                    if (o < 0 || o >= O) {
+#pragma omp atomic write
+                        bad = 1;
+                        continue;
+                    }
+                    for (int64_t m = 0; m < M; ++m) {
+                        const double a = bwd_a(dtype, X, W1, b1, m, o, N, O);
+                        h[m] = oracle_act(act1, a);
+                        da[m] = bwd_dh(dtype, W2, dY, m, o, P) * oracle_act_grad(act1, a);
+                    }
+                    if (dW1)
+                        for (int64_t n = 0; n < N; ++n) {
+                            double acc = 0.0;
+                            for (int64_t m = 0; m < M; ++m) acc += load(dtype, X, m * N + n) * da[m];
+                            dW1[n * ncols + c] = acc;
+                        }
+                    if (db1) {
+                        double acc = 0.0;
+                        for (int64_t m = 0; m < M; ++m) acc += da[m];
+                        db1[c] = acc;
+                    }
+                    if (dW2)
+                        for (int64_t p = 0; p < P; ++p) {
+                            double acc = 0.0;
+                            for (int64_t m = 0; m < M; ++m) acc += h[m] * load(dtype, dY, m * P + p);
+                            dW2[c * P + p] = acc;
+                        }
+                }
+            }
+            free(da);
+            free(h);
+        }
+    }
+    if (db2)
+        for (int64_t p = 0; p < P; ++p) {
+            double acc = 0.0;
+            for (int64_t m = 0; m < M; ++m) acc += load(dtype, dY, m * P + p);
+            db2[p] = acc;
+        }
     return bad ? -1 : 0;
 }
 

@@ -464,6 +464,96 @@ def test_router_identity_and_rows():
 
 
 # ----------------------------------------------------------------------------
+# 7d. backward: gradients against central differences of the forward oracle
+# ----------------------------------------------------------------------------
+
+def _bwd_inputs(rng, M, N, O, P):
+    """Dyadic values (k/8, exact in fp32); b1 offset by 1/128 so that no
+    pre-activation is exactly 0 (ReLU's kink: the difference quotient there is
+    the mean of the two slopes, the reading of the derivative is 0)."""
+    X, W1, W2, dY = (_dyadic(rng, s) for s in [(M, N), (N, O), (O, P), (M, P)])
+    b1 = (_dyadic(rng, (O,)) + np.float32(1.0 / 128)).astype(np.float32)
+    b2 = _dyadic(rng, (P,))
+    return X, W1, b1, W2, b2, dY
+
+
+def _loss(X, W1, b1, W2, b2, dY, act, lib=None):
+    # L = sum(Y * dY): its gradient with respect to Y is dY
+    return float(np.sum(oracle.ffn(X, W1, b1, W2, b2, act1=act, lib=lib) * dY.astype(np.float64)))
+
+
+def _fd_grads(X, W1, b1, W2, b2, dY, act, lib=None, h=2.0 ** -10):
+    out = []
+    args = [X, W1, b1, W2, b2]
+    for idx in range(5):
+        base = args[idx]
+        g = np.zeros(base.shape, np.float64)
+        for pos in np.ndindex(base.shape):
+            vals = []
+            for sgn in (1, -1):
+                pert = base.copy()
+                pert[pos] = np.float32(base[pos] + sgn * h)     # exact: dyadic + 2^-10
+                a = list(args)
+                a[idx] = pert
+                vals.append(_loss(*a, dY, act, lib=lib))
+            g[pos] = (vals[0] - vals[1]) / (2 * h)
+        out.append(g)
+    return out   # dX, dW1, db1, dW2, db2
+
+
+@pytest.mark.parametrize("shape", [(3, 5, 4, 6), (2, 3, 7, 4)])
+@pytest.mark.parametrize("act", [NONE, RELU, GELU])
+def test_backward_matches_finite_differences(shape, act):
+    """Each gradient equals the central difference of the forward oracle: exactly
+    (to rounding) for the piecewise-linear activations, to O(h^2) for GELU."""
+    rng = np.random.default_rng(sum(shape) + act)
+    X, W1, b1, W2, b2, dY = _bwd_inputs(rng, *shape)
+    fd = _fd_grads(X, W1, b1, W2, b2, dY, act)
+    got = oracle.ffn_backward(X, W1, b1, W2, dY, act1=act)
+    tol = 1e-9 if act != GELU else 2e-5
+    for name, g, f in zip(["dX", "dW1", "db1", "dW2", "db2"], got, fd):
+        assert g.shape == f.shape, name
+        np.testing.assert_allclose(g, f, rtol=0, atol=tol * (1 + np.abs(f).max()), err_msg=name)
+
+
+def test_act_grad_pins():
+    # GELU-tanh' against a central difference of GELU-tanh itself
+    for x in np.linspace(-5, 5, 41):
+        h = 1e-5
+        fd = (oracle.act(GELU, x + h) - oracle.act(GELU, x - h)) / (2 * h)
+        assert abs(oracle.act_grad(GELU, x) - fd) < 1e-8
+    assert oracle.act_grad(GELU, 0.0) == 0.5
+    assert oracle.act_grad(RELU, 2.0) == 1.0 and oracle.act_grad(RELU, -2.0) == 0.0
+    assert oracle.act_grad(RELU, 0.0) == 0.0
+    assert oracle.act_grad(NONE, -3.0) == 1.0
+
+
+def test_backward_relu_identity_closed_form():
+    """N = O = P, W1 = W2 = I, b1 = 0: dX = dY * [X > 0] exactly."""
+    n = 12
+    rng = np.random.default_rng(21)
+    X = rng.standard_normal((7, n)).astype(np.float32)
+    dY = rng.standard_normal((7, n)).astype(np.float32)
+    eye = np.eye(n, dtype=np.float32)
+    dX = oracle.ffn_backward(X, eye, np.zeros(n, np.float32), eye, dY, act1=RELU)[0]
+    assert np.array_equal(dX, dY.astype(np.float64) * (X > 0))
+
+
+def test_backward_subsets_bit_exact():
+    M, N, O, P = 9, 16, 24, 8
+    X, W1, b1, W2, b2 = synth.dense_inputs(M, N, O, P, dtype="bf16", seed=4)
+    dY = synth.f32_to_bf16_bits(np.random.default_rng(6).standard_normal((M, P)).astype(np.float32))
+    full = oracle.ffn_backward(X, W1, b1, W2, dY, act1=GELU)
+    rows, cols = [8, 0, 3], [23, 1, 7]
+    sub = oracle.ffn_backward(X, W1, b1, W2, dY, act1=GELU, rows=rows, cols=cols)
+    assert np.array_equal(sub[0], full[0][rows])
+    assert np.array_equal(sub[1], full[1][:, cols])
+    assert np.array_equal(sub[2], full[2][cols])
+    assert np.array_equal(sub[3], full[3][cols])
+    assert np.array_equal(sub[4], full[4])
+
+
+# ----------------------------------------------------------------------------
 # 8. planted mistakes in the oracle must be caught (CPU only)
 # ----------------------------------------------------------------------------
 
@@ -492,6 +582,17 @@ MUTANTS = {
     "router_bias_dropped": ("acc + (br ? (double)br[e] : 0.0)", "acc"),
     "router_skip_first_n": ("for (int64_t n = 0; n < N; ++n)\n                acc +=",
                             "for (int64_t n = 1; n < N; ++n)\n                acc +="),
+    "bwd_relu_grad": ("return x > 0.0 ? 1.0 : 0.0;", "return x > 0.0 ? 1.0 : 0.5;"),
+    "bwd_gelu_grad_term": (" + 0.5 * x * (1.0 - t * t) * c * (1.0 + 3.0 * 0.044715 * x * x);", ";"),
+    "bwd_dx_w1_cols_reversed": ("acc += da[o] * load(dtype, W1, n * O + o);",
+                                "acc += da[o] * load(dtype, W1, n * O + (O - 1 - o));"),
+    "bwd_db1_skips_first_row": ("for (int64_t m = 0; m < M; ++m) acc += da[m];",
+                                "for (int64_t m = 1; m < M; ++m) acc += da[m];"),
+    "bwd_dw2_uses_preactivation": ("h[m] = oracle_act(act1, a);", "h[m] = a;"),
+    "bwd_dx_no_act_grad": ("da[o] = bwd_dh(dtype, W2, dY, m, o, P) *\n                                oracle_act_grad(act1, bwd_a(dtype, X, W1, b1, m, o, N, O));",
+                           "da[o] = bwd_dh(dtype, W2, dY, m, o, P);"),
+    "bwd_dh_w2_cols_reversed": ("acc += load(dtype, dY, m * P + p) * load(dtype, W2, o * P + p);",
+                                "acc += load(dtype, dY, m * P + p) * load(dtype, W2, o * P + (P - 1 - p));"),
     "swiglu_skip_first_n": ("x = load(dtype, X, m * N + n);\n        for (int64_t o = 0; o < O; ++o) {\n            g[o]",
                             "x = n ? load(dtype, X, m * N + n) : 0.0;\n        for (int64_t o = 0; o < O; ++o) {\n            g[o]"),
 }
@@ -566,8 +667,18 @@ def _pin_suite(lib):
         got = oracle.router_logits(X, Wr, br, lib=lib)
         assert all(got[t, e] == float(exact[t][e]) for t in range(3) for e in range(4))
 
+    def backward():
+        for act in (RELU, GELU):
+            rng = np.random.default_rng(17 + act)
+            X, W1, b1, W2, b2, dY = _bwd_inputs(rng, 2, 3, 4, 3)
+            fd = _fd_grads(X, W1, b1, W2, b2, dY, act, lib=lib)
+            got = oracle.ffn_backward(X, W1, b1, W2, dY, act1=act, lib=lib)
+            for g, f in zip(got, fd):
+                assert np.allclose(g, f, rtol=0, atol=2e-5 * (1 + np.abs(f).max()))
+
     for name, fn in [("brute", brute), ("act2", act2), ("gelu", gelu), ("routing", routing),
-                     ("moe_combine", moe_combine), ("swiglu", swiglu), ("router", router)]:
+                     ("moe_combine", moe_combine), ("swiglu", swiglu), ("router", router),
+                     ("backward", backward)]:
         check(name, fn)
     return failures
 
