@@ -7,7 +7,8 @@
 A step is one call of the whole path on one batch of synthetic input that is
 already resident in HBM: for the dense workloads the fused FFN kernel and the
 ordered split reduction (or the two skinny layers at M <= 16); for the MoE
-workload routing, the grouped fused FFN and the combine; for the SwiGLU
+workload routing, the grouped fused FFN and the combine; for the backward
+workload the six steps of the gradients at the prefill shape; for the SwiGLU
 workloads the gated fused FFN and the reduction (two gated skinny layers at
 M <= 16).  W untimed warm-up
 steps, then K timed steps bracketed by a device synchronisation on both sides
@@ -336,6 +337,61 @@ def run_moe(cfg, steps, warmup, hip, torch, ffn, synth, workload):
                 bytes=set_bytes, rotate=R)
 
 
+def run_backward(cfg, steps, warmup, hip, torch, ffn, synth, workload):
+    """The FFN backward at a dense shape (act2 none): region 1 plain calls, region 2
+    the same calls with events between the six steps."""
+    X, W1, b1, W2, _ = synth.dense_inputs(cfg.M, cfg.N, cfg.O, cfg.P, seed=0)
+    dY = synth.f32_to_bf16_bits(np.random.default_rng(1).standard_normal((cfg.M, cfg.P)).astype(np.float32))
+    set_bytes = 2 * (cfg.M * cfg.N + cfg.N * cfg.O + cfg.O + cfg.O * cfg.P + cfg.M * cfg.P)
+    R = max(1, min(16, math.ceil(MALL_DEFEAT_BYTES / set_bytes)))
+    base = [to_dev(a, torch) for a in (X, W1, b1, W2, dY)]
+    sets = [[t.clone() for t in base] for _ in range(R)]
+    del base
+    f32 = lambda *shape: torch.empty(shape, dtype=torch.float32, device="cuda")  # noqa: E731
+    dX = torch.empty((cfg.M, cfg.N), dtype=torch.bfloat16, device="cuda")
+    dW1, db1, dW2, db2 = f32(cfg.N, cfg.O), f32(cfg.O), f32(cfg.O, cfg.P), f32(cfg.P)
+    ws = ffn.workspace(ffn.ffn_backward_workspace_size(cfg.M, cfg.N, cfg.O, cfg.P))
+    L = ffn.lib()
+    stream = torch.cuda.current_stream().cuda_stream
+    act = ffn.ACTS[cfg.act1]
+    nev = 7
+    evs = [hip.event(device_only=True) for _ in range(nev * steps)]
+    arr_t = ctypes.c_void_p * nev
+    p = lambda t: t.data_ptr()  # noqa: E731
+
+    def call(i, ev=None):
+        x, w1, c1, w2, dy = sets[i % R]
+        a = (p(x), p(w1), p(c1), p(w2), p(dy), p(dX), p(dW1), p(db1), p(dW2), p(db2), cfg.M, cfg.N,
+             cfg.O, cfg.P, ffn.BF16, act, p(ws), ws.numel(), stream)
+        rc = L.ffn_backward(*a) if ev is None else L.ffn_backward_traced(*a, ev, nev)
+        if rc != 0:
+            raise RuntimeError(ffn.ffn_last_error())
+
+    for i in range(warmup):
+        call(i)
+    torch.cuda.synchronize()
+    t0, t1 = hip.event(), hip.event()
+    hip.record(t0, stream)
+    for s_ in range(steps):
+        call(s_)
+    hip.record(t1, stream)
+    torch.cuda.synchronize()
+    total_ms = hip.ms(t0, t1)
+    ev_arrays = [arr_t(*evs[nev * s_: nev * (s_ + 1)]) for s_ in range(steps)]
+    for s_ in range(steps):
+        call(steps + s_, ev_arrays[s_])
+    torch.cuda.synchronize()
+    names = ["h_and_grad", "da", "dX", "dW1", "dW2", "bias_sums"]
+    per = {n: float(np.mean([hip.ms(evs[nev * s_ + j], evs[nev * s_ + j + 1]) for s_ in range(steps)]))
+           for j, n in enumerate(names)}
+    hip.destroy(evs + [t0, t1])
+    gemm = 2 * cfg.M * cfg.N * cfg.O   # each of the five products: 2 M N O = 2 M O P here
+    flops_alg = 2 * cfg.M * (2 * cfg.N * cfg.O + 2 * cfg.O * cfg.P)   # dh, dX, dW1, dW2
+    flops_exec = flops_alg + gemm                                        # + the recomputed a
+    return dict(ms_per_step=total_ms / steps, steps_ms=per, flops=flops_alg, flops_exec=flops_exec,
+                bytes=set_bytes, rotate=R)
+
+
 # ---------------------------------------------------------------- box ceilings
 
 def box_ceilings(hip, torch, ffn, reps=10):
@@ -398,7 +454,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="prefill",
                     choices=["prefill", "decode", "large", "moe", "tiny", "swiglu", "swiglu_decode",
-                             "moe_shard"])
+                             "moe_shard", "backward"])
     ap.add_argument("--all", action="store_true", help="also time the large and MoE workloads")
     ap.add_argument("--cpu-rows", type=int, default=2048, help="oracle sample rows (0: skip)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -423,12 +479,27 @@ def main():
     hip = Hip()
     cfgs = {"prefill": workload.PREFILL, "decode": workload.DECODE, "large": workload.LARGE,
             "tiny": workload.TINY_F32, "moe": workload.MOE, "swiglu": workload.SWIGLU_PREFILL,
-            "swiglu_decode": workload.SWIGLU_DECODE, "moe_shard": workload.MOE_SHARD}
+            "swiglu_decode": workload.SWIGLU_DECODE, "moe_shard": workload.MOE_SHARD,
+            "backward": workload.PREFILL}
     head = cfgs[args.workload]
     log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {head.name}")
 
     secondary = {}
-    if args.workload in ("moe", "moe_shard"):
+    if args.workload == "backward":
+        r = run_backward(head, args.steps, args.warmup, hip, torch, ffn, synth, workload)
+        r["traced_ms_per_step"] = sum(r["steps_ms"].values())
+        value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
+        unit = "TFLOP/s"
+        dom = max(r["steps_ms"], key=r["steps_ms"].get)
+        gemm_flops = 2 * head.M * head.N * head.O
+        ach = gemm_flops / (r["steps_ms"][dom] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "kernel": f"backward GEMM ({dom})", "achieved": ach,
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
+                "traffic": None, "kernel_us": 1e3 * r["steps_ms"][dom],
+                "steps_us": {k: 1e3 * v for k, v in r["steps_ms"].items()},
+                "executed_TFLOP_per_s": r["flops_exec"] / (r["ms_per_step"] * 1e-3) / 1e12}
+        dense = None
+    elif args.workload in ("moe", "moe_shard"):
         r = run_moe(head, args.steps, args.warmup, hip, torch, ffn, synth, workload)
         value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
         kern_tflops = r["flops"] / (r["k1_ms"] * 1e-3) / 1e12
@@ -494,6 +565,11 @@ def main():
                                      "kernel1_us": 1e3 * m["k1_ms"], "kernel2_us": 1e3 * m["k2_ms"]}
 
     if args.all:
+        b = run_backward(workload.PREFILL, args.steps, args.warmup, hip, torch, ffn, synth, workload)
+        secondary["backward_" + workload.PREFILL.name] = {
+            "TFLOP_per_s": b["flops"] / (b["ms_per_step"] * 1e-3) / 1e12,
+            "us_per_call": 1e3 * b["ms_per_step"],
+            "steps_us": {k: round(1e3 * v, 1) for k, v in b["steps_ms"].items()}}
         m = run_moe_router(workload.MOE, args.steps, args.warmup, hip, torch, ffn, synth, workload)
         secondary["moe_router_" + workload.MOE.name] = {
             "TFLOP_per_s": m["flops"] / (m["ms_per_step"] * 1e-3) / 1e12,
@@ -527,7 +603,8 @@ def main():
         "vs_baseline": None,
         "dtype": head.dtype,
         "data": "synthetic (seeded normal inputs, random-init weights of the workload's shape)",
-        "config": {"workload": head.name, **{k: getattr(head, k) for k in ("M", "N", "O", "P")},
+        "config": {"workload": ("backward_" if args.workload == "backward" else "") + head.name,
+                   **{k: getattr(head, k) for k in ("M", "N", "O", "P")},
                    "act1": getattr(head, "act1", "swiglu"), "rotate_input_sets": r["rotate"]},
         "pct_bf16_peak": 100.0 * value / PEAK_BF16_TFLOPS if unit == "TFLOP/s" else None,
         "roofline": roof,

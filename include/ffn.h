@@ -101,6 +101,39 @@ int ffn_forward_traced(const void* X, const void* W1, const void* b1, const void
                        int dtype, int act1, int act2, int variant, void* workspace,
                        size_t workspace_bytes, void* stream, void** events, int n_events);
 
+/* ---------------------------------------------------------------- backward
+ * Gradients of the dense FFN for act2 = NONE (the kernel-fusion post,
+ * brunomaga.github.io, names a fused backward pass as its next step: the
+ * forward keeps no H, so the backward recomputes it).  With a = X W1 + b1,
+ * h = act1(a), Y = h W2 + b2 and the output gradient dY (M x P):
+ *
+ *   dX = (dY W2^T * act1'(a)) W1^T           M x N, bf16
+ *   dW1 = X^T (dY W2^T * act1'(a))           N x O, fp32
+ *   db1 = column sums of dY W2^T * act1'(a)  O, fp32 (may be NULL)
+ *   dW2 = h^T dY                             O x P, fp32
+ *   db2 = column sums of dY                  P, fp32 (may be NULL)
+ *
+ * act1'(x): ReLU' = 1 for x > 0 else 0; GELU-tanh' the derivative of the
+ * tanh form; NONE: 1.  bf16 inputs (X, W1, b1 or NULL, W2, dY) only; the
+ * intermediates h, act1'(a) and dY W2^T * act1'(a) are rounded to bf16 once
+ * (they live in the workspace); sums accumulate in fp32 in a fixed order (no
+ * atomics: repeated calls are bitwise identical).  M*N, M*O and M*P must be
+ * below 2^30.  With M == 0 the weight and bias gradients are zero-filled. */
+size_t ffn_backward_workspace_size(int64_t M, int64_t N, int64_t O, int64_t P, int dtype);
+
+int ffn_backward(const void* X, const void* W1, const void* b1, const void* W2, const void* dY,
+                 void* dX, float* dW1, float* db1, float* dW2, float* db2, int64_t M, int64_t N,
+                 int64_t O, int64_t P, int dtype, int act1, void* workspace,
+                 size_t workspace_bytes, void* stream);
+
+/* As ffn_backward, recording events[0..6] on `stream` around its six steps
+ * (h and act1'(a); da; dX; dW1; dW2; the bias sums).  n_events >= 7. */
+int ffn_backward_traced(const void* X, const void* W1, const void* b1, const void* W2,
+                        const void* dY, void* dX, float* dW1, float* db1, float* dW2, float* db2,
+                        int64_t M, int64_t N, int64_t O, int64_t P, int dtype, int act1,
+                        void* workspace, size_t workspace_bytes, void* stream, void** events,
+                        int n_events);
+
 /* ---------------------------------------------------------------- SwiGLU
  * The gated FFN the benchmarked models use (the kernel-fusion post,
  * brunomaga.github.io, section "Benchmarks": a third weight matrix whose

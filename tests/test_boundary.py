@@ -184,6 +184,28 @@ def test_router_rejects():
     assert rc == E_WS
 
 
+def test_backward_rejects_on_host():
+    L = ffn.lib()
+    args = lambda **kw: dict(dict(X=FAKE, W1=FAKE, b1=None, W2=FAKE, dY=FAKE, dX=FAKE2, dW1=FAKE2,  # noqa: E731
+                                  db1=None, dW2=FAKE2, db2=None, M=64, N=64, O=64, P=64,
+                                  dt=ffn.BF16, act=2, ws=FAKE, wsb=0), **kw)
+    def call(**kw):
+        a = args(**kw)
+        return L.ffn_backward(a["X"], a["W1"], a["b1"], a["W2"], a["dY"], a["dX"], a["dW1"],
+                              a["db1"], a["dW2"], a["db2"], a["M"], a["N"], a["O"], a["P"],
+                              a["dt"], a["act"], a["ws"], a["wsb"], None)
+    assert call(dt=ffn.F32) == E_UNSUP
+    assert call(act=9) == E_INVAL
+    assert call(dW1=None) == E_INVAL
+    assert call(O=12) == E_UNSUP
+    assert call(dY=FAKE + 4) == E_ALIGN
+    assert call(M=1 << 20, N=1 << 12) == E_UNSUP
+    assert call() == E_WS
+    need = ffn.ffn_backward_workspace_size(4096, 4096, 1792, 4096)
+    assert need >= 3 * 4096 * 1792 * 2
+    assert call(M=4096, N=4096, O=1792, P=4096, wsb=need - 1) == E_WS
+
+
 def test_route_rejects():
     L = ffn.lib()
     assert L.moe_route(None, 8, 8, 2, None, None, None, None, FAKE, 1 << 20, None) == E_INVAL

@@ -11,7 +11,7 @@ from fp64 logits.  The checks are therefore:
   * every token whose fp64 top-k margin exceeds twice that bound gets the same
     experts as the oracle's routing of the fp64 logits;
   * Y matches the oracle's MoE layer on the GPU's logits within the bf16 rule
-    with the output's own bf16 rounding allowed for (compare_with_output_rounding:
+    with the output's own bf16 rounding allowed for (compare_with_bf16_rounding:
     at 4096 tokens the rounding of the exact result alone reaches 1.5e-2 rms).
 """
 from __future__ import annotations
@@ -23,7 +23,7 @@ import oracle
 import transformer_ffn_fusion_amd as ffn
 from transformer_ffn_fusion_amd import synth
 
-from gpu_util import BF16_TOL, compare_with_output_rounding, dev_bf16, dev_f32, host_f64, log
+from gpu_util import BF16_TOL, compare_with_bf16_rounding, dev_bf16, dev_f32, host_f64, log
 
 pytestmark = pytest.mark.gpu
 
@@ -103,4 +103,4 @@ def test_moe_with_router(M, E, k, N, O, P):
     rows = np.arange(M) if M <= 512 else synth.check_rows(M)
     ref = oracle.moe_ffn(X, lg_h, W1, b1, W2, b2, k=k, rows=rows)
     got = host_f64(Y[torch.as_tensor(rows, device="cuda")])
-    compare_with_output_rounding(got, ref, BF16_TOL, "moe with router")
+    compare_with_bf16_rounding(got, ref, BF16_TOL, "moe with router")

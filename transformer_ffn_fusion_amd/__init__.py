@@ -81,6 +81,14 @@ def lib():
         L.moe_ffn_forward_router.argtypes = [vp, vp, vp, i64, i64, i32, vp, vp, vp, vp, vp, i64, i64,
                                              i64, i32, i32, i32, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_ffn_forward_router.restype = i32
+        L.ffn_backward_workspace_size.argtypes = [i64, i64, i64, i64, i32]
+        L.ffn_backward_workspace_size.restype = sz
+        L.ffn_backward.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32,
+                                   i32, vp, sz, vp]
+        L.ffn_backward.restype = i32
+        L.ffn_backward_traced.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, i64, i64, i64, i64,
+                                          i32, i32, vp, sz, vp, ctypes.POINTER(vp), i32]
+        L.ffn_backward_traced.restype = i32
         L.ffn_last_error.argtypes = []
         L.ffn_last_error.restype = ctypes.c_char_p
         L.ffn_version.restype = i32
@@ -162,6 +170,24 @@ def ffn_forward_ex(X, W1, b1, W2, b2, Y, act1="gelu_tanh", act2="none", variant=
 
 def ffn_forward(X, W1, b1, W2, b2, Y, act1="gelu_tanh", act2="none", ws=None, stream=None):
     return ffn_forward_ex(X, W1, b1, W2, b2, Y, act1, act2, VARIANT_AUTO, ws, stream)
+
+
+def ffn_backward_workspace_size(M, N, O, P, dtype=BF16) -> int:
+    return lib().ffn_backward_workspace_size(M, N, O, P, dtype)
+
+
+def ffn_backward(X, W1, b1, W2, dY, dX, dW1, db1, dW2, db2, act1="gelu_tanh", ws=None, stream=None):
+    """Gradients of the FFN (act2 none) for the output gradient ``dY``; writes dX (bf16),
+    dW1, db1, dW2, db2 (fp32; db1/db2 may be None) in place."""
+    M, N = X.shape
+    O = W1.shape[1]
+    P = W2.shape[1]
+    dt = _dtype_code(X)
+    if ws is None:
+        ws = workspace(ffn_backward_workspace_size(M, N, O, P, dt), X.device)
+    _check(lib().ffn_backward(_ptr(X), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(dY), _ptr(dX), _ptr(dW1),
+                              _ptr(db1), _ptr(dW2), _ptr(db2), M, N, O, P, dt, _act(act1),
+                              _ptr(ws), ws.numel(), _stream(stream)))
 
 
 def ffn_swiglu_workspace_size(M, N, O, P, dtype=BF16, variant=VARIANT_AUTO) -> int:

@@ -125,6 +125,21 @@ SwigluLayout swiglu_layout(int64_t M, int64_t N, int64_t O, int64_t P, int varia
     return L;
 }
 
+// ---- backward workspace layout
+struct BackwardLayout {
+    size_t H = 0, G = 0, dA = 0, total = 0;
+};
+
+BackwardLayout backward_layout(int64_t M, int64_t O, int64_t) {
+    BackwardLayout L;
+    size_t off = 0;
+    L.H = off;     off += align_up(sizeof(uint16_t) * M * O);
+    L.G = off;     off += align_up(sizeof(uint16_t) * M * O);
+    L.dA = off;    off += align_up(sizeof(uint16_t) * M * O);
+    L.total = off ? off : kAlign;
+    return L;
+}
+
 // ---- MoE workspace layout
 struct MoeLayout {
     size_t ids, w, counts, offsets, sorted, pos, tiles, tile_count, blk_counts, blk_base, part,
@@ -299,6 +314,91 @@ int ffn_forward(const void* X, const void* W1, const void* b1, const void* W2, c
                 int act2, void* workspace, size_t workspace_bytes, void* stream) {
     return ffn_forward_ex(X, W1, b1, W2, b2, Y, M, N, O, P, dtype, act1, act2,
                           FFN_VARIANT_AUTO, workspace, workspace_bytes, stream);
+}
+
+// ---------------------------------------------------------------- backward
+
+size_t ffn_backward_workspace_size(int64_t M, int64_t N, int64_t O, int64_t P, int dtype) {
+    if (check_dims(M, N, O, P) != FFN_OK || dtype != FFN_BF16) return 0;
+    return backward_layout(M, O, P).total;
+}
+
+static int backward(const void* X, const void* W1, const void* b1, const void* W2,
+                    const void* dY, void* dX, float* dW1, float* db1, float* dW2, float* db2,
+                    int64_t M, int64_t N, int64_t O, int64_t P, int dtype, int act1,
+                    void* workspace, size_t workspace_bytes, void* stream, void** events,
+                    int n_events) {
+    if (events && n_events < 7) return fail(FFN_EINVAL, "traced backward calls take at least 7 events");
+    int rc = check_dims(M, N, O, P);
+    if (rc) return rc;
+    if (dtype != FFN_F32 && dtype != FFN_BF16) return fail(FFN_EINVAL, "unknown dtype %d", dtype);
+    if (dtype != FFN_BF16) return fail(FFN_EUNSUPPORTED, "the backward takes bf16 only");
+    if (!valid_act(act1)) return fail(FFN_EINVAL, "unknown activation %d", act1);
+    if (!W1 || !W2 || !dW1 || !dW2 || (M > 0 && (!X || !dY || !dX)))
+        return fail(FFN_EINVAL, "X, W1, W2, dY, dX, dW1 and dW2 must not be NULL");
+    if (!workspace) return fail(FFN_EINVAL, "workspace must not be NULL");
+    const void* ps[] = {X, W1, b1, W2, dY, dX, dW1, db1, dW2, db2};
+    const char* nm[] = {"X", "W1", "b1", "W2", "dY", "dX", "dW1", "db1", "dW2", "db2"};
+    for (int i = 0; i < 10; ++i)
+        if (ps[i] && !aligned16(ps[i])) return fail(FFN_EALIGN, "%s is not 16-byte aligned", nm[i]);
+    if ((reinterpret_cast<uintptr_t>(workspace) & (kAlign - 1)) != 0)
+        return fail(FFN_EALIGN, "workspace is not 256-byte aligned");
+    if (M * N >= ((int64_t)1 << 30) || M * O >= ((int64_t)1 << 30) || M * P >= ((int64_t)1 << 30))
+        return fail(FFN_EUNSUPPORTED, "the backward addresses M x N, M x O and M x P with 32-bit "
+                    "offsets: each must be below 2^30");
+    const BackwardLayout L = backward_layout(M, O, P);
+    if (workspace_bytes < L.total)
+        return fail(FFN_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
+    hipStream_t st = reinterpret_cast<hipStream_t>(stream);
+    if (M == 0) {
+        // no rows: every gradient is zero (a fill kernel: no memset nodes in a captured graph)
+        const int64_t zn[4] = {N * O, O, O * P, P};
+        float* zp[4] = {dW1, db1, dW2, db2};
+        for (int i = 0; i < 4; ++i)
+            if ((rc = launched(ffn::launch_zero_f32(zp[i], zn[i], st), "zero fill"))) return rc;
+        return ok();
+    }
+    char* ws = static_cast<char*>(workspace);
+    ffn::BackwardIO io;
+    io.X = static_cast<const uint16_t*>(X);
+    io.W1 = static_cast<const uint16_t*>(W1);
+    io.b1 = static_cast<const uint16_t*>(b1);
+    io.W2 = static_cast<const uint16_t*>(W2);
+    io.dY = static_cast<const uint16_t*>(dY);
+    io.dX = static_cast<uint16_t*>(dX);
+    io.dW1 = dW1;
+    io.db1 = db1;
+    io.dW2 = dW2;
+    io.db2 = db2;
+    io.H = reinterpret_cast<uint16_t*>(ws + L.H);
+    io.Gr = reinterpret_cast<uint16_t*>(ws + L.G);
+    io.dA = reinterpret_cast<uint16_t*>(ws + L.dA);
+    io.M = M;
+    io.N = N;
+    io.O = O;
+    io.P = P;
+    io.act1 = act1;
+    rc = launched(ffn::launch_ffn_backward(io, st, events, n_events), "backward kernels");
+    if (rc) return rc;
+    return ok();
+}
+
+int ffn_backward(const void* X, const void* W1, const void* b1, const void* W2, const void* dY,
+                 void* dX, float* dW1, float* db1, float* dW2, float* db2, int64_t M, int64_t N,
+                 int64_t O, int64_t P, int dtype, int act1, void* workspace,
+                 size_t workspace_bytes, void* stream) {
+    return backward(X, W1, b1, W2, dY, dX, dW1, db1, dW2, db2, M, N, O, P, dtype, act1, workspace,
+                    workspace_bytes, stream, nullptr, 0);
+}
+
+int ffn_backward_traced(const void* X, const void* W1, const void* b1, const void* W2,
+                        const void* dY, void* dX, float* dW1, float* db1, float* dW2, float* db2,
+                        int64_t M, int64_t N, int64_t O, int64_t P, int dtype, int act1,
+                        void* workspace, size_t workspace_bytes, void* stream, void** events,
+                        int n_events) {
+    if (!events) return fail(FFN_EINVAL, "events must not be NULL");
+    return backward(X, W1, b1, W2, dY, dX, dW1, db1, dW2, db2, M, N, O, P, dtype, act1, workspace,
+                    workspace_bytes, stream, events, n_events);
 }
 
 // ---------------------------------------------------------------- SwiGLU

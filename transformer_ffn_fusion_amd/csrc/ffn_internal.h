@@ -109,6 +109,23 @@ hipError_t launch_moe_combine(const float* part, int splits, int64_t rows_total,
                               const uint16_t* b2, uint16_t* Y, int64_t M, int k, int64_t P,
                               int act2, hipStream_t stream);
 
+// ---- backward (act2 none): recompute h and act1'(a), then five GEMMs and the
+// bias column sums (ffn_backward.hip)
+
+struct BackwardIO {
+    const uint16_t *X = nullptr, *W1 = nullptr, *b1 = nullptr, *W2 = nullptr, *dY = nullptr;
+    uint16_t* dX = nullptr;              // M x N bf16
+    float *dW1 = nullptr, *db1 = nullptr, *dW2 = nullptr, *db2 = nullptr;
+    uint16_t *H = nullptr, *Gr = nullptr, *dA = nullptr;   // workspace, M x O bf16 each
+    int64_t M = 0, N = 0, O = 0, P = 0;
+    int act1 = 0;
+};
+hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);   // a fill kernel, no memset
+// events (may be null): events[s] recorded before step s + 1 (steps: h and g,
+// da, dX, dW1, dW2, bias sums), events[6] after the last; n_events >= 7 to get all
+hipError_t launch_ffn_backward(const BackwardIO& io, hipStream_t stream, void** events,
+                               int n_events);
+
 // ---- measurement support (ceilings.hip): the box's own MFMA and HBM ceilings
 
 int ceiling_sink_floats();
