@@ -59,11 +59,16 @@ TRAFFIC_FILE = os.path.join(HERE, "profiles", "traffic.json")
 COPY_BYTES = 256 << 20   # the plain copy used to calibrate the HBM byte counters
 
 
+# the sources of the kernels whose HBM traffic is recorded (forward fused and grouped,
+# decode layers, routing and combine, and the headers they include)
+TRAFFIC_SOURCES = ("ffn_fused.hip", "ffn_skinny.hip", "moe.hip", "ffn_device.h", "ffn_internal.h")
+
+
 def kernel_source_hash() -> str:
-    """Hash of the HIP sources: traffic counters are valid only for the kernels they measured."""
+    """Hash of the measured kernels' sources: traffic counters are valid only for them."""
     h = hashlib.sha256()
     csrc = os.path.join(HERE, "transformer_ffn_fusion_amd", "csrc")
-    for name in sorted(os.listdir(csrc)):
+    for name in TRAFFIC_SOURCES:
         with open(os.path.join(csrc, name), "rb") as f:
             h.update(name.encode() + b"\0" + f.read())
     return h.hexdigest()[:16]
