@@ -262,13 +262,9 @@ template <bool kAOuter, bool kBOuter, int kEpi>
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     if (a.I <= 0 || a.J <= 0) return hipSuccess;
     auto kern = gemm_bf16_kernel<kAOuter, kBOuter, kEpi>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, kGLds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static bool lds_set[kMaxDevices] = {};
+    hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), kGLds, lds_set);
+    if (e != hipSuccess) return e;
     dim3 grid((unsigned)((a.J + kGT - 1) / kGT), (unsigned)((a.I + kGT - 1) / kGT));
     hipLaunchKernelGGL(kern, grid, dim3(kGThreads), kGLds, stream, a);
     return hipGetLastError();

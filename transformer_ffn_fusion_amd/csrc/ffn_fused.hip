@@ -104,8 +104,21 @@ struct FusedArgs {
     int splits;
     int act1;
     int cus;              // compute units of the device (grouped form: tail splitting)
+    bool part_wt;         // partials written through to the memory-side cache (sc1)
     GroupedRows g;
 };
+
+// Partial stores.  Partials that fit the 256 MB memory-side cache (the MALL)
+// are written through to it at device scope (sc1), so the reduction that
+// follows reads most of them from there; larger ones are streamed past the
+// caches (non-temporal).  Measured on MI355X (kernel + reduction, us): prefill
+// shard, 256 MiB of partials: 166 + 54 streamed, 168 + 44 written through
+// (SwiGLU shard: 230 + 55, 233 + 45; expert-sharded MoE, 128 MiB: kernel 140,
+// 137); large shard, 2 GiB: 1307 + 429 streamed, 1480 + 472 written through;
+// MoE, 512 MiB: 488 streamed, 510 written through.
+constexpr int64_t kMallBytes = 256ll << 20;
+constexpr int kCpolSc1 = 16;   // buffer cache-policy bits: sc1 (device scope)
+typedef unsigned uint32x4_t __attribute__((ext_vector_type(4)));
 
 // Unit -> (row tile, hidden chunk).  Workgroups are dispatched round-robin
 // over the 8 XCDs (unit u runs on XCD u % 8), and each XCD has its own L2.
@@ -419,13 +432,17 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     // same lines at the same moment and queue on the same L2 channels.
     // Workgroup j of the XCD starts instead at K stage j (wrapping) and at W2
     // stage (j, j) of the (pass, k) grid, so at any moment they read different
-    // stages.  The grouped form keeps the plain order: its co-resident
-    // workgroups belong to several experts, and walking each expert's weights
-    // in step keeps the L2 footprint to one sliding window per expert
-    // (measured: 560 -> 530 us on the MoE workload).
-    const int64_t jx = kGrouped ? 0 : (blockIdx.x >> 3);
-    c.rot1 = jx % c.nk;
-    const int64_t rotp = jx % npl;
+    // stages (measured against smaller rotations, j mod 16 .. j mod 2, and
+    // against rotating only the k order inside each pass: all slower).  The
+    // grouped form walks the first product and the passes in plain order: its
+    // co-resident workgroups belong to several experts, and walking each
+    // expert's weights in step keeps the L2 footprint to one sliding window
+    // per expert (560 -> 530 us on the MoE workload); only the k order inside
+    // a pass rotates, so that workgroups of one expert read different slabs
+    // of the same pass (530 -> 487 us).
+    const int64_t jx = blockIdx.x >> 3;
+    c.rot1 = kGrouped ? 0 : jx % c.nk;
+    const int64_t rotp = kGrouped ? 0 : jx % npl;
     const int rotk = (int)(jx % Cfg::kKS);
     char* const hreg = smem + Cfg::kHOff;
 
@@ -508,7 +525,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
             for (int fm = 0; fm < 4; ++fm) acc2[j][fm] = mfma16x16x32(bh[fm], wop[j], acc2[j][fm]);
     };
 
-    float* const part = a.part + (int64_t)s * a.rows_out * P + (row0 + 4 * lg) * P + 64 * wc + 4 * li;
+    float* const part_plane = a.part + (int64_t)s * a.rows_out * P;
+    float* const part = part_plane + (row0 + 4 * lg) * P + 64 * wc + 4 * li;
+    const __amdgpu_buffer_rsrc_t rpart = make_rsrc(part_plane, a.rows_out * P * 4);
     uint2 RA[8], RB[8];
     load2(0, RA);
     load2(1, RB);   // the stage count is even
@@ -523,11 +542,17 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
 #pragma unroll
             for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    if (16 * fm + 4 * lg + r < valid)   // streaming: read once, by the reduction
-                        __builtin_nontemporal_store(
-                            floatx4_t{acc2[0][fm][r], acc2[1][fm][r], acc2[2][fm][r], acc2[3][fm][r]},
-                            reinterpret_cast<floatx4_t*>(part + (int64_t)(16 * fm + r) * P + pt * kBN2));
+                for (int r = 0; r < 4; ++r) {
+                    if (16 * fm + 4 * lg + r >= valid) continue;
+                    const floatx4_t v{acc2[0][fm][r], acc2[1][fm][r], acc2[2][fm][r], acc2[3][fm][r]};
+                    const int64_t o = (int64_t)(16 * fm + r) * P + pt * kBN2;
+                    if (a.part_wt)   // offsets below 2^31 bytes (checked at launch)
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            __builtin_bit_cast(uint32x4_t, v), rpart,
+                            (uint32_t)((part - part_plane + o) * 4), 0, kCpolSc1);
+                    else   // streaming: read once, by the reduction
+                        __builtin_nontemporal_store(v, reinterpret_cast<floatx4_t*>(part + o));
+                }
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -593,17 +618,16 @@ template <int CA, int CB, bool G, bool kGated>
 hipError_t launch_fused_impl(const FusedArgs& a, int64_t units, hipStream_t stream) {
     using Cfg = FusedCfg<CA, CB, kGated>;
     auto kern = fused_ffn_bf16_kernel<CA, CB, G, kGated>;
-    static bool attr_set = false;
-    if (!attr_set) {
-        hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                           hipFuncAttributeMaxDynamicSharedMemorySize, Cfg::kLds);
-        if (e != hipSuccess) return e;
-        attr_set = true;
-    }
+    static bool lds_set[kMaxDevices] = {};
+    hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), Cfg::kLds, lds_set);
+    if (e != hipSuccess) return e;
     // grouped form: workgroups for the pieces of a short last round (at most
     // cus, plus up to 7 x 8 for the XCD-aligned numbering of the pieces)
     const int64_t grid = units + (G ? a.cus + 64 : 0);
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), Cfg::kLds, stream, a);
+    const int64_t part_bytes = (int64_t)a.splits * a.rows_out * a.P * 4;
+    FusedArgs b = a;
+    b.part_wt = part_bytes <= kMallBytes && a.rows_out * a.P * 4 < (1ll << 31);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), Cfg::kLds, stream, b);
     return hipGetLastError();
 }
 

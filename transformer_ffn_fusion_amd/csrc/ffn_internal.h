@@ -9,6 +9,20 @@
 
 namespace ffn {
 
+// Raises a kernel's dynamic LDS limit on the current device, once per device
+// (the attribute belongs to the device the call is made on).  `done` is the
+// caller's per-kernel record.
+constexpr int kMaxDevices = 64;
+inline hipError_t set_dynamic_lds(const void* kern, int bytes, bool (&done)[kMaxDevices]) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev >= 0 && dev < kMaxDevices && done[dev]) return hipSuccess;
+    e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+    if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) done[dev] = true;
+    return e;
+}
+
 // ---- fused bf16 FFN with H kept in LDS (prefill shapes and the MoE groups)
 
 constexpr int kBM = 64;     // token rows per workgroup tile
