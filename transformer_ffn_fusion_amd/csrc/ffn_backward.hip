@@ -19,9 +19,11 @@
 // fragments (the X-slab layout of the forward kernel); a k-strided one row by
 // row in 8 x 64 blocks and read back k-contiguous through the transposing LDS
 // read -- the layouts, and the checks of them, are the forward kernel's.
-// Output tile 128 x 128, four waves of 64 x 64, a 4-stage LDS ring filled by
-// direct global->LDS loads; every output element is one workgroup's sum over
-// the whole K in a fixed order: no atomics, bitwise reproducible.
+// Output tiles of 256 x 256 (eight waves of 128 x 64) when they fill the chip,
+// else 128 x 128 (four waves of 64 x 64, two workgroups per CU); a 4-stage LDS
+// ring filled by direct global->LDS loads.  Every output element is one
+// workgroup's sum over the whole K in a fixed order: no atomics, bitwise
+// reproducible for a given shape and device.
 #include "ffn_device.h"
 #include "ffn_internal.h"
 
@@ -30,13 +32,29 @@ namespace ffn {
 namespace {
 
 constexpr int kGK = 32;                   // k-stage depth (one MFMA k-step)
-constexpr int kGT = 128;                 // output tile edge
-constexpr int kGThreads = 256;           // 4 waves, 2 x 2 tiles of 64 x 64
-constexpr int kGNS = 4;                  // LDS ring stages
-constexpr int kGOp = kGT * kGK * 2;      // one operand's stage: 8 KiB
-constexpr int kGStage = 2 * kGOp;
-constexpr int kGLds = kGNS * kGStage;    // 64 KiB
-constexpr int kGLoads = 4;               // direct loads per wave per stage (2 per operand)
+
+// Output tile TI x TJ, WI x WJ waves of (TI/WI) x (TJ/WJ) each.  A stage holds
+// TI and TJ operand indices x 32 k (TI/16 + TJ/16 units of 1 KiB, spread over
+// the waves).  Bigger tiles and bigger wave tiles cut the L2 -> LDS bytes and
+// the LDS -> register bytes per MFMA.
+template <int TI_, int TJ_, int WI_, int WJ_, int NS_ = 4>
+struct GemmCfg {
+    static constexpr int TI = TI_, TJ = TJ_, WI = WI_, WJ = WJ_;
+    static constexpr int kGNS = NS_;                            // LDS ring stages
+    static constexpr int kWaves = WI * WJ;
+    static constexpr int kThreads = 64 * kWaves;
+    static constexpr int FI = TI / WI / 16, FJ = TJ / WJ / 16;   // fragments per wave
+    static constexpr int kOpA = TI * kGK * 2;
+    static constexpr int kStage = kOpA + TJ * kGK * 2;
+    static constexpr int kLds = kGNS * kStage;
+    static_assert(kGNS >= 3, "the ring keeps one stage being read and one landing");
+    static constexpr int kUnits = TI / 16 + TJ / 16;
+    static constexpr int kLoads = kUnits / kWaves;              // direct loads per wave per stage
+    static_assert(TI % 64 == 0 && TJ % 64 == 0, "k-strided operands stage 64-index blocks");
+    static_assert(FI * 16 * WI == TI && FJ * 16 * WJ == TJ, "whole fragments per wave");
+    static_assert(kUnits % kWaves == 0, "every wave issues the same loads");
+    static_assert(kLds <= 160 * 1024, "LDS budget");
+};
 
 enum { EPI_F32 = 0, EPI_BF16 = 1, EPI_HG = 2, EPI_MULG = 3 };
 
@@ -67,12 +85,13 @@ __device__ __forceinline__ float act_grad(int act, float x) {
 }
 
 // One operand's loads of the k-stage starting at k0 into LDS at `dst`: unit q
-// (0..7) of the 8 per operand.  k-contiguous: unit q = fragment q (indices
-// 16q..16q+15 x 32 k; lane l brings index 16q + l/4, k-group (l&3)^((l>>3)&3),
-// which lands in slot l of the fragment).  k-strided: unit q = block (r, c) =
-// (q / 2, q % 2) of 8 k-rows x 64 indices (lane l brings slot l, see
+// (0 .. T/16-1) of an operand with T indices per tile.  k-contiguous: unit q =
+// fragment q (indices 16q..16q+15 x 32 k; lane l brings index 16q + l/4,
+// k-group (l&3)^((l>>3)&3), which lands in slot l of the fragment).
+// k-strided: unit q = block (r, c) = (q / nb, q % nb) of 8 k-rows x 64
+// indices, nb = T/64 blocks per row group (lane l brings slot l, see
 // wtile_dma_off); rows at or past K read zeros.
-template <bool kOuter>
+template <bool kOuter, int T>
 __device__ __forceinline__ void gemm_issue(const int32x4_t& rs, int64_t ld, int64_t n_idx,
                                            int64_t K, int64_t i0, int64_t k0, int q, int lane,
                                            char* dst) {
@@ -83,7 +102,8 @@ __device__ __forceinline__ void gemm_issue(const int32x4_t& rs, int64_t ld, int6
         if (i < n_idx && k < K) off = (uint32_t)((i * ld + k) * 2);
         dma16(rs, off, dst + q * kFrag);
     } else {
-        const int r = q >> 1, c = q & 1;
+        constexpr int nb = T / 64;
+        const int r = q / nb, c = q % nb;
         const int64_t k = k0 + 8 * r + (lane >> 3);
         if (k < K)
             off = (uint32_t)(((k0 + 8 * r) * ld + i0 + 64 * c) * 2) + wtile_dma_off(lane, (uint32_t)(ld * 2));
@@ -92,81 +112,88 @@ __device__ __forceinline__ void gemm_issue(const int32x4_t& rs, int64_t ld, int6
 }
 
 // Operand fragment f (indices 16f..16f+15) of a stage, for this lane.
-template <bool kOuter>
+template <bool kOuter, int T>
 __device__ __forceinline__ uint4 gemm_frag(const char* st, int f, int lane) {
     if constexpr (!kOuter) {
         return ld16(st + f * kFrag + 16 * xfrag_slot(lane & 15, lane >> 4));
     } else {
-        const char* p = st + wtile_tr_base(lane, 2, f & 3) + 1024 * (f >> 2);
+        const char* p = st + wtile_tr_base(lane, T / 64, f & 3) + 1024 * (f >> 2);
         const uint2 lo = lds_read_tr16(p);
         const uint2 hi = lds_read_tr16(p + 512);
         return make_uint4(lo.x, lo.y, hi.x, hi.y);
     }
 }
 
-template <bool kAOuter, bool kBOuter, int kEpi>
-__global__ __launch_bounds__(kGThreads) void gemm_bf16_kernel(GemmArgs a) {
+template <class Cfg, bool kAOuter, bool kBOuter, int kEpi>
+__global__ __launch_bounds__(Cfg::kThreads) void gemm_bf16_kernel(GemmArgs a) {
+    constexpr int FI = Cfg::FI, FJ = Cfg::FJ;
     extern __shared__ __attribute__((aligned(16))) char smem[];
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wi = wave >> 1, wj = wave & 1;
+    const int wi = wave / Cfg::WJ, wj = wave % Cfg::WJ;
     const int li = lane & 15, lg = lane >> 4;
-    const int64_t i0 = (int64_t)blockIdx.y * kGT;
-    const int64_t j0 = (int64_t)blockIdx.x * kGT;
+    const int64_t i0 = (int64_t)blockIdx.y * Cfg::TI;
+    const int64_t j0 = (int64_t)blockIdx.x * Cfg::TJ;
     const int64_t K = a.K;
     const int64_t nk = (K + kGK - 1) / kGK;
     // the resources span whole operands (every offset below 2^31 bytes)
     const int32x4_t ra = make_srd(a.A, (kAOuter ? K * a.lda : a.I * a.lda) * 2);
     const int32x4_t rb = make_srd(a.B, (kBOuter ? K * a.ldb : a.J * a.ldb) * 2);
 
-    // wave w loads units w and w + 4 of each operand
+    // wave w issues units w, w + W, ... of the stage (A's units first, then B's)
     auto issue = [&](int64_t kt, int buf) {
-        char* st = smem + buf * kGStage;
+        char* st = smem + buf * Cfg::kStage;
         const int64_t k0 = kt * kGK;
 #pragma unroll
-        for (int u = 0; u < 2; ++u) {
-            gemm_issue<kAOuter>(ra, a.lda, a.I, K, i0, k0, wave + 4 * u, lane, st);
-            gemm_issue<kBOuter>(rb, a.ldb, a.J, K, j0, k0, wave + 4 * u, lane, st + kGOp);
+        for (int u = 0; u < Cfg::kLoads; ++u) {
+            const int q = wave + Cfg::kWaves * u;
+            if (q < Cfg::TI / 16)
+                gemm_issue<kAOuter, Cfg::TI>(ra, a.lda, a.I, K, i0, k0, q, lane, st);
+            else
+                gemm_issue<kBOuter, Cfg::TJ>(rb, a.ldb, a.J, K, j0, k0, q - Cfg::TI / 16, lane,
+                                             st + Cfg::kOpA);
         }
     };
 
-    floatx4_t acc[4][4];   // [i fragment][j fragment]
+    floatx4_t acc[FI][FJ];   // [i fragment][j fragment]
 #pragma unroll
-    for (int x = 0; x < 4; ++x)
+    for (int x = 0; x < FI; ++x)
 #pragma unroll
-        for (int y = 0; y < 4; ++y) acc[x][y] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        for (int y = 0; y < FJ; ++y) acc[x][y] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
+    constexpr int kGNS = Cfg::kGNS;
 #pragma unroll
     for (int s = 0; s < kGNS - 1; ++s)
         if (s < nk) issue(s, s);
     for (int64_t kt = 0; kt < nk; ++kt) {
         // stages kt .. min(kt + NS - 2, nk - 1) are in flight; stage kt must land
-        if (kt + kGNS - 2 < nk) wait_vmcnt<kGLoads * (kGNS - 2)>();
+        if (kt + kGNS - 2 < nk) wait_vmcnt<Cfg::kLoads * (kGNS - 2)>();
         else wait_vmcnt<0>();
         __syncthreads();   // stage kt is complete everywhere; stage kt - 1 is read
         if (kt + kGNS - 1 < nk) issue(kt + kGNS - 1, (int)((kt + kGNS - 1) % kGNS));
-        const char* st = smem + (kt % kGNS) * kGStage;
-        uint4 fa[4], fb[4];
+        const char* st = smem + (kt % kGNS) * Cfg::kStage;
+        uint4 fa[FI], fb[FJ];
 #pragma unroll
-        for (int x = 0; x < 4; ++x) fa[x] = gemm_frag<kAOuter>(st, 4 * wi + x, lane);
+        for (int x = 0; x < FI; ++x) fa[x] = gemm_frag<kAOuter, Cfg::TI>(st, FI * wi + x, lane);
 #pragma unroll
-        for (int y = 0; y < 4; ++y) fb[y] = gemm_frag<kBOuter>(st + kGOp, 4 * wj + y, lane);
+        for (int y = 0; y < FJ; ++y)
+            fb[y] = gemm_frag<kBOuter, Cfg::TJ>(st + Cfg::kOpA, FJ * wj + y, lane);
         // B first: the lane then holds four consecutive output columns of a row
 #pragma unroll
-        for (int x = 0; x < 4; ++x)
+        for (int x = 0; x < FI; ++x)
 #pragma unroll
-            for (int y = 0; y < 4; ++y) acc[x][y] = mfma16x16x32(fb[y], fa[x], acc[x][y]);
+            for (int y = 0; y < FJ; ++y) acc[x][y] = mfma16x16x32(fb[y], fa[x], acc[x][y]);
     }
 
-    // lane (li, lg) holds C[i0 + 64 wi + 16 x + li][j0 + 64 wj + 16 y + 4 lg + r]
+    // lane (li, lg) holds C[i0 + 16 (FI wi + x) + li][j0 + 16 (FJ wj + y) + 4 lg + r]
 #pragma unroll
-    for (int x = 0; x < 4; ++x) {
-        const int64_t i = i0 + 64 * wi + 16 * x + li;
+    for (int x = 0; x < FI; ++x) {
+        const int64_t i = i0 + 16 * (FI * wi + x) + li;
         if (i >= a.I) continue;
 #pragma unroll
-        for (int y = 0; y < 4; ++y) {
-            const int64_t j = j0 + 64 * wj + 16 * y + 4 * lg;
+        for (int y = 0; y < FJ; ++y) {
+            const int64_t j = j0 + 16 * (FJ * wj + y) + 4 * lg;
             if (j >= a.J) continue;   // J % 8 == 0: the 4 columns are all in or all out
             const int64_t o = i * a.J + j;
             float v[4] = {acc[x][y][0], acc[x][y][1], acc[x][y][2], acc[x][y][3]};
@@ -258,16 +285,38 @@ __global__ __launch_bounds__(256) void zero_f32_kernel(float* p, int64_t n) {
     for (int64_t i = blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) p[i] = 0.f;
 }
 
+template <class Cfg, bool kAOuter, bool kBOuter, int kEpi>
+hipError_t launch_gemm_cfg(const GemmArgs& a, hipStream_t stream) {
+    auto kern = gemm_bf16_kernel<Cfg, kAOuter, kBOuter, kEpi>;
+    static std::atomic<bool> lds_set[kMaxDevices] = {};
+    hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), Cfg::kLds, lds_set);
+    if (e != hipSuccess) return e;
+    dim3 grid((unsigned)((a.J + Cfg::TJ - 1) / Cfg::TJ), (unsigned)((a.I + Cfg::TI - 1) / Cfg::TI));
+    hipLaunchKernelGGL(kern, grid, dim3(Cfg::kThreads), Cfg::kLds, stream, a);
+    return hipGetLastError();
+}
+
+// Tile choice, measured at the prefill shard (4096 x 4096 x 1792 x 4096, us per
+// product): 256 x 256 with eight waves of 128 x 64 wins when its tiles fill
+// the chip (dX, 4096 x 4096 outputs: 83 -> 62), but leaves it half idle on the
+// 4096 x 1792 outputs (97 -> 143); there the 128 x 128 tile (two workgroups
+// per CU) stays best: 256 x 128 or 128 x 256 tiles with four waves of 128 x 64
+// (one wave per SIMD) measured 101-127, with eight waves of 64 x 64 88-101,
+// a 5-stage ring for the 256 x 256 tile 69 on dX; four extra waves that only
+// issue the loads (as in the fused forward kernel) beside eight multiplying
+// waves of 64 x 64 on 256 x 128 or 128 x 256 tiles 103-189 (register caps
+// of three waves per SIMD).
+using GemmSmall = GemmCfg<128, 128, 2, 2>;   // four waves of 64 x 64
+using GemmLarge = GemmCfg<256, 256, 2, 4>;   // eight waves of 128 x 64
+
 template <bool kAOuter, bool kBOuter, int kEpi>
 hipError_t launch_gemm(const GemmArgs& a, hipStream_t stream) {
     if (a.I <= 0 || a.J <= 0) return hipSuccess;
-    auto kern = gemm_bf16_kernel<kAOuter, kBOuter, kEpi>;
-    static bool lds_set[kMaxDevices] = {};
-    hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), kGLds, lds_set);
-    if (e != hipSuccess) return e;
-    dim3 grid((unsigned)((a.J + kGT - 1) / kGT), (unsigned)((a.I + kGT - 1) / kGT));
-    hipLaunchKernelGGL(kern, grid, dim3(kGThreads), kGLds, stream, a);
-    return hipGetLastError();
+    const int64_t large_tiles = ((a.I + GemmLarge::TI - 1) / GemmLarge::TI) *
+                                ((a.J + GemmLarge::TJ - 1) / GemmLarge::TJ);
+    if (large_tiles >= device_cus())
+        return launch_gemm_cfg<GemmLarge, kAOuter, kBOuter, kEpi>(a, stream);
+    return launch_gemm_cfg<GemmSmall, kAOuter, kBOuter, kEpi>(a, stream);
 }
 
 GemmArgs gemm_args(const uint16_t* A, int64_t lda, const uint16_t* B, int64_t ldb, int64_t I,

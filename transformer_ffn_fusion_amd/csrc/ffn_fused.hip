@@ -618,7 +618,7 @@ template <int CA, int CB, bool G, bool kGated>
 hipError_t launch_fused_impl(const FusedArgs& a, int64_t units, hipStream_t stream) {
     using Cfg = FusedCfg<CA, CB, kGated>;
     auto kern = fused_ffn_bf16_kernel<CA, CB, G, kGated>;
-    static bool lds_set[kMaxDevices] = {};
+    static std::atomic<bool> lds_set[kMaxDevices] = {};
     hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), Cfg::kLds, lds_set);
     if (e != hipSuccess) return e;
     // grouped form: workgroups for the pieces of a short last round (at most
@@ -629,20 +629,6 @@ hipError_t launch_fused_impl(const FusedArgs& a, int64_t units, hipStream_t stre
     b.part_wt = part_bytes <= kMallBytes && a.rows_out * a.P * 4 < (1ll << 31);
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), Cfg::kLds, stream, b);
     return hipGetLastError();
-}
-
-// Compute units of the current device (queried once per device).
-int device_cus() {
-    static int cached[64] = {0};
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
-    if (cached[dev] == 0) {
-        int n = 0;
-        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
-            n = 256;
-        cached[dev] = n;
-    }
-    return cached[dev];
 }
 
 }  // namespace

@@ -4,6 +4,8 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+
+#include <atomic>
 #include <stddef.h>
 #include <stdint.h>
 
@@ -11,16 +13,34 @@ namespace ffn {
 
 // Raises a kernel's dynamic LDS limit on the current device, once per device
 // (the attribute belongs to the device the call is made on).  `done` is the
-// caller's per-kernel record.
+// caller's per-kernel record; concurrent first calls both set the attribute,
+// which is harmless.
 constexpr int kMaxDevices = 64;
-inline hipError_t set_dynamic_lds(const void* kern, int bytes, bool (&done)[kMaxDevices]) {
+inline hipError_t set_dynamic_lds(const void* kern, int bytes,
+                                  std::atomic<bool> (&done)[kMaxDevices]) {
     int dev = 0;
     hipError_t e = hipGetDevice(&dev);
     if (e != hipSuccess) return e;
-    if (dev >= 0 && dev < kMaxDevices && done[dev]) return hipSuccess;
+    const bool known = dev >= 0 && dev < kMaxDevices;
+    if (known && done[dev].load(std::memory_order_acquire)) return hipSuccess;
     e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-    if (e == hipSuccess && dev >= 0 && dev < kMaxDevices) done[dev] = true;
+    if (e == hipSuccess && known) done[dev].store(true, std::memory_order_release);
     return e;
+}
+
+// Compute units of the current device (queried once per device; 256 if the
+// query fails).
+inline int device_cus() {
+    static std::atomic<int> cached[kMaxDevices] = {};
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+            n = 256;
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
 }
 
 // ---- fused bf16 FFN with H kept in LDS (prefill shapes and the MoE groups)
