@@ -35,7 +35,7 @@
  *    (as in Switch Transformer and GShard, which the section names):
  *    logits = X Wr + br.
  *
- * Readings where the pages are silent (each also listed in the design doc):
+ * Readings where the pages are silent:
  *  - act1 is ReLU or the tanh form of GELU; GELU-tanh is
  *    0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))) (Hendrycks & Gimpel).
  *  - top-k ties go to the smaller expert index; slot 0 holds the largest logit.

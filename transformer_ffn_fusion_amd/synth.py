@@ -6,7 +6,7 @@ routing.
 Both sides of every parity check (the HIP library and the fp64 oracle) receive
 the arrays produced here, bit for bit.
 
-Recipe (the reading is recorded in the design doc):
+Recipe (seeds, drawing order and the variance reading are choices of this package):
 * ``numpy.random.default_rng(seed)`` (PCG64), ``standard_normal(dtype=float32)``
   scaled by the standard deviation, in the order X, W1, b1, W2, b2
   (MoE with logits as input: X, the logit draws, then per expert W1_e, b1_e,
