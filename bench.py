@@ -61,7 +61,8 @@ COPY_BYTES = 256 << 20   # the plain copy used to calibrate the HBM byte counter
 
 # the sources of the kernels whose HBM traffic is recorded (forward fused and grouped,
 # decode layers, routing and combine, and the headers they include)
-TRAFFIC_SOURCES = ("ffn_fused.hip", "ffn_skinny.hip", "moe.hip", "ffn_device.h", "ffn_internal.h")
+TRAFFIC_SOURCES = ("ffn_fused.hip", "ffn_skinny.hip", "moe.hip", "ffn_backward.hip", "ffn_device.h",
+                   "ffn_internal.h")
 
 
 def kernel_source_hash() -> str:
@@ -501,12 +502,12 @@ def main():
         r["traced_ms_per_step"] = sum(r["steps_ms"].values())
         value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
         unit = "TFLOP/s"
-        dom = max(r["steps_ms"], key=r["steps_ms"].get)
+        dom = "h_and_grad"   # the first product (recomputes H and act1'(a)): the longest step
         gemm_flops = 2 * head.M * head.N * head.O
         ach = gemm_flops / (r["steps_ms"][dom] * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": f"backward GEMM ({dom})", "achieved": ach,
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s", "frac": ach / PEAK_BF16_TFLOPS,
-                "traffic": None, "kernel_us": 1e3 * r["steps_ms"][dom],
+                "traffic": recorded_traffic(head.name), "kernel_us": 1e3 * r["steps_ms"][dom],
                 "steps_us": {k: 1e3 * v for k, v in r["steps_ms"].items()},
                 "executed_TFLOP_per_s": r["flops_exec"] / (r["ms_per_step"] * 1e-3) / 1e12}
         dense = None
