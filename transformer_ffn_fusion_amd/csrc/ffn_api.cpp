@@ -127,16 +127,17 @@ SwigluLayout swiglu_layout(int64_t M, int64_t N, int64_t O, int64_t P, int varia
 
 // ---- backward workspace layout
 struct BackwardLayout {
-    size_t H = 0, G = 0, dA = 0, total = 0;
+    size_t H = 0, G = 0, dA = 0, colpart = 0, total = 0;
 };
 
-BackwardLayout backward_layout(int64_t M, int64_t O, int64_t) {
+BackwardLayout backward_layout(int64_t M, int64_t O, int64_t P) {
     BackwardLayout L;
     size_t off = 0;
-    L.H = off;     off += align_up(sizeof(uint16_t) * M * O);
-    L.G = off;     off += align_up(sizeof(uint16_t) * M * O);
-    L.dA = off;    off += align_up(sizeof(uint16_t) * M * O);
-    L.total = off ? off : kAlign;
+    L.H = off;       off += align_up(sizeof(uint16_t) * M * O);
+    L.G = off;       off += align_up(sizeof(uint16_t) * M * O);
+    L.dA = off;      off += align_up(sizeof(uint16_t) * M * O);
+    L.colpart = off; off += align_up(sizeof(float) * ffn::colsum_partial_floats(O, P));
+    L.total = off;
     return L;
 }
 
@@ -373,6 +374,7 @@ static int backward(const void* X, const void* W1, const void* b1, const void* W
     io.H = reinterpret_cast<uint16_t*>(ws + L.H);
     io.Gr = reinterpret_cast<uint16_t*>(ws + L.G);
     io.dA = reinterpret_cast<uint16_t*>(ws + L.dA);
+    io.colpart = reinterpret_cast<float*>(ws + L.colpart);
     io.M = M;
     io.N = N;
     io.O = O;

@@ -151,10 +151,12 @@ struct BackwardIO {
     uint16_t* dX = nullptr;              // M x N bf16
     float *dW1 = nullptr, *db1 = nullptr, *dW2 = nullptr, *db2 = nullptr;
     uint16_t *H = nullptr, *Gr = nullptr, *dA = nullptr;   // workspace, M x O bf16 each
+    float* colpart = nullptr;   // workspace, colsum_partial_floats(O, P) floats
     int64_t M = 0, N = 0, O = 0, P = 0;
     int act1 = 0;
 };
 hipError_t launch_zero_f32(float* p, int64_t n, hipStream_t stream);   // a fill kernel, no memset
+size_t colsum_partial_floats(int64_t O, int64_t P);   // row-chunk partials of the bias sums
 // events (may be null): events[s] recorded before step s + 1 (steps: h and g,
 // da, dX, dW1, dW2, bias sums), events[6] after the last; n_events >= 7 to get all
 hipError_t launch_ffn_backward(const BackwardIO& io, hipStream_t stream, void** events,
