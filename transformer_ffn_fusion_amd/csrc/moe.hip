@@ -197,7 +197,6 @@ __global__ __launch_bounds__(kScanThreads) void moe_scan_kernel(
     __shared__ int s_tot[kMaxE];
     __shared__ int s_off[kMaxE];
     __shared__ int s_order[kMaxE];
-    __shared__ int s_done[kMaxE];
     __shared__ int s_tstart[kMaxE + 1];
     const int tid = threadIdx.x;
     int epow = 1;
@@ -221,36 +220,48 @@ __global__ __launch_bounds__(kScanThreads) void moe_scan_kernel(
         for (int64_t bb = b0; bb < b1; ++bb) sum += bcount(bb);
     s_part[tid] = sum;
     __syncthreads();
+    // only the first nparts threads of an expert own blocks (the rest hold
+    // zeros): the prefix and the total loop over those alone (a loop over all
+    // tpe = 1024 / E threads cost ~10 us of serial LDS reads at E = 8)
+    const int nparts = per > 0 ? (int)((nblk_b + per - 1) / per) : 0;
     int pre = 0;
     if (act) {
-        for (int q = 0; q < r; ++q) pre += s_part[e * tpe + q];
+        const int upto = r < nparts ? r : nparts;
+        for (int q = 0; q < upto; ++q) pre += s_part[e * tpe + q];
         if (r == 0) {
             int tot = 0;
-            for (int q = 0; q < tpe; ++q) tot += s_part[e * tpe + q];
+            for (int q = 0; q < nparts; ++q) tot += s_part[e * tpe + q];
             s_tot[e] = tot;
         }
     }
     __syncthreads();
-    if (tid == 0) {
-        int run = 0;
-        for (int x = 0; x < E; ++x) {
-            s_off[x] = run;
-            counts[x] = s_tot[x];
-            offsets[x] = run;
-            run += s_tot[x];
-            s_done[x] = 0;
+    // one thread per expert: its offset (the totals of the experts before
+    // it), its place in the heaviest-first order (ties to the smaller index)
+    // and its first tile (the tiles of the experts placed before it); every
+    // thread reads all E totals, so no step waits on another's result
+    if (tid < E) {
+        const int x = tid, tx = s_tot[x];
+        int off = 0, place = 0, first = 0, all = 0;
+        for (int y = 0; y < E; ++y) {
+            const int ty = s_tot[y];
+            const int ny = (ty + kBM - 1) / kBM;
+            all += ny;
+            if (y < x) off += ty;
+            if (ty > tx || (ty == tx && y < x)) {
+                ++place;
+                first += ny;
+            }
         }
-        offsets[E] = run;
-        s_tstart[0] = 0;
-        for (int p = 0; p < E; ++p) {
-            int best = -1;
-            for (int x = 0; x < E; ++x)
-                if (!s_done[x] && (best < 0 || s_tot[x] > s_tot[best])) best = x;
-            s_done[best] = 1;
-            s_order[p] = best;
-            s_tstart[p + 1] = s_tstart[p] + (s_tot[best] + kBM - 1) / kBM;
+        s_off[x] = off;
+        counts[x] = tx;
+        offsets[x] = off;
+        s_order[place] = x;
+        s_tstart[place] = first;
+        if (x == E - 1) offsets[E] = off + tx;
+        if (x == 0) {
+            s_tstart[E] = all;
+            *tile_count = all;
         }
-        *tile_count = s_tstart[E];
     }
     __syncthreads();
     if (act) {
@@ -262,8 +273,15 @@ __global__ __launch_bounds__(kScanThreads) void moe_scan_kernel(
     }
     const int ntiles = s_tstart[E];
     for (int i = tid; i < ntiles; i += kScanThreads) {
-        int p = 0;
-        while (s_tstart[p + 1] <= i) ++p;   // i < s_tstart[E]: stops at p < E
+        // the place p with s_tstart[p] <= i < s_tstart[p + 1]: a bisection
+        // that keeps s_tstart[lo] <= i < s_tstart[hi] (true at 0 and E)
+        int lo = 0, hi = E;
+        while (hi - lo > 1) {
+            const int mid = (lo + hi) >> 1;
+            if (s_tstart[mid] <= i) lo = mid;
+            else hi = mid;
+        }
+        const int p = lo;
         const int x = s_order[p];
         const int r0 = (i - s_tstart[p]) * kBM;
         tiles[3 * i + 0] = x;
