@@ -203,6 +203,8 @@ def test_moe_workload():
     (64, 1, 1, 256, 448, 512),
     (100, 4, 2, 128, 512, 4096),   # a short round: each unit cut into 8 pass ranges
     (300, 8, 2, 64, 1024, 2048),   # 2 chunks, pass ranges of a 4-pass output
+    (200, 64, 2, 64, 448, 128),    # many experts, a few tokens each, some with none
+    (90, 256, 1, 64, 256, 64),     # the largest expert count: most experts receive no token
 ])
 def test_moe_shapes(M, E, k, N, O, P):
     log(f"case moe M={M} E={E} k={k} N={N} O={O} P={P}")
