@@ -15,7 +15,8 @@ import oracle
 import transformer_ffn_fusion_amd as ffn
 from transformer_ffn_fusion_amd import synth, workload
 
-from gpu_util import BF16_TOL, F32_TOL, compare, dev_bf16, dev_f32, host_f64, log
+from gpu_util import (BF16_TOL, F32_TOL, compare, compare_with_bf16_rounding, dev_bf16, dev_f32,
+                      host_f64, log)
 
 pytestmark = pytest.mark.gpu
 
@@ -302,3 +303,62 @@ def test_ceiling_kernels_run():
     assert flops == 2048 * 4 * 4 * 8 * (2.0 * 16 * 16 * 32)
     assert nbytes == 1 << 20
     assert float(sink.abs().sum()) == 0.0   # the sink is never written
+
+
+# ---------------------------------------------------------------- every row at full size
+#
+# A row of Y depends on its own row of X only (and, for MoE, on its own
+# logits).  Permuting the tokens must therefore permute the output rows; this
+# checks every row of the full-size workloads without the oracle.  Bitwise
+# where the summation order of every output element is fixed by its column
+# alone (decode: the K blocks of a column are summed in ascending order
+# whatever the row; MoE routing: integers).  The fused and grouped kernels
+# start each unit's k-loops at a stage rotated by the unit's index (to spread
+# the L2 traffic of units that stream the same weights), so a row's summation
+# order depends on the tile it lands in: each call is bitwise reproducible, but
+# a permuted call agrees with the original only to the two outputs' bf16
+# roundings, |a - b| <= 2e-2 rms + 2^-8 |b|, on every row.
+
+
+def _rows_agree(got, ref, bitwise, what):
+    import torch
+    assert bool(torch.isfinite(got.float()).all()), f"{what}: non-finite output"
+    if bitwise:
+        assert torch.equal(got, ref), f"{what}: permuted rows give different bits"
+    else:
+        compare_with_bf16_rounding(host_f64(got), host_f64(ref), BF16_TOL, what)
+
+
+@pytest.mark.parametrize("which", ["prefill", "decode"])
+def test_rows_permutation_equivariant(which):
+    import torch
+    c = workload.PREFILL if which == "prefill" else workload.DECODE
+    log(f"case row permutation {c.name}")
+    X, W1, b1, W2, b2 = (dev_bf16(a) for a in synth.dense_inputs(c.M, c.N, c.O, c.P, seed=21))
+    perm = torch.as_tensor(np.random.default_rng(22).permutation(c.M), device="cuda")
+    Y = torch.empty((c.M, c.P), dtype=torch.bfloat16, device="cuda")
+    Yp = torch.empty_like(Y)
+    ffn.ffn_forward(X, W1, b1, W2, b2, Y)
+    ffn.ffn_forward(X[perm].contiguous(), W1, b1, W2, b2, Yp)
+    torch.cuda.synchronize()
+    _rows_agree(Yp, Y[perm], which == "decode", f"row permutation {c.name}")
+
+
+def test_moe_tokens_permutation_equivariant():
+    import torch
+    c = workload.MOE
+    log(f"case token permutation {c.name}")
+    X, lg, W1, b1, W2, b2 = synth.moe_inputs(c.M, c.E, c.N, c.O, c.P, seed=23)
+    dX, dW1, db1, dW2, db2 = (dev_bf16(a) for a in (X, W1, b1, W2, b2))
+    dl = dev_f32(lg)
+    perm = torch.as_tensor(np.random.default_rng(24).permutation(c.M), device="cuda")
+    outs = []
+    for xs, ls in ((dX, dl), (dX[perm].contiguous(), dl[perm].contiguous())):
+        Y = torch.empty((c.M, c.P), dtype=torch.bfloat16, device="cuda")
+        ids = torch.empty((c.M, c.k), dtype=torch.int32, device="cuda")
+        ffn.moe_ffn_forward(xs, ls, c.k, dW1, db1, dW2, db2, Y, topk_ids=ids)
+        outs.append((Y, ids))
+    torch.cuda.synchronize()
+    (Y, ids), (Yp, idsp) = outs
+    assert torch.equal(idsp, ids[perm]), "permuted tokens route differently"
+    _rows_agree(Yp, Y[perm], False, f"token permutation {c.name}")
