@@ -117,6 +117,8 @@ struct FusedArgs {
 // 137); large shard, 2 GiB: 1307 + 429 streamed, 1480 + 472 written through;
 // MoE, 512 MiB: 488 streamed, 510 written through.
 constexpr int64_t kMallBytes = 256ll << 20;
+constexpr int64_t kL2Bytes = 4ll << 20;   // L2 of one XCD
+constexpr int64_t kPassWindow = 4;        // pass rotation window when W2's block overflows it
 constexpr int kCpolSc1 = 16;   // buffer cache-policy bits: sc1 (device scope)
 typedef unsigned uint32x4_t __attribute__((ext_vector_type(4)));
 
@@ -440,9 +442,18 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     // per expert (560 -> 530 us on the MoE workload); only the k order inside
     // a pass rotates, so that workgroups of one expert read different slabs
     // of the same pass (530 -> 487 us).
+    // The pass rotation spans every pass only while the chunk's W2 block
+    // (hidden columns x P) fits the XCD's 4 MB L2 and stays resident; a larger
+    // block is walked by the co-resident workgroups inside a window of 4
+    // passes, so the lines they share are still in L2 when the later ones
+    // read them (large shard, 448 x 8192 block: kernel 1325 -> ~1150 us, an
+    // 8-pass window ~1190; prefill shard, 448 x 4096 block: a window of 4, 2
+    // or 1 passes 172-176 us against 155 for the full rotation).
     const int64_t jx = blockIdx.x >> 3;
     c.rot1 = kGrouped ? 0 : jx % c.nk;
-    const int64_t rotp = kGrouped ? 0 : jx % npl;
+    const int64_t rot_span =
+        (int64_t)Cfg::kHid * P * 2 <= kL2Bytes ? npl : (npl < kPassWindow ? npl : kPassWindow);
+    const int64_t rotp = kGrouped ? 0 : jx % rot_span;
     const int rotk = (int)(jx % Cfg::kKS);
     char* const hreg = smem + Cfg::kHOff;
 
