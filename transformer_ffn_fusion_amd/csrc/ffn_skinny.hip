@@ -34,7 +34,7 @@ namespace ffn {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kBatch = 8;    // partials the last arriver loads at once
+constexpr int kBatch = 8;    // a reduction thread keeps 2 * kBatch K-block partial loads in flight
 
 struct SkinnyArgs {
     const uint16_t* A;
