@@ -227,3 +227,13 @@ def test_ceiling_entry_points_reject_before_launch():
     assert L.ffn_ceiling_read(FAKE + 4, 1 << 20, FAKE, sink_bytes, None) == E_ALIGN
     assert L.ffn_ceiling_read(FAKE, 24, FAKE, sink_bytes, None) == E_INVAL
     assert L.ffn_ceiling_read(FAKE, 1 << 20, FAKE, 8, None) == E_WS
+
+
+def test_workspace_follows_the_split_count():
+    """The dense fused form's workspace holds the fp32 partials of its splits:
+    448-wide chunks at the prefill shard (4 splits), 896-wide two-pass chunks at
+    the large shard (4 splits instead of 8), from the shape alone (no device)."""
+    pre = ffn.ffn_workspace_size(4096, 4096, 1792, 4096)
+    assert 4 * 4096 * 4096 * 4 <= pre < 5 * 4096 * 4096 * 4
+    big = ffn.ffn_workspace_size(8192, 8192, 3584, 8192)
+    assert 4 * 8192 * 8192 * 4 <= big < 5 * 8192 * 8192 * 4

@@ -223,6 +223,20 @@ def test_moe_expert_shard_workload():
     compare(got, ref, BF16_TOL, c.name)
 
 
+def test_fused_two_pass_chunk_sampled_rows():
+    """Where 448-wide chunks would give four or more full rounds of units, each
+    workgroup covers 896 hidden columns in two first-product passes (half the
+    splits): 64 row tiles (the last ragged) x 8 splits, ragged K and output pass."""
+    M, N, O, P = 4090, 136, 7168, 1032
+    rows = synth.check_rows(M)
+    rows = np.union1d(rows, np.arange(4032, M))   # every row of the ragged last tile
+    log(f"case fused two-pass chunk {(M, N, O, P)}, {rows.size} rows")
+    got, ref, outs = _run_dense(M, N, O, P, variant=ffn.VARIANT_FUSED, seed=31, rows=rows, repeat=2)
+    compare(got, ref, BF16_TOL, "fused two-pass chunk")
+    import torch
+    assert torch.equal(outs[0], outs[1]), "two calls differ"
+
+
 @pytest.mark.parametrize("shape", [(100, 256, 256, 520), (70, 64, 136, 64)])
 def test_fused_narrow_hidden(shape):
     """Hidden widths of at most 256 run the 256-wide chunk."""

@@ -74,7 +74,7 @@ struct DenseLayout {
 DenseLayout dense_layout(int64_t M, int64_t N, int64_t O, int64_t P, int variant) {
     DenseLayout L;
     if (variant == FFN_VARIANT_FUSED) {
-        const int chunk = ffn::fused_pick_chunk(O);
+        const int chunk = ffn::fused_pick_dense_chunk(M, O);
         const int S = ffn::fused_num_splits(O, chunk);
         L.part = 0;
         L.total = align_up((size_t)S * M * P * sizeof(float));
@@ -249,7 +249,7 @@ static int dense_forward(const void* X, const void* W1, const void* b1, const vo
     char* ws = static_cast<char*>(workspace);
     if ((rc = mark(events, n_events, 0, st))) return rc;
     if (v == FFN_VARIANT_FUSED) {
-        const int chunk = ffn::fused_pick_chunk(O);
+        const int chunk = ffn::fused_pick_dense_chunk(M, O);
         const int S = ffn::fused_num_splits(O, chunk);
         float* part = reinterpret_cast<float*>(ws + L.part);
         const int64_t rbs = (M + ffn::kBM - 1) / ffn::kBM;

@@ -48,13 +48,13 @@ constexpr int kSub = kBM * kBK * 2;    // one 32-deep slab of X or H in LDS: 4 K
 
 // One first-product pass: a stage of 32 k-rows of X (64 rows) and of CP
 // columns of W1, held in an NS-deep LDS ring.
-template <int CP>
+template <int CP, int NS = 4>
 struct PassCfg {
     static constexpr int kNB1 = CP / 64;               // W1 stage: 64-column blocks per row group
     static constexpr int kFO = CP / 64;                // fragments per multiplier wave (every 4th)
     static constexpr int kW1Stage = 4 * kNB1 * kFrag;  // 32 x CP bf16
     static constexpr int kStage1 = kSub + kW1Stage;    // X slab + W1 slab
-    static constexpr int kNS1 = 4;                     // stages in the LDS ring
+    static constexpr int kNS1 = NS;                    // stages in the LDS ring
     static constexpr int kD1 = 1 + kNB1;               // loads per loader wave per stage
     static constexpr int kLds1 = kNS1 * kStage1;
     static_assert(CP % 64 == 0, "a pass splits over four waves in 16-column fragments");
@@ -71,8 +71,11 @@ struct PassCfg {
 // over, so H is contiguous and the whole kernel needs max(ring A, ring B + H A).
 template <int CA, int CB, bool kGated>
 struct FusedCfg {
+    // the dense two-pass chunk (448 + 448 hidden columns) fits the LDS only
+    // with a 3-deep ring for its second pass
+    static constexpr int kNSB = (CB > 0 && !kGated) ? 3 : 4;
     using PA = PassCfg<CA>;
-    using PB = PassCfg<(CB > 0 ? CB : 64)>;            // unused with one pass
+    using PB = PassCfg<(CB > 0 ? CB : 64), kNSB>;      // unused with one pass
     static constexpr bool kTwoPass = CB > 0;
     static constexpr int kHidA = kGated ? CA / 2 : CA;
     static constexpr int kHidB = kTwoPass ? (kGated ? CB / 2 : CB) : 0;
@@ -85,7 +88,6 @@ struct FusedCfg {
     static_assert(kHidA % kBK == 0 && kHidB % kBK == 0, "passes cover whole H slabs");
     static_assert(!kGated || (PA::kNB1 % 2 == 0 && (!kTwoPass || PB::kNB1 % 2 == 0)),
                   "gate and up halves are whole 64-column blocks");
-    static_assert(!kTwoPass || kGated, "two passes are used by the gated form only");
     static_assert(kKS % 2 == 0, "GEMM2 runs its stages in pairs");
     static_assert(kBN2 == 64 * 2 * kMulWaves, "each of the eight waves owns 64 columns of a pass");
     static_assert(kLds <= 160 * 1024, "LDS budget");
@@ -119,6 +121,8 @@ struct FusedArgs {
 constexpr int64_t kMallBytes = 256ll << 20;
 constexpr int64_t kL2Bytes = 4ll << 20;   // L2 of one XCD
 constexpr int64_t kPassWindow = 4;        // pass rotation window when W2's block overflows it
+constexpr int kWideChunk = 896;           // dense two-pass chunk: 448 + 448 hidden columns
+constexpr int64_t kRoundUnits = 256;      // workgroups in one round on MI355X (one per CU)
 constexpr int kCpolSc1 = 16;   // buffer cache-policy bits: sc1 (device scope)
 typedef unsigned uint32x4_t __attribute__((ext_vector_type(4)));
 
@@ -658,6 +662,22 @@ int fused_pick_chunk(int64_t O) {
 
 int fused_num_splits(int64_t O, int chunk) { return (int)((O + chunk - 1) / chunk); }
 
+// Dense form: where 448-wide chunks would give at least four full rounds of
+// units on MI355X's 256 CUs, two 448-column first-product passes per
+// workgroup (896 hidden columns) halve the split count, and with it the fp32
+// partials written and reduced, while still filling whole rounds (large
+// shard, 8192 rows x 3584 hidden: 8 splits and 1024 units become 4 splits and
+// 512 units).  The rule depends on the shape only, so the workspace size is
+// known without a device.
+int fused_pick_dense_chunk(int64_t M, int64_t O) {
+    const int c = fused_pick_chunk(O);
+    const int64_t rows = (M + kBM - 1) / kBM;
+    if (c == 448 && O % kWideChunk == 0 && 8 % (O / kWideChunk) == 0 &&
+        rows * (O / 448) >= 4 * kRoundUnits && (rows * (O / kWideChunk)) % kRoundUnits == 0)
+        return kWideChunk;
+    return c;
+}
+
 hipError_t launch_fused_bf16(const uint16_t* X, const uint16_t* W1, const uint16_t* b1,
                              const uint16_t* W2, float* part, int64_t M, int64_t N, int64_t O,
                              int64_t P, int act1, int chunk, int64_t row_blocks,
@@ -681,6 +701,8 @@ hipError_t launch_fused_bf16(const uint16_t* X, const uint16_t* W1, const uint16
     if (grouped) a.g = *grouped;
     const int64_t units = row_blocks * a.splits;
     if (units <= 0) return hipSuccess;
+    if (chunk == kWideChunk && !grouped)
+        return launch_fused_impl<448, 448, false, false>(a, units, stream);
     if (chunk == 448)
         return grouped ? launch_fused_impl<448, 0, true, false>(a, units, stream)
                        : launch_fused_impl<448, 0, false, false>(a, units, stream);

@@ -51,6 +51,7 @@ constexpr int kBN2 = 512;   // output columns per second-layer pass
 // Hidden-chunk widths the fused kernel is instantiated for.
 int fused_pick_chunk(int64_t O);                 // 256, 448 or 512
 int fused_num_splits(int64_t O, int chunk);      // ceil(O / chunk)
+int fused_pick_dense_chunk(int64_t M, int64_t O); // dense form: 896 (two passes) or fused_pick_chunk(O)
 
 struct GroupedRows {
     const int32_t* tiles = nullptr;       // [max_tiles][3]: expert, first row, valid rows
