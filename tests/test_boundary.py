@@ -237,3 +237,6 @@ def test_workspace_follows_the_split_count():
     assert 4 * 4096 * 4096 * 4 <= pre < 5 * 4096 * 4096 * 4
     big = ffn.ffn_workspace_size(8192, 8192, 3584, 8192)
     assert 4 * 8192 * 8192 * 4 <= big < 5 * 8192 * 8192 * 4
+    # the GPU parity case of the two-pass form (4090 rows, 7168 hidden): 8 splits, not 16
+    two = ffn.ffn_workspace_size(4090, 136, 7168, 1032)
+    assert 8 * 4090 * 1032 * 4 <= two < 9 * 4090 * 1032 * 4
