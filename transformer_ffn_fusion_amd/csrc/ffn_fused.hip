@@ -662,20 +662,20 @@ int fused_pick_chunk(int64_t O) {
 
 int fused_num_splits(int64_t O, int chunk) { return (int)((O + chunk - 1) / chunk); }
 
-// Dense form: where 448-wide chunks would give at least four full rounds of
-// units on MI355X's 256 CUs, two 448-column first-product passes per
-// workgroup (896 hidden columns) halve the split count, and with it the fp32
-// partials written and reduced, while still filling whole rounds (large
-// shard, 8192 rows x 3584 hidden: 8 splits and 1024 units become 4 splits and
-// 512 units).  The rule depends on the shape only, so the workspace size is
-// known without a device.
+// Dense form: where 896 hidden columns divide O into a split count that
+// divides 8 and the units fill two or more whole rounds of MI355X's 256 CUs,
+// each workgroup covers 896 columns in two 448-column first-product passes:
+// fewer splits, and fewer fp32 partials written and reduced, than any
+// single-pass chunk (large shard, 8192 rows x 3584 hidden: 8 splits and 1024
+// units of 448 become 4 splits and 512 units).  The rule depends on the shape
+// only, so the workspace size is known without a device.
 int fused_pick_dense_chunk(int64_t M, int64_t O) {
-    const int c = fused_pick_chunk(O);
     const int64_t rows = (M + kBM - 1) / kBM;
-    if (c == 448 && O % kWideChunk == 0 && 8 % (O / kWideChunk) == 0 &&
-        rows * (O / 448) >= 4 * kRoundUnits && (rows * (O / kWideChunk)) % kRoundUnits == 0)
+    const int64_t s = O / kWideChunk;
+    if (O % kWideChunk == 0 && s >= 1 && 8 % s == 0 && rows * s >= 2 * kRoundUnits &&
+        (rows * s) % kRoundUnits == 0)
         return kWideChunk;
-    return c;
+    return fused_pick_chunk(O);
 }
 
 hipError_t launch_fused_bf16(const uint16_t* X, const uint16_t* W1, const uint16_t* b1,
