@@ -46,13 +46,13 @@ def compare_with_bf16_rounding(y_gpu, y_ref, tol, what=""):
     """As ``compare``, with one bf16 rounding per element added to the allowance:
     |Y - Yref| <= tol * rms(Yref) + 2^-8 |Yref|.
 
-    For a bf16 output, rounding the exact result alone moves an element by up to
-    2^-9 |y|; with max|Yref| ~ 5.4 rms (a million sampled outputs) that is 1.5e-2 rms,
-    most of the 2e-2 rms budget, before any accumulation error.  For a gradient
-    whose terms are products with one bf16-rounded factor (da or h), a short sum
-    (one token: an outer product) keeps that factor's relative error 2^-9 on every
-    element, and the largest elements of a product of two normal draws are ~12 rms.
-    2^-8 |Yref| covers one such rounding of a value that carries its own error."""
+    bf16 keeps 8 significant bits, so rounding to nearest moves a value y by at most
+    half an ulp, 2^-8 |y| (reached just above a power of two; 2^-9 |y| is only the
+    typical size).  For a gradient whose terms are products with one bf16-rounded
+    factor (da or h), a short sum (one token: an outer product) keeps that factor's
+    relative rounding error on every element, and the largest elements of a product
+    of two normal draws are ~12 rms.  2^-8 |Yref| covers one such rounding.  The
+    forward outputs are checked with ``compare`` (the plain rule) instead."""
     assert y_gpu.shape == y_ref.shape, (y_gpu.shape, y_ref.shape)
     assert np.all(np.isfinite(y_gpu)), f"{what}: non-finite output"
     rms = float(np.sqrt(np.mean(y_ref ** 2)))

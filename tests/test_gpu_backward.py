@@ -5,7 +5,7 @@ Every gradient tensor is checked with the bf16 rule of the forward (max |err| <=
 (compare_with_bf16_rounding): the intermediates h, act1'(a) and dY W2^T * act1'(a)
 are rounded to bf16 once and enter every product as a factor, the sums accumulate
 in fp32; with one token, dW1 is an outer product whose every element keeps the
-2^-9 relative rounding of its da factor.  At full size the oracle
+relative rounding of its da factor (up to 2^-8).  At full size the oracle
 computes sampled rows of dX and sampled hidden columns of dW1, db1 and dW2 (rows of
 dX and columns of the weight gradients are independent of each other)."""
 from __future__ import annotations

@@ -152,10 +152,23 @@ def test_zero_rows_is_noop_and_errors_leave_output_untouched():
 
 # ---------------------------------------------------------------- MoE
 
+def moe_layer_inputs(M, E, N, O, P, *, seed=0, offsets=synth.MOE_SKEW_OFFSETS):
+    """MoE inputs with the gate logits formed as the workload states them: one linear
+    router, logits = X Wr + offsets (the MoE review, zhongzhuzhou.org, section 2.2,
+    step 1: each token runs the gate).  The oracle sums in fp64 and the result is
+    rounded once to fp32; both sides then route from the same fp32 array."""
+    X, Wr, br, W1, b1, W2, b2 = synth.moe_router_inputs(M, E, N, O, P, seed=seed, offsets=offsets)
+    logits = oracle.router_logits(X, Wr, br).astype(np.float32)
+    return X, logits, W1, b1, W2, b2
+
+
 def _run_moe(M, E, k, N, O, P, *, seed=0, offsets=synth.MOE_SKEW_OFFSETS, rows=None,
-             check_all_rows=False):
+             check_all_rows=False, router_logits=False):
     import torch
-    X, logits, W1, b1, W2, b2 = synth.moe_inputs(M, E, N, O, P, seed=seed, offsets=offsets)
+    if router_logits:
+        X, logits, W1, b1, W2, b2 = moe_layer_inputs(M, E, N, O, P, seed=seed, offsets=offsets)
+    else:
+        X, logits, W1, b1, W2, b2 = synth.moe_inputs(M, E, N, O, P, seed=seed, offsets=offsets)
     dX, dl = dev_bf16(X), dev_f32(logits)
     Y = torch.empty((M, P), dtype=torch.bfloat16, device="cuda")
     ids = torch.empty((M, k), dtype=torch.int32, device="cuda")
@@ -190,11 +203,22 @@ def _run_moe(M, E, k, N, O, P, *, seed=0, offsets=synth.MOE_SKEW_OFFSETS, rows=N
 
 
 def test_moe_workload():
+    """The MoE workload as configured (router logits X Wr + offsets), every token."""
     c = workload.MOE
-    log(f"case {c.name}")
-    got, ref, counts = _run_moe(c.M, c.E, c.k, c.N, c.O, c.P)
+    log(f"case {c.name}, every token")
+    got, ref, counts = _run_moe(c.M, c.E, c.k, c.N, c.O, c.P, router_logits=True,
+                                check_all_rows=True)
     log(f"  expert loads {counts.tolist()}")
     compare(got, ref, BF16_TOL, c.name)
+
+
+def test_moe_workload_drawn_logits_sampled():
+    """The same layer with the logits drawn directly (normal + offset): sampled rows,
+    the first and last token of every expert list."""
+    c = workload.MOE
+    log(f"case {c.name}, drawn logits, sampled tokens")
+    got, ref, _ = _run_moe(c.M, c.E, c.k, c.N, c.O, c.P)
+    compare(got, ref, BF16_TOL, c.name + " (drawn logits)")
 
 
 @pytest.mark.parametrize("M,E,k,N,O,P", [
@@ -215,10 +239,12 @@ def test_moe_shapes(M, E, k, N, O, P):
 
 
 def test_moe_expert_shard_workload():
-    """One GPU's share of an 8-way expert-sharded layer: every expert at O = 256."""
+    """One GPU's share of an 8-way expert-sharded layer: every expert at O = 256, the
+    router logits of the full layer, every token."""
     c = workload.MOE_SHARD
-    log(f"case {c.name}")
-    got, ref, counts = _run_moe(c.M, c.E, c.k, c.N, c.O, c.P)
+    log(f"case {c.name}, every token")
+    got, ref, counts = _run_moe(c.M, c.E, c.k, c.N, c.O, c.P, router_logits=True,
+                                check_all_rows=True)
     log(f"  expert loads {counts.tolist()}")
     compare(got, ref, BF16_TOL, c.name)
 
@@ -288,21 +314,19 @@ def test_decode_workload():
     assert torch.equal(outs[0], outs[1]), "two calls differ"
 
 
-def test_prefill_workload_sampled_rows():
+def test_prefill_workload():
     c = workload.PREFILL
-    rows = synth.check_rows(c.M)
-    log(f"case {c.name}, {rows.size} sampled rows")
-    got, ref, outs = _run_dense(c.M, c.N, c.O, c.P, rows=rows, repeat=2)
+    log(f"case {c.name}, every row")
+    got, ref, outs = _run_dense(c.M, c.N, c.O, c.P, repeat=2)
     compare(got, ref, BF16_TOL, c.name)
     import torch
     assert torch.equal(outs[0], outs[1]), "two calls differ"
 
 
-def test_large_workload_sampled_rows():
+def test_large_workload():
     c = workload.LARGE
-    rows = synth.check_rows(c.M, n_random=57)
-    log(f"case {c.name}, {rows.size} sampled rows")
-    got, ref, _ = _run_dense(c.M, c.N, c.O, c.P, rows=rows)
+    log(f"case {c.name}, every row")
+    got, ref, _ = _run_dense(c.M, c.N, c.O, c.P)
     compare(got, ref, BF16_TOL, c.name)
 
 

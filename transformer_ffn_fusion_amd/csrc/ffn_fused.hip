@@ -69,7 +69,11 @@ struct PassCfg {
 // passes, pass B's ring ends where pass A's H begins (pass A's H must survive
 // pass B) and pass B's own H goes into the top of its ring once the pass is
 // over, so H is contiguous and the whole kernel needs max(ring A, ring B + H A).
-template <int CA, int CB, bool kGated>
+// kHLo (compensated H): H is held as two bf16 tiles, hi = bf16(h) and
+// lo = bf16(h - hi), kLoOff bytes apart; the second product multiplies both
+// with the same W2 operand into the same fp32 accumulators, so the error H
+// adds to Y is that of a ~16-bit significand instead of bf16's 8 bits.
+template <int CA, int CB, bool kGated, bool kHLo = false>
 struct FusedCfg {
     // the dense two-pass chunk (448 + 448 hidden columns) fits the LDS only
     // with a 3-deep ring for its second pass
@@ -83,7 +87,9 @@ struct FusedCfg {
     static constexpr int kKS = kHid / kBK;             // GEMM2 k-stages per output pass
     static constexpr int kSlabsB = kHidB / kBK;
     static constexpr int kHOff = kTwoPass ? PB::kLds1 - kSlabsB * kSub : 0;
-    static constexpr int kHEnd = kHOff + kKS * kSub;
+    // compensated H: a second set of kKS slabs holds the bf16 rounding residue
+    static constexpr int kLoOff = kKS * kSub;
+    static constexpr int kHEnd = kHOff + (kHLo ? 2 : 1) * kKS * kSub;
     static constexpr int kLds = PA::kLds1 > kHEnd ? PA::kLds1 : kHEnd;
     static_assert(kHidA % kBK == 0 && kHidB % kBK == 0, "passes cover whole H slabs");
     static_assert(!kGated || (PA::kNB1 % 2 == 0 && (!kTwoPass || PB::kNB1 % 2 == 0)),
@@ -282,8 +288,9 @@ __device__ __forceinline__ void gemm1_mma(const G1Ctx& c, floatx4_t (&acc)[PC::k
 // hidden index of the pass's first column; columns at or past O become zero.
 // Gated form: fragment fo (< kFO/2) holds gate columns and fragment fo + kFO/2
 // the up columns of the same hidden indices (block fo of the W1 stage is
-// fragment fo of every wave).  Both forms round H to bf16 once.
-template <class PC, bool kGated>
+// fragment fo of every wave).  Both forms round H to bf16 once; with kHLo the
+// residue h - bf16(h), rounded to bf16, goes kLoOff bytes further.
+template <class PC, bool kGated, bool kHLo, int kLoOff>
 __device__ __forceinline__ void gemm1_epilogue(const floatx4_t (&acc)[PC::kFO][4], char* hs,
                                                int64_t og0, int64_t O, const uint16_t* b1,
                                                int act1, int w4, int lane) {
@@ -314,15 +321,22 @@ __device__ __forceinline__ void gemm1_epilogue(const floatx4_t (&acc)[PC::kFO][4
                 else
                     h[r] = colok ? apply_act(act1, acc[fo][fm][r] + bias[r]) : 0.f;
             }
-            uint2 pk = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
-            *reinterpret_cast<uint2*>(hs + slab * kSub + frag_off(16 * fm + li, g) + 2 * e) = pk;
+            const uint2 pk = make_uint2(pack_bf16x2(h[0], h[1]), pack_bf16x2(h[2], h[3]));
+            char* dst = hs + slab * kSub + frag_off(16 * fm + li, g) + 2 * e;
+            *reinterpret_cast<uint2*>(dst) = pk;
+            if constexpr (kHLo) {
+                // h - hi is exact in fp32 (hi is h rounded to 8 significant bits)
+                const uint2 lo = make_uint2(pack_bf16x2(h[0] - bf16_lo(pk.x), h[1] - bf16_hi(pk.x)),
+                                            pack_bf16x2(h[2] - bf16_lo(pk.y), h[3] - bf16_hi(pk.y)));
+                *reinterpret_cast<uint2*>(dst + kLoOff) = lo;
+            }
         }
     }
 }
 
-template <int CA, int CB, bool kGrouped, bool kGated>
+template <int CA, int CB, bool kGrouped, bool kGated, bool kHLo>
 __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a) {
-    using Cfg = FusedCfg<CA, CB, kGated>;
+    using Cfg = FusedCfg<CA, CB, kGated, kHLo>;
     using PA = typename Cfg::PA;
     using PB = typename Cfg::PB;
     static_assert(!(kGrouped && kGated), "the grouped form is not gated");
@@ -473,12 +487,14 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
         {
             floatx4_t acc[PA::kFO][4];
             gemm1_mma<PA>(c, acc);
-            gemm1_epilogue<PA, kGated>(acc, hreg + Cfg::kSlabsB * kSub, o0, O, b1, a.act1, w4, lane);
+            gemm1_epilogue<PA, kGated, kHLo, Cfg::kLoOff>(acc, hreg + Cfg::kSlabsB * kSub, o0, O, b1,
+                                                          a.act1, w4, lane);
         }
         if constexpr (Cfg::kTwoPass) {
             floatx4_t acc[PB::kFO][4];
             gemm1_mma<PB>(c, acc);
-            gemm1_epilogue<PB, kGated>(acc, hreg, o0 + Cfg::kHidA, O, b1, a.act1, w4, lane);
+            gemm1_epilogue<PB, kGated, kHLo, Cfg::kLoOff>(acc, hreg, o0 + Cfg::kHidA, O, b1, a.act1,
+                                                          w4, lane);
         }
     }
     __syncthreads();   // H is complete
@@ -527,9 +543,13 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
         const int kr = (int)(step - pr * Cfg::kKS);
         const int ks = kr + rotk < Cfg::kKS ? kr + rotk : kr + rotk - Cfg::kKS;
         const char* hs = hreg + ks * kSub;
-        uint4 bh[4], wop[4];
+        uint4 bh[4], bl[4], wop[4];
 #pragma unroll
         for (int fm = 0; fm < 4; ++fm) bh[fm] = ld16(hs + frag_off(16 * fm + li, lg));
+        if constexpr (kHLo) {
+#pragma unroll
+            for (int fm = 0; fm < 4; ++fm) bl[fm] = ld16(hs + Cfg::kLoOff + frag_off(16 * fm + li, lg));
+        }
         transpose8x4(R, wop);
         __builtin_amdgcn_sched_barrier(0);
         load2(step + 2, R);
@@ -538,6 +558,12 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
         for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int fm = 0; fm < 4; ++fm) acc2[j][fm] = mfma16x16x32(bh[fm], wop[j], acc2[j][fm]);
+        if constexpr (kHLo) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+#pragma unroll
+                for (int fm = 0; fm < 4; ++fm) acc2[j][fm] = mfma16x16x32(bl[fm], wop[j], acc2[j][fm]);
+        }
     };
 
     float* const part_plane = a.part + (int64_t)s * a.rows_out * P;
@@ -629,10 +655,10 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
     }
 }
 
-template <int CA, int CB, bool G, bool kGated>
+template <int CA, int CB, bool G, bool kGated, bool kHLo = false>
 hipError_t launch_fused_impl(const FusedArgs& a, int64_t units, hipStream_t stream) {
-    using Cfg = FusedCfg<CA, CB, kGated>;
-    auto kern = fused_ffn_bf16_kernel<CA, CB, G, kGated>;
+    using Cfg = FusedCfg<CA, CB, kGated, kHLo>;
+    auto kern = fused_ffn_bf16_kernel<CA, CB, G, kGated, kHLo>;
     static std::atomic<bool> lds_set[kMaxDevices] = {};
     hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), Cfg::kLds, lds_set);
     if (e != hipSuccess) return e;
@@ -704,12 +730,12 @@ hipError_t launch_fused_bf16(const uint16_t* X, const uint16_t* W1, const uint16
     if (chunk == kWideChunk && !grouped)
         return launch_fused_impl<448, 448, false, false>(a, units, stream);
     if (chunk == 448)
-        return grouped ? launch_fused_impl<448, 0, true, false>(a, units, stream)
+        return grouped ? launch_fused_impl<448, 0, true, false, true>(a, units, stream)
                        : launch_fused_impl<448, 0, false, false>(a, units, stream);
     if (chunk == 256)
-        return grouped ? launch_fused_impl<256, 0, true, false>(a, units, stream)
+        return grouped ? launch_fused_impl<256, 0, true, false, true>(a, units, stream)
                        : launch_fused_impl<256, 0, false, false>(a, units, stream);
-    return grouped ? launch_fused_impl<512, 0, true, false>(a, units, stream)
+    return grouped ? launch_fused_impl<512, 0, true, false, true>(a, units, stream)
                    : launch_fused_impl<512, 0, false, false>(a, units, stream);
 }
 
