@@ -49,10 +49,15 @@ int check_dims(int64_t M, int64_t N, int64_t O, int64_t P) {
     const int64_t lim = (int64_t)1 << 31;
     if (M >= lim || N >= lim || O >= lim || P >= lim)
         return fail(FFN_EUNSUPPORTED, "dimensions must be below 2^31");
-    // the kernels address each weight matrix and each 64-row tile of X with
-    // 32-bit byte offsets below 2^31
+    // the kernels address each weight matrix with 32-bit byte offsets below 2^31
     if (N * O >= ((int64_t)1 << 30) || O * P >= ((int64_t)1 << 30))
         return fail(FFN_EUNSUPPORTED, "each weight matrix must hold fewer than 2^30 elements");
+    // ... and a 64-row tile of X (fused kernel) or the up-to-16 rows of X and H
+    // (decode layers, whose K is N or O) the same way: 64 * N * 2 and
+    // 16 * O * 2 bytes below 2^31
+    if (N >= ((int64_t)1 << 24) || O >= ((int64_t)1 << 24))
+        return fail(FFN_EUNSUPPORTED, "N and O must be below 2^24 (got %lld, %lld)", (long long)N,
+                    (long long)O);
     return FFN_OK;
 }
 
