@@ -93,6 +93,29 @@ int ffn_forward_ex(const void* X, const void* W1, const void* b1, const void* W2
                    int dtype, int act1, int act2, int variant, void* workspace,
                    size_t workspace_bytes, void* stream);
 
+/* ---------------------------------------------------------------- no allocation
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): as
+ * ffn_forward_ex, with the workspace taken from a static device array of
+ * FFN_NOALLOC_SCRATCH_BYTES inside the library instead of an argument.  The
+ * call allocates and frees nothing.  Each device holds its own copy of the
+ * array from the library's first call on it until the process ends.
+ *  - A shape whose ffn_workspace_size_ex() exceeds FFN_NOALLOC_SCRATCH_BYTES
+ *    is refused with FFN_EWORKSPACE before any HIP call, outputs untouched.
+ *    16 MiB holds every decode-shaped call (M <= 16) up to 16 x 8192 x 3584 x
+ *    8192 (14.1 MiB) and fused calls with up to 16 MiB of split partials
+ *    (S*M*P*4 bytes: 256 x 4096 x 1792 x 4096 needs exactly 16 MiB).
+ *  - Every call on one device shares that device's array, which keeps the
+ *    last call's contents (nothing in it needs clearing between calls).
+ *    Calls that overlap on one device -- on different streams, from different
+ *    host threads, or from processes sharing the device context -- race on
+ *    it; order them (one stream) or use ffn_forward_ex with a workspace each.
+ *  - Otherwise as ffn_forward_ex: the same kernels, so the same output bits. */
+#define FFN_NOALLOC_SCRATCH_BYTES ((size_t)16 << 20)
+int ffn_forward_noalloc(const void* X, const void* W1, const void* b1, const void* W2,
+                        const void* b2, void* Y, int64_t M, int64_t N, int64_t O, int64_t P,
+                        int dtype, int act1, int act2, int variant, void* stream);
+
 /* As ffn_forward_ex, and records caller-created HIP events (hipEvent_t cast
  * to void*) on `stream` around the path's kernels, for per-kernel timing:
  * events[0] before the first kernel, events[1] between the first (the fused

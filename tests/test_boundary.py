@@ -242,3 +242,25 @@ def test_workspace_follows_the_split_count():
     # the GPU parity case of the two-pass form (4090 rows, 7168 hidden): 8 splits, not 16
     two = ffn.ffn_workspace_size(4090, 136, 7168, 1032)
     assert 8 * 4090 * 1032 * 4 <= two < 9 * 4090 * 1032 * 4
+
+
+def test_noalloc_refuses_shapes_beyond_its_scratch_on_the_host():
+    """The size check of ffn_forward_noalloc runs before any HIP call (no GPU here)."""
+    L = ffn.lib()
+    M, N, O, P = 4096, 4096, 1792, 4096     # 256 MiB of split partials
+    assert ffn.ffn_workspace_size(M, N, O, P) > ffn.NOALLOC_SCRATCH_BYTES
+    rc = L.ffn_forward_noalloc(FAKE, FAKE, None, FAKE, None, FAKE2, M, N, O, P, ffn.BF16, 2, 0, 0,
+                               None)
+    assert rc == E_WS, (rc, ffn.ffn_last_error())
+    assert "static scratch" in ffn.ffn_last_error()
+
+
+def test_noalloc_scratch_size_matches_the_header_and_its_stated_shapes():
+    text = open(HEADER).read()
+    m = re.search(r"#define FFN_NOALLOC_SCRATCH_BYTES \(\(size_t\)(\d+) << 20\)", text)
+    assert m and int(m.group(1)) << 20 == ffn.NOALLOC_SCRATCH_BYTES
+    ws = ffn.ffn_workspace_size
+    assert ws(16, 4096, 1792, 4096) <= ffn.NOALLOC_SCRATCH_BYTES      # the decode shard
+    assert ws(16, 8192, 3584, 8192) <= ffn.NOALLOC_SCRATCH_BYTES      # stated in the header
+    assert ws(256, 4096, 1792, 4096) <= ffn.NOALLOC_SCRATCH_BYTES     # stated in the header
+    assert ws(257, 4096, 1792, 4096) > ffn.NOALLOC_SCRATCH_BYTES

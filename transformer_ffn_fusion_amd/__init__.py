@@ -19,6 +19,7 @@ __all__ = [
     "F32", "BF16", "ACT_NONE", "ACT_RELU", "ACT_GELU_TANH",
     "VARIANT_AUTO", "VARIANT_FUSED", "VARIANT_SKINNY", "VARIANT_F32",
     "FFNError", "lib", "lib_path", "ffn_workspace_size", "ffn_forward", "ffn_forward_ex",
+    "ffn_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
     "moe_workspace_size", "moe_route", "moe_ffn_forward", "ffn_last_error", "workspace",
 ]
 
@@ -26,6 +27,7 @@ F32, BF16 = 0, 1
 ACT_NONE, ACT_RELU, ACT_GELU_TANH = 0, 1, 2
 VARIANT_AUTO, VARIANT_FUSED, VARIANT_SKINNY, VARIANT_F32 = 0, 1, 2, 3
 ACTS = {"none": ACT_NONE, "relu": ACT_RELU, "gelu_tanh": ACT_GELU_TANH}
+NOALLOC_SCRATCH_BYTES = 16 << 20   # FFN_NOALLOC_SCRATCH_BYTES in include/ffn.h
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
 lib_path = os.path.join(_PKG, "libffn.so")
@@ -55,6 +57,9 @@ def lib():
         L.ffn_forward_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, i32,
                                      vp, sz, vp]
         L.ffn_forward_ex.restype = i32
+        L.ffn_forward_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32,
+                                          i32, i32, vp]
+        L.ffn_forward_noalloc.restype = i32
         L.moe_workspace_size.argtypes = [i64, i64, i32, i64, i64, i64, i32]
         L.moe_workspace_size.restype = sz
         L.moe_route.argtypes = [vp, i64, i64, i32, vp, vp, vp, vp, vp, sz, vp]
@@ -208,12 +213,8 @@ def workspace(nbytes: int, device="cuda"):
     return torch.zeros(max(int(nbytes), 256), dtype=torch.uint8, device=device)
 
 
-def ffn_forward_ex(X, W1, b1, W2, b2, Y, act1="gelu_tanh", act2="none", variant=VARIANT_AUTO,
-                   ws=None, stream=None):
-    """``Y = act2(act1(X W1 + b1) W2 + b2)`` on the GPU; ``Y`` is written in place.
-
-    ``ws`` is a zero-initialised uint8 device tensor of at least
-    ``ffn_workspace_size(...)`` bytes (allocated here when None)."""
+def _dense_args(X, W1, b1, W2, b2, Y, ws=None):
+    """Checks the dense call's tensors; returns M, N, O, P and the dtype code."""
     M, N = _dims(X, "X", 2)
     O = _dims(W1, "W1", 2)[1]
     P = _dims(W2, "W2", 2)[1]
@@ -227,6 +228,27 @@ def ffn_forward_ex(X, W1, b1, W2, b2, Y, act1="gelu_tanh", act2="none", variant=
     _arg(Y, "Y", (M, P), tdt)
     _ws_arg(ws)
     _on_device(X, W1, b1, W2, b2, Y, ws)
+    return M, N, O, P, dt
+
+
+def ffn_forward_noalloc(X, W1, b1, W2, b2, Y, act1="gelu_tanh", act2="none",
+                        variant=VARIANT_AUTO, stream=None):
+    """As ``ffn_forward_ex`` with the library's static device scratch as the workspace:
+    nothing is allocated (the shape's workspace must fit FFN_NOALLOC_SCRATCH_BYTES)."""
+    M, N, O, P, dt = _dense_args(X, W1, b1, W2, b2, Y)
+    _check(lib().ffn_forward_noalloc(_ptr(X), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), _ptr(Y),
+                                     M, N, O, P, dt, _act(act1), _act(act2), int(variant),
+                                     _stream(stream)))
+    return Y
+
+
+def ffn_forward_ex(X, W1, b1, W2, b2, Y, act1="gelu_tanh", act2="none", variant=VARIANT_AUTO,
+                   ws=None, stream=None):
+    """``Y = act2(act1(X W1 + b1) W2 + b2)`` on the GPU; ``Y`` is written in place.
+
+    ``ws`` is a zero-initialised uint8 device tensor of at least
+    ``ffn_workspace_size(...)`` bytes (allocated here when None)."""
+    M, N, O, P, dt = _dense_args(X, W1, b1, W2, b2, Y, ws)
     if ws is None:
         ws = workspace(ffn_workspace_size(M, N, O, P, dt, variant), X.device)
     _check(lib().ffn_forward_ex(_ptr(X), _ptr(W1), _ptr(b1), _ptr(W2), _ptr(b2), _ptr(Y),

@@ -199,6 +199,16 @@ int launched(hipError_t e, const char* what) {
 
 }  // namespace
 
+namespace ffn {
+int set_error(int code, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return code;
+}
+}  // namespace ffn
+
 extern "C" {
 
 int ffn_version(void) { return 100; }

@@ -28,6 +28,9 @@ inline hipError_t set_dynamic_lds(const void* kern, int bytes,
     return e;
 }
 
+// Sets the calling thread's error text (ffn_last_error) and returns `code`.
+int set_error(int code, const char* fmt, ...);
+
 // Compute units of the current device (queried once per device; 256 if the
 // query fails).
 inline int device_cus() {
