@@ -68,6 +68,8 @@ def test_fused_shapes(shape):
     (16, 4096, 1792, 4096),
     (16, 1024, 3584, 512),
     (9, 8192, 256, 1024),
+    (7, 520, 1000, 2056),     # layer 2 over the whole K: K tail inside a step, ragged last block
+    (16, 256, 2048, 2048),    # layer 2 over the whole K in two load batches
 ])
 def test_skinny_shapes(shape):
     M, N, O, P = shape
