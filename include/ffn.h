@@ -104,7 +104,7 @@ int ffn_forward_ex(const void* X, const void* W1, const void* b1, const void* W2
  *    is refused with FFN_EWORKSPACE before any HIP call, outputs untouched.
  *    16 MiB holds every decode-shaped call (M <= 16) up to 16 x 8192 x 3584 x
  *    8192 (14.1 MiB) and fused calls with up to 16 MiB of split partials
- *    (S*M*P*4 bytes: 256 x 4096 x 1792 x 4096 needs exactly 16 MiB).
+ *    (S*M*P*3 bytes: up to 341 rows at 4096 x 1792 x 4096).
  *  - Every call on one device shares that device's array, which keeps the
  *    last call's contents (nothing in it needs clearing between calls).
  *    Calls that overlap on one device -- on different streams, from different

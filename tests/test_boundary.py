@@ -80,7 +80,7 @@ def test_forward_rejects(kw, code):
 
 def test_workspace_one_byte_short_is_rejected():
     need = ffn.ffn_workspace_size(4096, 4096, 1792, 4096)
-    assert need >= 4 * 4096 * 4096 * 4          # four fp32 split partials of Y
+    assert need >= 4 * 4096 * 4096 * 3          # four packed (3-byte) split partials of Y
     assert _fwd(M=4096, N=4096, O=1792, P=4096, wsb=need - 1) == E_WS
     skinny = ffn.ffn_workspace_size(16, 4096, 1792, 4096)
     assert 0 < skinny < need
@@ -126,13 +126,13 @@ def test_swiglu_rejects(kw, code):
 def test_swiglu_workspace_sizes():
     S = ffn.ffn_swiglu_workspace_size
     fused = S(4096, 4096, 1792, 4096)
-    assert fused >= 4 * 4096 * 4096 * 4         # four 448-column hidden chunks of fp32 partials
+    assert fused >= 4 * 4096 * 4096 * 3         # four 448-column hidden chunks of packed partials
     assert _swiglu(M=4096, N=4096, O=1792, P=4096, wsb=fused - 1) == E_WS
     dec = S(16, 4096, 1792, 4096)
     assert 0 < dec < fused
     assert _swiglu(M=16, N=4096, O=1792, P=4096, wsb=dec - 1) == E_WS
-    assert S(16, 4096, 1792, 4096, ffn.BF16, ffn.VARIANT_FUSED) == 4 * 16 * 4096 * 4
-    assert S(16, 4096, 2048, 4096, ffn.BF16, ffn.VARIANT_FUSED) == 8 * 16 * 4096 * 4  # 256-wide
+    assert S(16, 4096, 1792, 4096, ffn.BF16, ffn.VARIANT_FUSED) == 4 * 16 * 4096 * 3
+    assert S(16, 4096, 2048, 4096, ffn.BF16, ffn.VARIANT_FUSED) == 8 * 16 * 4096 * 3  # 256-wide
     assert S(4, 4, 448, 64) == 0
     assert S(4, 64, 448, 64, 5) == 0
 
@@ -232,22 +232,22 @@ def test_ceiling_entry_points_reject_before_launch():
 
 
 def test_workspace_follows_the_split_count():
-    """The dense fused form's workspace holds the fp32 partials of its splits:
+    """The dense fused form's workspace holds the packed (3-byte) partials of its splits:
     448-wide chunks at the prefill shard (4 splits), 896-wide two-pass chunks at
     the large shard (4 splits instead of 8), from the shape alone (no device)."""
     pre = ffn.ffn_workspace_size(4096, 4096, 1792, 4096)
-    assert 4 * 4096 * 4096 * 4 <= pre < 5 * 4096 * 4096 * 4
+    assert 4 * 4096 * 4096 * 3 <= pre < 5 * 4096 * 4096 * 3
     big = ffn.ffn_workspace_size(8192, 8192, 3584, 8192)
-    assert 4 * 8192 * 8192 * 4 <= big < 5 * 8192 * 8192 * 4
+    assert 4 * 8192 * 8192 * 3 <= big < 5 * 8192 * 8192 * 3
     # the GPU parity case of the two-pass form (4090 rows, 7168 hidden): 8 splits, not 16
     two = ffn.ffn_workspace_size(4090, 136, 7168, 1032)
-    assert 8 * 4090 * 1032 * 4 <= two < 9 * 4090 * 1032 * 4
+    assert 8 * 4090 * 1032 * 3 <= two < 9 * 4090 * 1032 * 3
 
 
 def test_noalloc_refuses_shapes_beyond_its_scratch_on_the_host():
     """The size check of ffn_forward_noalloc runs before any HIP call (no GPU here)."""
     L = ffn.lib()
-    M, N, O, P = 4096, 4096, 1792, 4096     # 256 MiB of split partials
+    M, N, O, P = 4096, 4096, 1792, 4096     # 192 MiB of split partials
     assert ffn.ffn_workspace_size(M, N, O, P) > ffn.NOALLOC_SCRATCH_BYTES
     rc = L.ffn_forward_noalloc(FAKE, FAKE, None, FAKE, None, FAKE2, M, N, O, P, ffn.BF16, 2, 0, 0,
                                None)
@@ -262,5 +262,5 @@ def test_noalloc_scratch_size_matches_the_header_and_its_stated_shapes():
     ws = ffn.ffn_workspace_size
     assert ws(16, 4096, 1792, 4096) <= ffn.NOALLOC_SCRATCH_BYTES      # the decode shard
     assert ws(16, 8192, 3584, 8192) <= ffn.NOALLOC_SCRATCH_BYTES      # stated in the header
-    assert ws(256, 4096, 1792, 4096) <= ffn.NOALLOC_SCRATCH_BYTES     # stated in the header
-    assert ws(257, 4096, 1792, 4096) > ffn.NOALLOC_SCRATCH_BYTES
+    assert ws(341, 4096, 1792, 4096) <= ffn.NOALLOC_SCRATCH_BYTES     # stated in the header
+    assert ws(342, 4096, 1792, 4096) > ffn.NOALLOC_SCRATCH_BYTES

@@ -59,7 +59,7 @@ def test_noalloc_matches_workspace_call(pair):
 
 def test_noalloc_refuses_oversized_shape_and_leaves_output_untouched():
     import torch
-    M, N, O, P = 4096, 64, 1792, 512     # 32 MiB of split partials
+    M, N, O, P = 4096, 64, 1792, 512     # 24 MiB of split partials
     assert ffn.ffn_workspace_size(M, N, O, P) > ffn.NOALLOC_SCRATCH_BYTES
     X, W1, b1, W2, b2 = (dev_bf16(a) for a in synth.dense_inputs(M, N, O, P, seed=6))
     Y = torch.full((M, P), 7.0, dtype=torch.bfloat16, device="cuda")

@@ -71,7 +71,7 @@ int resolve_variant(int variant, int dtype, int64_t M) {
 
 // ---- dense workspace layouts (byte offsets, each region 256-byte aligned)
 struct DenseLayout {
-    size_t part = 0;       // fused / f32: fp32 partials
+    size_t part = 0;       // fused: packed partials; f32: fp32 partials
     size_t part1 = 0, h = 0, part2 = 0;
     size_t total = 0;
 };
@@ -82,7 +82,7 @@ DenseLayout dense_layout(int64_t M, int64_t N, int64_t O, int64_t P, int variant
         const int chunk = ffn::fused_pick_dense_chunk(M, O);
         const int S = ffn::fused_num_splits(O, chunk);
         L.part = 0;
-        L.total = align_up((size_t)S * M * P * sizeof(float));
+        L.total = align_up((size_t)S * M * P * ffn::kPartBytes);
     } else if (variant == FFN_VARIANT_F32) {
         const int64_t S = (O + ffn::kF32Chunk - 1) / ffn::kF32Chunk;
         L.total = align_up((size_t)S * M * P * sizeof(float));
@@ -102,7 +102,7 @@ DenseLayout dense_layout(int64_t M, int64_t N, int64_t O, int64_t P, int variant
 
 // ---- SwiGLU workspace layouts
 struct SwigluLayout {
-    size_t part = 0;                          // fused / f32: fp32 partials
+    size_t part = 0;                          // fused: packed partials; f32: fp32 partials
     size_t part_g = 0, part_u = 0, h = 0, part2 = 0;  // skinny
     size_t total = 0;
 };
@@ -110,7 +110,7 @@ struct SwigluLayout {
 SwigluLayout swiglu_layout(int64_t M, int64_t N, int64_t O, int64_t P, int variant) {
     SwigluLayout L;
     if (variant == FFN_VARIANT_FUSED) {
-        L.total = align_up((size_t)ffn::fused_swiglu_splits(O) * M * P * sizeof(float));
+        L.total = align_up((size_t)ffn::fused_swiglu_splits(O) * M * P * ffn::kPartBytes);
     } else if (variant == FFN_VARIANT_F32) {
         const int64_t S = (O + ffn::kF32Chunk - 1) / ffn::kF32Chunk;
         L.total = align_up((size_t)S * M * P * sizeof(float));
@@ -172,7 +172,7 @@ MoeLayout moe_layout(int64_t M, int64_t E, int k, int64_t O, int64_t P) {
     // block histograms sized for the router form's 16-token blocks (the most blocks)
     L.blk_counts = off; off += align_up(sizeof(int32_t) * E * ffn::moe_route_blocks_a(M, E, true));
     L.blk_base = off;   off += align_up(sizeof(int32_t) * E * ffn::moe_route_blocks_b(M));
-    L.part = off;       off += align_up(sizeof(float) * (size_t)L.splits * mk * P);
+    L.part = off;       off += align_up((size_t)ffn::kPartBytes * L.splits * mk * P);
     L.total = off;
     return L;
 }
@@ -266,7 +266,7 @@ static int dense_forward(const void* X, const void* W1, const void* b1, const vo
     if (v == FFN_VARIANT_FUSED) {
         const int chunk = ffn::fused_pick_dense_chunk(M, O);
         const int S = ffn::fused_num_splits(O, chunk);
-        float* part = reinterpret_cast<float*>(ws + L.part);
+        char* part = ws + L.part;
         const int64_t rbs = (M + ffn::kBM - 1) / ffn::kBM;
         rc = launched(ffn::launch_fused_bf16((const uint16_t*)X, (const uint16_t*)W1,
                                              (const uint16_t*)b1, (const uint16_t*)W2, part, M,
@@ -458,7 +458,7 @@ static int swiglu_forward(const void* X, const void* Wg, const void* Wu, const v
     char* ws = static_cast<char*>(workspace);
     if ((rc = mark(events, n_events, 0, st))) return rc;
     if (v == FFN_VARIANT_FUSED) {
-        float* part = reinterpret_cast<float*>(ws + L.part);
+        char* part = ws + L.part;   // packed partials
         rc = launched(ffn::launch_fused_swiglu_bf16((const uint16_t*)X, (const uint16_t*)Wg,
                                                     (const uint16_t*)Wu, (const uint16_t*)Wd, part,
                                                     M, N, O, P, st),
@@ -668,7 +668,7 @@ static int moe_forward(const void* X, const float* logits, const void* Wr, const
     g.w2_stride = O * P;
     g.b1_stride = O;
     const int64_t row_blocks = (L.max_tiles + 7) / 8 * 8;
-    float* part = reinterpret_cast<float*>(ws + L.part);
+    char* part = ws + L.part;   // packed partials
     rc = launched(ffn::launch_fused_bf16((const uint16_t*)X, (const uint16_t*)W1,
                                          (const uint16_t*)b1, (const uint16_t*)W2, part, M, N, O,
                                          P, act1, L.chunk, row_blocks, M * k, &g, st),

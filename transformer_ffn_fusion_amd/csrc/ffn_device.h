@@ -68,6 +68,44 @@ __device__ __forceinline__ float apply_act(int act, float x) {
     return x;
 }
 
+// ---------------------------------------------------------------- split partials
+//
+// The fp32 partial sums of Y that the split-O kernels hand to their ordered
+// reduction are stored with a 16-bit significand: the upper three bytes of
+// the fp32 pattern (the low byte is dropped, i.e. rounded toward zero).  That
+// moves a partial by less than 2^-15 of its magnitude -- far below the one
+// bf16 rounding of Y that follows -- and cuts the partial traffic, written and
+// read back through HBM or the memory-side cache, by a quarter.  Infinities
+// and NaNs stay non-finite.  Four values pack into three dwords:
+// w0 = a | b << 24, w1 = b >> 8 | c << 16, w2 = c >> 16 | d << 8 (a..d the
+// 24-bit codes), formed with funnel shifts straight from the fp32 patterns.
+// (Rounding to nearest instead measured 1.5 us slower on the prefill kernel,
+// and 10 us slower with a NaN guard: the packing runs inside the second
+// product's loop.)
+__device__ __forceinline__ float f24_value(uint32_t code) { return __uint_as_float(code << 8); }
+
+__device__ __forceinline__ void pack_f24x4(float a, float b, float c, float d, uint32_t (&w)[3]) {
+    const uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+    const uint32_t uc = __float_as_uint(c), ud = __float_as_uint(d);
+    w[0] = __builtin_amdgcn_alignbit(ub >> 8, ua, 8);    // a >> 8 | (b >> 8) << 24
+    w[1] = __builtin_amdgcn_alignbit(uc >> 8, ub, 16);   // b >> 16 | (c >> 8) << 16
+    w[2] = __builtin_amdgcn_alignbit(ud >> 8, uc, 24);   // c >> 24 | (d >> 8) << 8
+}
+__device__ __forceinline__ void unpack_f24x4(uint32_t w0, uint32_t w1, uint32_t w2, float* v) {
+    v[0] = f24_value(w0 & 0xffffffu);
+    v[1] = f24_value((w0 >> 24) | ((w1 & 0xffffu) << 8));
+    v[2] = f24_value((w1 >> 16) | ((w2 & 0xffu) << 16));
+    v[3] = f24_value(w2 >> 8);
+}
+// Eight consecutive packed values (24 bytes, 8-byte aligned) -> floats.
+__device__ __forceinline__ void load_f24x8(const char* src, float (&v)[8]) {
+    const uint2 a = *reinterpret_cast<const uint2*>(src);
+    const uint2 b = *reinterpret_cast<const uint2*>(src + 8);
+    const uint2 c = *reinterpret_cast<const uint2*>(src + 16);
+    unpack_f24x4(a.x, a.y, b.x, v);
+    unpack_f24x4(b.y, c.x, c.y, v + 4);
+}
+
 // ---------------------------------------------------------------- MFMA
 
 __device__ __forceinline__ floatx4_t mfma16x16x32(const uint4& a, const uint4& b, floatx4_t c) {

@@ -14,7 +14,8 @@
 //    epilogue adds b1, applies the activation, rounds once to bf16 and writes
 //    the 64 x C tile of H into LDS in the operand layout GEMM2 reads;
 //  * GEMM2 sweeps the output columns in passes of 512, reading H from LDS and
-//    streaming W2; each pass stores an fp32 partial of Y for this hidden chunk
+//    streaming W2; each pass stores a partial of Y for this hidden chunk
+//    (fp32 sums cut to a 16-bit significand: three bytes each)
 //    (split-O).  A separate pass sums the chunks in ascending order, adds b2
 //    once (the tensor-parallel equation: the bias is added after the sum) and
 //    casts.  No floating-point atomics: results are bitwise reproducible.
@@ -105,7 +106,7 @@ struct FusedArgs {
     const uint16_t* W1u;  // gated form: the up matrix Wu (unused otherwise)
     const uint16_t* b1;
     const uint16_t* W2;
-    float* part;
+    char* part;           // packed partials, kPartBytes each: [splits][rows_out][P]
     int64_t M, N, O, P;
     int64_t rows_out;     // rows of each split in `part`
     int64_t row_blocks;   // row tiles used for the unit mapping
@@ -113,6 +114,7 @@ struct FusedArgs {
     int act1;
     int cus;              // compute units of the device (grouped form: tail splitting)
     bool part_wt;         // partials written through to the memory-side cache (sc1)
+    bool part_rsrc;       // a split's plane is below 2^31 bytes (32-bit buffer offsets)
     GroupedRows g;
 };
 
@@ -130,7 +132,8 @@ constexpr int64_t kPassWindow = 4;        // pass rotation window when W2's bloc
 constexpr int kWideChunk = 896;           // dense two-pass chunk: 448 + 448 hidden columns
 constexpr int64_t kRoundUnits = 256;      // workgroups in one round on MI355X (one per CU)
 constexpr int kCpolSc1 = 16;   // buffer cache-policy bits: sc1 (device scope)
-typedef unsigned uint32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kCpolNt = 2;     // ... nt (streaming)
+typedef unsigned uint32x3_t __attribute__((ext_vector_type(3)));
 
 // Unit -> (row tile, hidden chunk).  Workgroups are dispatched round-robin
 // over the 8 XCDs (unit u runs on XCD u % 8), and each XCD has its own L2.
@@ -566,9 +569,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
         }
     };
 
-    float* const part_plane = a.part + (int64_t)s * a.rows_out * P;
-    float* const part = part_plane + (row0 + 4 * lg) * P + 64 * wc + 4 * li;
-    const __amdgpu_buffer_rsrc_t rpart = make_rsrc(part_plane, a.rows_out * P * 4);
+    char* const part_plane = a.part + (int64_t)s * a.rows_out * P * kPartBytes;
+    const int64_t part_lane = ((row0 + 4 * lg) * P + 64 * wc + 4 * li) * kPartBytes;
+    const __amdgpu_buffer_rsrc_t rpart = make_rsrc(part_plane, a.rows_out * P * kPartBytes);
     uint2 RA[8], RB[8];
     load2(0, RA);
     load2(1, RB);   // the stage count is even
@@ -585,14 +588,21 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
 #pragma unroll
                 for (int r = 0; r < 4; ++r) {
                     if (16 * fm + 4 * lg + r >= valid) continue;
-                    const floatx4_t v{acc2[0][fm][r], acc2[1][fm][r], acc2[2][fm][r], acc2[3][fm][r]};
-                    const int64_t o = (int64_t)(16 * fm + r) * P + pt * kBN2;
-                    if (a.part_wt)   // offsets below 2^31 bytes (checked at launch)
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            __builtin_bit_cast(uint32x4_t, v), rpart,
-                            (uint32_t)((part - part_plane + o) * 4), 0, kCpolSc1);
-                    else   // streaming: read once, by the reduction
-                        __builtin_nontemporal_store(v, reinterpret_cast<floatx4_t*>(part + o));
+                    uint32_t w[3];
+                    pack_f24x4(acc2[0][fm][r], acc2[1][fm][r], acc2[2][fm][r], acc2[3][fm][r], w);
+                    const int64_t o = part_lane + ((int64_t)(16 * fm + r) * P + pt * kBN2) * kPartBytes;
+                    if (a.part_wt)   // written through to the MALL
+                        __builtin_amdgcn_raw_buffer_store_b96(uint32x3_t{w[0], w[1], w[2]}, rpart,
+                                                              (uint32_t)o, 0, kCpolSc1);
+                    else if (a.part_rsrc)   // streamed: read once, by the reduction
+                        __builtin_amdgcn_raw_buffer_store_b96(uint32x3_t{w[0], w[1], w[2]}, rpart,
+                                                              (uint32_t)o, 0, kCpolNt);
+                    else {   // a plane past 2^31 bytes: 64-bit addresses, streamed
+                        uint32_t* d = reinterpret_cast<uint32_t*>(part_plane + o);
+                        __builtin_nontemporal_store(w[0], d);
+                        __builtin_nontemporal_store(w[1], d + 1);
+                        __builtin_nontemporal_store(w[2], d + 2);
+                    }
                 }
         }
 #pragma unroll
@@ -604,8 +614,10 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
 
 // ---------------------------------------------------------------- reduce
 
+// kYF32: fp32 output from fp32 partials (the fp32 path); otherwise bf16 output
+// from packed partials (kPartBytes each).
 template <bool kYF32, bool kBF32>
-__global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restrict__ part,
+__global__ __launch_bounds__(256) void reduce_splits_kernel(const void* __restrict__ part,
                                                             int splits, const void* b2,
                                                             void* Y, int64_t M, int64_t P,
                                                             int act2) {
@@ -615,17 +627,30 @@ __global__ __launch_bounds__(256) void reduce_splits_kernel(const float* __restr
          v += (int64_t)gridDim.x * blockDim.x) {
         const int64_t m = v / (P / 8);
         const int64_t p = (v - m * (P / 8)) * 8;
-        const float* src = part + m * P + p;
-        float4 lo = *reinterpret_cast<const float4*>(src);
-        float4 hi = *reinterpret_cast<const float4*>(src + 4);
-        for (int s = 1; s < splits; ++s) {
-            const float* q = src + s * split_stride;
-            float4 a = *reinterpret_cast<const float4*>(q);
-            float4 b = *reinterpret_cast<const float4*>(q + 4);
-            lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
-            hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
+        float y[8];
+        if constexpr (kYF32) {
+            const float* src = reinterpret_cast<const float*>(part) + m * P + p;
+            float4 lo = *reinterpret_cast<const float4*>(src);
+            float4 hi = *reinterpret_cast<const float4*>(src + 4);
+            for (int s = 1; s < splits; ++s) {
+                const float* q = src + s * split_stride;
+                float4 a = *reinterpret_cast<const float4*>(q);
+                float4 b = *reinterpret_cast<const float4*>(q + 4);
+                lo.x += a.x; lo.y += a.y; lo.z += a.z; lo.w += a.w;
+                hi.x += b.x; hi.y += b.y; hi.z += b.z; hi.w += b.w;
+            }
+            y[0] = lo.x; y[1] = lo.y; y[2] = lo.z; y[3] = lo.w;
+            y[4] = hi.x; y[5] = hi.y; y[6] = hi.z; y[7] = hi.w;
+        } else {
+            const char* src = reinterpret_cast<const char*>(part) + (m * P + p) * kPartBytes;
+            load_f24x8(src, y);
+            for (int s = 1; s < splits; ++s) {
+                float t[8];
+                load_f24x8(src + s * split_stride * kPartBytes, t);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) y[i] += t[i];
+            }
         }
-        float y[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
         if (b2) {
             if constexpr (kBF32) {
                 const float* bb = reinterpret_cast<const float*>(b2) + p;
@@ -665,9 +690,10 @@ hipError_t launch_fused_impl(const FusedArgs& a, int64_t units, hipStream_t stre
     // grouped form: workgroups for the pieces of a short last round (at most
     // cus, plus up to 7 x 8 for the XCD-aligned numbering of the pieces)
     const int64_t grid = units + (G ? a.cus + 64 : 0);
-    const int64_t part_bytes = (int64_t)a.splits * a.rows_out * a.P * 4;
+    const int64_t plane_bytes = a.rows_out * a.P * kPartBytes;
     FusedArgs b = a;
-    b.part_wt = part_bytes <= kMallBytes && a.rows_out * a.P * 4 < (1ll << 31);
+    b.part_rsrc = plane_bytes < (1ll << 31);
+    b.part_wt = b.part_rsrc && (int64_t)a.splits * plane_bytes <= kMallBytes;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), Cfg::kLds, stream, b);
     return hipGetLastError();
 }
@@ -691,7 +717,7 @@ int fused_num_splits(int64_t O, int chunk) { return (int)((O + chunk - 1) / chun
 // Dense form: where 896 hidden columns divide O into a split count that
 // divides 8 and the units fill two or more whole rounds of MI355X's 256 CUs,
 // each workgroup covers 896 columns in two 448-column first-product passes:
-// fewer splits, and fewer fp32 partials written and reduced, than any
+// fewer splits, and fewer partials written and reduced, than any
 // single-pass chunk (large shard, 8192 rows x 3584 hidden: 8 splits and 1024
 // units of 448 become 4 splits and 512 units).  The rule depends on the shape
 // only, so the workspace size is known without a device.
@@ -705,7 +731,7 @@ int fused_pick_dense_chunk(int64_t M, int64_t O) {
 }
 
 hipError_t launch_fused_bf16(const uint16_t* X, const uint16_t* W1, const uint16_t* b1,
-                             const uint16_t* W2, float* part, int64_t M, int64_t N, int64_t O,
+                             const uint16_t* W2, void* part, int64_t M, int64_t N, int64_t O,
                              int64_t P, int act1, int chunk, int64_t row_blocks,
                              int64_t rows_out, const GroupedRows* grouped, hipStream_t stream) {
     FusedArgs a;
@@ -714,7 +740,7 @@ hipError_t launch_fused_bf16(const uint16_t* X, const uint16_t* W1, const uint16
     a.W1u = nullptr;
     a.b1 = b1;
     a.W2 = W2;
-    a.part = part;
+    a.part = static_cast<char*>(part);
     a.M = M;
     a.N = N;
     a.O = O;
@@ -757,7 +783,7 @@ int fused_swiglu_splits(int64_t O) {
 }
 
 hipError_t launch_fused_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
-                                    const uint16_t* Wd, float* part, int64_t M, int64_t N,
+                                    const uint16_t* Wd, void* part, int64_t M, int64_t N,
                                     int64_t O, int64_t P, hipStream_t stream) {
     FusedArgs a;
     a.X = X;
@@ -765,7 +791,7 @@ hipError_t launch_fused_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, const
     a.W1u = Wu;
     a.b1 = nullptr;
     a.W2 = Wd;
-    a.part = part;
+    a.part = static_cast<char*>(part);
     a.M = M;
     a.N = N;
     a.O = O;
@@ -782,7 +808,7 @@ hipError_t launch_fused_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, const
     return launch_fused_impl<512, 0, false, true>(a, units, stream);
 }
 
-hipError_t launch_reduce_splits(const float* part, int splits, const void* b2, int b2_f32,
+hipError_t launch_reduce_splits(const void* part, int splits, const void* b2, int b2_f32,
                                 void* Y, int y_f32, int64_t M, int64_t P, int act2,
                                 hipStream_t stream) {
     const int64_t nvec = M * (P / 8);

@@ -48,6 +48,7 @@ inline int device_cus() {
 
 // ---- fused bf16 FFN with H kept in LDS (prefill shapes and the MoE groups)
 
+constexpr int kPartBytes = 3;   // bytes of one packed split partial (16-bit significand)
 constexpr int kBM = 64;     // token rows per workgroup tile
 constexpr int kBN2 = 512;   // output columns per second-layer pass
 
@@ -64,9 +65,10 @@ struct GroupedRows {
     int64_t w1_stride = 0, w2_stride = 0, b1_stride = 0;  // per expert, in elements
 };
 
-// Writes fp32 partial outputs part[s][row][p] (s < splits) for rows < rows_out.
+// Writes packed partial outputs part[s][row][p] (kPartBytes each, s < splits)
+// for rows < rows_out.
 hipError_t launch_fused_bf16(const uint16_t* X, const uint16_t* W1, const uint16_t* b1,
-                             const uint16_t* W2, float* part, int64_t M, int64_t N,
+                             const uint16_t* W2, void* part, int64_t M, int64_t N,
                              int64_t O, int64_t P, int act1, int chunk, int64_t row_blocks,
                              int64_t rows_out, const GroupedRows* grouped, hipStream_t stream);
 
@@ -75,11 +77,13 @@ hipError_t launch_fused_bf16(const uint16_t* X, const uint16_t* W1, const uint16
 int fused_swiglu_hid(int64_t O);                 // 448 or 256
 int fused_swiglu_splits(int64_t O);              // ceil(O / fused_swiglu_hid(O))
 hipError_t launch_fused_swiglu_bf16(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
-                                    const uint16_t* Wd, float* part, int64_t M, int64_t N,
+                                    const uint16_t* Wd, void* part, int64_t M, int64_t N,
                                     int64_t O, int64_t P, hipStream_t stream);
 
 // Y[m][p] = act2(sum_s part[s][m][p] + b2[p]) in ascending s; bf16 or fp32 out.
-hipError_t launch_reduce_splits(const float* part, int splits, const void* b2, int b2_f32,
+// The partials are packed (kPartBytes) with a bf16 output, fp32 with an fp32
+// output (the fp32 path).
+hipError_t launch_reduce_splits(const void* part, int splits, const void* b2, int b2_f32,
                                 void* Y, int y_f32, int64_t M, int64_t P, int act2,
                                 hipStream_t stream);
 
@@ -142,7 +146,7 @@ struct RouteIO {
 int64_t moe_route_blocks_a(int64_t M, int64_t E, bool router);
 int64_t moe_route_blocks_b(int64_t M);
 hipError_t launch_moe_route(const RouteIO& io, hipStream_t stream);
-hipError_t launch_moe_combine(const float* part, int splits, int64_t rows_total,
+hipError_t launch_moe_combine(const void* part, int splits, int64_t rows_total,
                               const int32_t* pos, const int32_t* ids, const float* w,
                               const uint16_t* b2, uint16_t* Y, int64_t M, int k, int64_t P,
                               int act2, hipStream_t stream);

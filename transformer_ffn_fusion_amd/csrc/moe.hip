@@ -337,7 +337,7 @@ __global__ __launch_bounds__(kScatterTokens) void moe_scatter_kernel(
 }
 
 __global__ __launch_bounds__(256) void moe_combine_kernel(
-    const float* __restrict__ part, int splits, int64_t rows_total, const int32_t* __restrict__ pos,
+    const char* __restrict__ part, int splits, int64_t rows_total, const int32_t* __restrict__ pos,
     const int32_t* __restrict__ ids, const float* __restrict__ w, const uint16_t* __restrict__ b2,
     uint16_t* __restrict__ Y, int64_t M, int k, int64_t P, int act2) {
     const int64_t nvec = M * (P / 8);
@@ -351,16 +351,15 @@ __global__ __launch_bounds__(256) void moe_combine_kernel(
             const int64_t r = pos[t * k + j];
             const int64_t e = ids[t * k + j];
             const float wt = w[t * k + j];
-            const float* src = part + r * P + p;
-            float4 lo = *reinterpret_cast<const float4*>(src);
-            float4 hi = *reinterpret_cast<const float4*>(src + 4);
-            float z[8] = {lo.x, lo.y, lo.z, lo.w, hi.x, hi.y, hi.z, hi.w};
+            // packed partials (kPartBytes each), splits summed in ascending order
+            const char* src = part + (r * P + p) * kPartBytes;
+            float z[8];
+            load_f24x8(src, z);
             for (int s = 1; s < splits; ++s) {
-                const float* q = src + s * split_stride;
-                lo = *reinterpret_cast<const float4*>(q);
-                hi = *reinterpret_cast<const float4*>(q + 4);
-                z[0] += lo.x; z[1] += lo.y; z[2] += lo.z; z[3] += lo.w;
-                z[4] += hi.x; z[5] += hi.y; z[6] += hi.z; z[7] += hi.w;
+                float t[8];
+                load_f24x8(src + s * split_stride * kPartBytes, t);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) z[i] += t[i];
             }
             if (b2) {
                 uint4 bb = ld16(b2 + e * P + p);
@@ -447,7 +446,7 @@ hipError_t launch_moe_route(const RouteIO& io, hipStream_t stream) {
     return hipGetLastError();
 }
 
-hipError_t launch_moe_combine(const float* part, int splits, int64_t rows_total,
+hipError_t launch_moe_combine(const void* part, int splits, int64_t rows_total,
                               const int32_t* pos, const int32_t* ids, const float* w,
                               const uint16_t* b2, uint16_t* Y, int64_t M, int k, int64_t P,
                               int act2, hipStream_t stream) {
@@ -455,8 +454,9 @@ hipError_t launch_moe_combine(const float* part, int splits, int64_t rows_total,
     if (nvec <= 0) return hipSuccess;
     int64_t blocks = (nvec + 255) / 256;
     if (blocks > 8192) blocks = 8192;
-    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, part,
-                       splits, rows_total, pos, ids, w, b2, Y, M, k, P, act2);
+    hipLaunchKernelGGL(moe_combine_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const char*>(part), splits, rows_total, pos, ids, w, b2, Y, M, k,
+                       P, act2);
     return hipGetLastError();
 }
 
