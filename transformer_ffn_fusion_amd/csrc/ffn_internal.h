@@ -109,7 +109,7 @@ hipError_t launch_skinny_swiglu_bf16(const uint16_t* A, const uint16_t* Wg, cons
 
 // ---- fp32 path
 
-constexpr int kF32Chunk = 512;
+constexpr int kF32Chunk = 64;   // hidden columns per workgroup of the fp32 path
 hipError_t launch_fused_f32(const float* X, const float* W1, const float* b1, const float* W2,
                             float* part, int64_t M, int64_t N, int64_t O, int64_t P, int act1,
                             hipStream_t stream);
