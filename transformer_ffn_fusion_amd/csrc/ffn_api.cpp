@@ -611,7 +611,7 @@ int moe_route(const float* logits, int64_t M, int64_t E, int k, int32_t* topk_id
 static int check_router_args(const void* Wr, const float* br, const float* logits_out, int64_t E) {
     if (!Wr) return fail(FFN_EINVAL, "Wr must not be NULL");
     if (!aligned16(Wr)) return fail(FFN_EALIGN, "Wr is not 16-byte aligned");
-    if (E % 8 != 0) return fail(FFN_EUNSUPPORTED, "the router form takes E % 8 == 0 (got %lld)", (long long)E);
+    if (E % 8 != 0) return fail(FFN_EUNSUPPORTED, "the router form takes E a multiple of 8 (got %lld)", (long long)E);
     if (reinterpret_cast<uintptr_t>(br) & 3u) return fail(FFN_EALIGN, "br not 4-byte aligned");
     if (reinterpret_cast<uintptr_t>(logits_out) & 3u)
         return fail(FFN_EALIGN, "logits_out not 4-byte aligned");
