@@ -480,12 +480,14 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     // stage (j, j) of the (pass, k) grid, so at any moment they read different
     // stages (measured against smaller rotations, j mod 16 .. j mod 2, and
     // against rotating only the k order inside each pass: all slower).  The
-    // grouped form walks the first product and the passes in plain order: its
-    // co-resident workgroups belong to several experts, and walking each
-    // expert's weights in step keeps the L2 footprint to one sliding window
-    // per expert (560 -> 530 us on the MoE workload); only the k order inside
-    // a pass rotates, so that workgroups of one expert read different slabs
-    // of the same pass (530 -> 487 us).
+    // grouped form walks its passes in plain order: its co-resident
+    // workgroups can belong to several experts, and walking each expert's W2
+    // in step keeps the L2 footprint to one sliding window per expert (560 ->
+    // 530 us on the MoE workload); the k order inside a pass rotates, so that
+    // workgroups of one expert read different slabs of the same pass (530 ->
+    // 487 us), and with the blocked unit numbering (mostly one expert per XCD
+    // at a time) the first product takes the dense form's staggered start
+    // too (499 -> 495 us; rotating the passes as well: 508 us).
     // The pass rotation spans every pass only while the chunk's W2 block
     // (hidden columns x P) fits the XCD's 4 MB L2 and stays resident; a larger
     // block is walked by the co-resident workgroups inside a window of 4
@@ -494,7 +496,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     // 8-pass window ~1190; prefill shard, 448 x 4096 block: a window of 4, 2
     // or 1 passes 172-176 us against 155 for the full rotation).
     const int64_t jx = blockIdx.x >> 3;
-    c.rot1 = kGrouped ? 0 : jx % c.nk;
+    c.rot1 = jx % c.nk;
     const int64_t rot_span =
         (int64_t)Cfg::kHid * P * 2 <= kL2Bytes ? npl : (npl < kPassWindow ? npl : kPassWindow);
     const int64_t rotp = kGrouped ? 0 : jx % rot_span;
