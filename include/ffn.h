@@ -56,13 +56,23 @@ typedef enum { FFN_F32 = 0, FFN_BF16 = 1 } ffn_dtype_t;
 /* act1 / act2.  GELU_TANH is 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))). */
 typedef enum { FFN_ACT_NONE = 0, FFN_ACT_RELU = 1, FFN_ACT_GELU_TANH = 2 } ffn_act_t;
 
-/* Kernel family.  AUTO picks SKINNY for bf16 with M <= 16, FUSED for other
- * bf16 shapes and F32 for fp32 data; the others force a family (tests). */
+/* Kernel family.  AUTO picks DECODE for bf16 with M <= 16 where it applies
+ * (N = P = 4096, O a multiple of 256 up to 2048, a device of 256 CUs), SKINNY
+ * for other bf16 shapes with M <= 16, FUSED for other bf16 shapes and F32 for
+ * fp32 data; the others force a family (tests).  SwiGLU has no DECODE form.
+ * DECODE (the dense form of the tensor-parallelism post, brunomaga.github.io,
+ * "Megatron-LM tensor parallelism", at decode batch sizes): one kernel
+ * streams W1 and W2 together, cuts the hidden dimension into one slice per
+ * XCD and passes each slice of H between the workgroups of that XCD through
+ * its L2; a second kernel sums the 8 slice partials of Y.  Its waits are
+ * bounded: if one expires, or the hardware deals workgroups to XCDs
+ * otherwise than round-robin, every element of Y is NaN. */
 typedef enum {
     FFN_VARIANT_AUTO = 0,
     FFN_VARIANT_FUSED = 1,   /* bf16, H in LDS, split-O partials + ordered reduce */
     FFN_VARIANT_SKINNY = 2,  /* bf16, M <= 16: two weight-streaming layers        */
-    FFN_VARIANT_F32 = 3      /* fp32 data, fp32 arithmetic                       */
+    FFN_VARIANT_F32 = 3,     /* fp32 data, fp32 arithmetic                       */
+    FFN_VARIANT_DECODE = 4   /* bf16, M <= 16: one streaming kernel + reduction  */
 } ffn_variant_t;
 
 enum {
@@ -119,8 +129,9 @@ int ffn_forward_noalloc(const void* X, const void* W1, const void* b1, const voi
 /* As ffn_forward_ex, and records caller-created HIP events (hipEvent_t cast
  * to void*) on `stream` around the path's kernels, for per-kernel timing:
  * events[0] before the first kernel, events[1] between the first (the fused
- * FFN, the fp32 FFN or skinny layer 1) and the second (the split reduction or
- * skinny layer 2), events[2] after the second.  n_events >= 3. */
+ * FFN, the fp32 FFN, skinny layer 1 or the decode streaming kernel) and the
+ * second (the split reduction, skinny layer 2 or the decode slice
+ * reduction), events[2] after the second.  n_events >= 3. */
 int ffn_forward_traced(const void* X, const void* W1, const void* b1, const void* W2,
                        const void* b2, void* Y, int64_t M, int64_t N, int64_t O, int64_t P,
                        int dtype, int act1, int act2, int variant, void* workspace,

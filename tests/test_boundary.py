@@ -70,6 +70,12 @@ def _fwd(X=FAKE, W1=FAKE, b1=None, W2=FAKE, b2=None, Y=FAKE2, M=64, N=64, O=448,
     (dict(variant=ffn.VARIANT_SKINNY, M=17), E_UNSUP),
     (dict(variant=ffn.VARIANT_F32), E_UNSUP),
     (dict(dtype=ffn.F32, variant=ffn.VARIANT_FUSED), E_UNSUP),
+    (dict(variant=ffn.VARIANT_DECODE, M=16), E_UNSUP),                    # N, P not 4096
+    (dict(variant=ffn.VARIANT_DECODE, M=17, N=4096, O=1792, P=4096), E_UNSUP),
+    (dict(variant=ffn.VARIANT_DECODE, M=16, N=4096, O=1920, P=4096), E_UNSUP),  # O % 256
+    (dict(variant=ffn.VARIANT_DECODE, M=16, N=4096, O=2304, P=4096), E_UNSUP),  # O > 2048
+    (dict(variant=ffn.VARIANT_DECODE, M=16, N=4096, O=1792, P=8192), E_UNSUP),
+    (dict(variant=ffn.VARIANT_DECODE, dtype=ffn.F32, M=16, N=4096, O=1792, P=4096), E_UNSUP),
     (dict(), E_WS),
 ])
 def test_forward_rejects(kw, code):
@@ -85,6 +91,22 @@ def test_workspace_one_byte_short_is_rejected():
     skinny = ffn.ffn_workspace_size(16, 4096, 1792, 4096)
     assert 0 < skinny < need
     assert _fwd(M=16, N=4096, O=1792, P=4096, wsb=skinny - 1) == E_WS
+
+
+def test_decode_stream_workspace_sizes():
+    # [256][16][O/8] fp32 K-block partials, 16 x O bf16 H, [8][16][P] fp32 slice
+    # partials, 2 x 256 flags and a status word, each region 256-byte aligned
+    dec = ffn.ffn_workspace_size(16, 4096, 1792, 4096, ffn.BF16, ffn.VARIANT_DECODE)
+    assert dec == 256 * 16 * 224 * 4 + 16 * 1792 * 2 + 8 * 16 * 4096 * 4 + 2 * 256 * 8 + 256
+    skinny_only = ffn.ffn_workspace_size(16, 4096, 1792, 4096, ffn.BF16, ffn.VARIANT_SKINNY)
+    auto = ffn.ffn_workspace_size(16, 4096, 1792, 4096)
+    assert auto == max(dec, skinny_only)          # AUTO may take either path
+    assert _fwd(M=16, N=4096, O=1792, P=4096, variant=ffn.VARIANT_DECODE, wsb=dec - 1) == E_WS
+    assert ffn.ffn_workspace_size(16, 4096, 1920, 4096, ffn.BF16, ffn.VARIANT_DECODE) == 0
+    assert ffn.ffn_workspace_size(16, 4096, 1792, 4096, ffn.F32, ffn.VARIANT_DECODE) == 0
+    # shapes the decode stream does not take keep the skinny size under AUTO
+    assert ffn.ffn_workspace_size(16, 4096, 1920, 4096) == \
+        ffn.ffn_workspace_size(16, 4096, 1920, 4096, ffn.BF16, ffn.VARIANT_SKINNY)
 
 
 def test_workspace_size_invalid_shapes():
@@ -115,6 +137,7 @@ def _swiglu(X=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, Y=FAKE2, M=64, N=64, O=256, P=64,
     (dict(Wd=FAKE + 4), E_ALIGN),
     (dict(variant=ffn.VARIANT_SKINNY, M=17), E_UNSUP),
     (dict(dtype=ffn.F32, variant=ffn.VARIANT_SKINNY), E_UNSUP),
+    (dict(variant=ffn.VARIANT_DECODE, M=16, N=4096, O=1792, P=4096), E_UNSUP),
     (dict(), E_WS),
 ])
 def test_swiglu_rejects(kw, code):

@@ -17,7 +17,7 @@ import os
 
 __all__ = [
     "F32", "BF16", "ACT_NONE", "ACT_RELU", "ACT_GELU_TANH",
-    "VARIANT_AUTO", "VARIANT_FUSED", "VARIANT_SKINNY", "VARIANT_F32",
+    "VARIANT_AUTO", "VARIANT_FUSED", "VARIANT_SKINNY", "VARIANT_F32", "VARIANT_DECODE",
     "FFNError", "lib", "lib_path", "ffn_workspace_size", "ffn_forward", "ffn_forward_ex",
     "ffn_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
     "moe_workspace_size", "moe_route", "moe_ffn_forward", "ffn_last_error", "workspace",
@@ -25,7 +25,7 @@ __all__ = [
 
 F32, BF16 = 0, 1
 ACT_NONE, ACT_RELU, ACT_GELU_TANH = 0, 1, 2
-VARIANT_AUTO, VARIANT_FUSED, VARIANT_SKINNY, VARIANT_F32 = 0, 1, 2, 3
+VARIANT_AUTO, VARIANT_FUSED, VARIANT_SKINNY, VARIANT_F32, VARIANT_DECODE = 0, 1, 2, 3, 4
 ACTS = {"none": ACT_NONE, "relu": ACT_RELU, "gelu_tanh": ACT_GELU_TANH}
 NOALLOC_SCRATCH_BYTES = 16 << 20   # FFN_NOALLOC_SCRATCH_BYTES in include/ffn.h
 

@@ -3,15 +3,19 @@
 //
 // Every check that can fail runs on the host before the first launch, so a
 // rejected call leaves all outputs untouched.  The library keeps no state
-// between calls other than the error text of the calling host thread.
+// between calls other than the error text of the calling host thread and the
+// decode-stream call counter.
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
 
 #include "ffn.h"
 #include "ffn_device.h"
+
 #include "ffn_internal.h"
 
 namespace {
@@ -61,6 +65,16 @@ int check_dims(int64_t M, int64_t N, int64_t O, int64_t P) {
     return FFN_OK;
 }
 
+// A number that is new for every decode-stream call of this process (the
+// call's flags in the workspace carry it, so they never need clearing); the
+// start depends on the process's start time, so that another process's old
+// flags in reused memory do not match either.
+uint64_t next_epoch() {
+    static std::atomic<uint64_t> counter{
+        (uint64_t)std::chrono::steady_clock::now().time_since_epoch().count() << 20};
+    return counter.fetch_add(1, std::memory_order_relaxed) + 1;
+}
+
 int resolve_variant(int variant, int dtype, int64_t M) {
     if (variant == FFN_VARIANT_AUTO) {
         if (dtype == FFN_F32) return FFN_VARIANT_F32;
@@ -86,7 +100,9 @@ DenseLayout dense_layout(int64_t M, int64_t N, int64_t O, int64_t P, int variant
     } else if (variant == FFN_VARIANT_F32) {
         const int64_t S = (O + ffn::kF32Chunk - 1) / ffn::kF32Chunk;
         L.total = align_up((size_t)S * M * P * sizeof(float));
-    } else {  // skinny
+    } else if (variant == FFN_VARIANT_DECODE) {
+        L.total = ffn::decode_stream_layout(O, P).total;
+    } else {  // skinny; AUTO may run the decode stream instead, so the size covers both
         size_t off = 0;
         L.part1 = off;
         off += align_up(sizeof(float) * ffn::skinny_partial_floats(N, O));
@@ -95,6 +111,10 @@ DenseLayout dense_layout(int64_t M, int64_t N, int64_t O, int64_t P, int variant
         L.part2 = off;
         off += align_up(sizeof(float) * ffn::skinny_partial_floats(O, P));
         L.total = off;
+        if (ffn::decode_stream_shape(M, N, O, P)) {
+            const size_t d = ffn::decode_stream_layout(O, P).total;
+            if (d > L.total) L.total = d;
+        }
     }
     if (L.total == 0) L.total = kAlign;
     return L;
@@ -220,7 +240,9 @@ size_t ffn_workspace_size_ex(int64_t M, int64_t N, int64_t O, int64_t P, int dty
     if (check_dims(M, N, O, P) != FFN_OK) return 0;
     if (dtype != FFN_F32 && dtype != FFN_BF16) return 0;
     const int v = resolve_variant(variant, dtype, M);
-    if (v < FFN_VARIANT_FUSED || v > FFN_VARIANT_F32) return 0;
+    if (v < FFN_VARIANT_FUSED || v > FFN_VARIANT_DECODE) return 0;
+    if (v == FFN_VARIANT_DECODE && (dtype != FFN_BF16 || !ffn::decode_stream_shape(M, N, O, P)))
+        return 0;
     return dense_layout(M, N, O, P, v).total;
 }
 
@@ -245,7 +267,7 @@ static int dense_forward(const void* X, const void* W1, const void* b1, const vo
     if (dtype != FFN_F32 && dtype != FFN_BF16) return fail(FFN_EINVAL, "unknown dtype %d", dtype);
     if (!valid_act(act1) || !valid_act(act2))
         return fail(FFN_EINVAL, "unknown activation (act1=%d, act2=%d)", act1, act2);
-    if (variant < FFN_VARIANT_AUTO || variant > FFN_VARIANT_F32)
+    if (variant < FFN_VARIANT_AUTO || variant > FFN_VARIANT_DECODE)
         return fail(FFN_EINVAL, "unknown variant %d", variant);
     rc = check_common_ptrs(X, W1, b1, W2, b2, Y, workspace, M);
     if (rc) return rc;
@@ -255,6 +277,16 @@ static int dense_forward(const void* X, const void* W1, const void* b1, const vo
     if (v == FFN_VARIANT_SKINNY && M > ffn::kSkinnyMaxM)
         return fail(FFN_EUNSUPPORTED, "the skinny variant takes M <= %d (got %lld)",
                     ffn::kSkinnyMaxM, (long long)M);
+    if (v == FFN_VARIANT_DECODE) {
+        if (dtype != FFN_BF16 || !ffn::decode_stream_shape(M, N, O, P))
+            return fail(FFN_EUNSUPPORTED,
+                        "the decode variant takes bf16, M <= 16, N = P = 4096 and O a multiple "
+                        "of 256 up to 2048 (got %lld x %lld x %lld x %lld)",
+                        (long long)M, (long long)N, (long long)O, (long long)P);
+        if (ffn::device_cus() != 256)
+            return fail(FFN_EUNSUPPORTED, "the decode variant needs a device of 256 CUs (has %d)",
+                        ffn::device_cus());
+    }
     const DenseLayout L = dense_layout(M, N, O, P, v);
     if (workspace_bytes < L.total)
         return fail(FFN_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
@@ -287,6 +319,20 @@ static int dense_forward(const void* X, const void* W1, const void* b1, const vo
         if ((rc = mark(events, n_events, 1, st))) return rc;
         rc = launched(ffn::launch_reduce_splits(part, S, b2, 1, Y, 1, M, P, act2, st),
                       "split reduction kernel");
+        if (rc) return rc;
+    } else if (v == FFN_VARIANT_DECODE ||
+               (variant == FFN_VARIANT_AUTO && ffn::decode_stream_shape(M, N, O, P) &&
+                ffn::device_cus() == 256)) {
+        const uint64_t epoch = next_epoch();
+        rc = launched(ffn::launch_decode_stream((const uint16_t*)X, (const uint16_t*)W1,
+                                                (const uint16_t*)b1, (const uint16_t*)W2, ws, M,
+                                                O, P, act1, epoch, st),
+                      "decode streaming kernel");
+        if (rc) return rc;
+        if ((rc = mark(events, n_events, 1, st))) return rc;
+        rc = launched(ffn::launch_decode_reduce((const uint16_t*)b2, (uint16_t*)Y, ws, M, O, P,
+                                                act2, epoch, st),
+                      "decode slice reduction");
         if (rc) return rc;
     } else {
         uint16_t* H = reinterpret_cast<uint16_t*>(ws + L.h);
@@ -437,8 +483,10 @@ static int swiglu_forward(const void* X, const void* Wg, const void* Wu, const v
     int rc = check_dims(M, N, O, P);
     if (rc) return rc;
     if (dtype != FFN_F32 && dtype != FFN_BF16) return fail(FFN_EINVAL, "unknown dtype %d", dtype);
-    if (variant < FFN_VARIANT_AUTO || variant > FFN_VARIANT_F32)
+    if (variant < FFN_VARIANT_AUTO || variant > FFN_VARIANT_DECODE)
         return fail(FFN_EINVAL, "unknown variant %d", variant);
+    if (variant == FFN_VARIANT_DECODE)
+        return fail(FFN_EUNSUPPORTED, "the SwiGLU form has no decode-stream variant");
     if (!Wu) return fail(FFN_EINVAL, "Wu must not be NULL");
     if (!aligned16(Wu)) return fail(FFN_EALIGN, "Wu is not 16-byte aligned");
     rc = check_common_ptrs(X, Wg, nullptr, Wd, nullptr, Y, workspace, M);

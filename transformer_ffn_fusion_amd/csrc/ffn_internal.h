@@ -87,6 +87,22 @@ hipError_t launch_reduce_splits(const void* part, int splits, const void* b2, in
                                 void* Y, int y_f32, int64_t M, int64_t P, int act2,
                                 hipStream_t stream);
 
+// ---- decode FFN (M <= 16) as one streaming kernel + one reduction, H
+// exchanged inside each XCD's L2 (ffn_decode.hip).  Shapes: N = 4096,
+// P = 4096, O a multiple of 256 up to 2048; a device of 256 CUs in 8 XCDs.
+constexpr int64_t kDecodeN = 4096;
+constexpr int64_t kDecodeP = 4096;
+bool decode_stream_shape(int64_t M, int64_t N, int64_t O, int64_t P);
+struct DecodeStreamLayout {   // workspace byte offsets, 256-byte aligned
+    size_t part1, h, part2, flags, status, total;
+};
+DecodeStreamLayout decode_stream_layout(int64_t O, int64_t P);
+hipError_t launch_decode_stream(const uint16_t* X, const uint16_t* W1, const uint16_t* b1,
+                                const uint16_t* W2, char* ws, int64_t M, int64_t O, int64_t P,
+                                int act1, uint64_t epoch, hipStream_t stream);
+hipError_t launch_decode_reduce(const uint16_t* b2, uint16_t* Y, char* ws, int64_t M, int64_t O,
+                                int64_t P, int act2, uint64_t epoch, hipStream_t stream);
+
 // ---- skinny (M <= 16) bf16 layer with a fixed-order split-K reduction
 
 constexpr int kSkinnyCols = 128;   // output columns per workgroup
