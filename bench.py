@@ -6,7 +6,8 @@
 
 A step is one call of the whole path on one batch of synthetic input that is
 already resident in HBM: for the dense workloads the fused FFN kernel and the
-ordered split reduction (or the two skinny layers at M <= 16); for the MoE
+ordered split reduction (at M <= 16: the decode streaming kernel and its slice
+reduction, or the two skinny layers where the streaming kernel does not apply); for the MoE
 workload routing, the grouped fused FFN and the combine; for the backward
 workload the six steps of the gradients at the prefill shape; for the SwiGLU
 workloads the gated fused FFN and the reduction (two gated skinny layers at
@@ -67,9 +68,9 @@ COPY_BYTES = 256 << 20   # the plain copy used to calibrate the HBM byte counter
 
 
 # the sources of the kernels whose HBM traffic is recorded (forward fused and grouped,
-# decode layers, routing and combine, and the headers they include)
-TRAFFIC_SOURCES = ("ffn_fused.hip", "ffn_skinny.hip", "moe.hip", "ffn_backward.hip", "ffn_device.h",
-                   "ffn_internal.h")
+# decode stream and layers, routing and combine, and the headers they include)
+TRAFFIC_SOURCES = ("ffn_fused.hip", "ffn_skinny.hip", "ffn_decode.hip", "moe.hip", "ffn_backward.hip",
+                   "ffn_device.h", "ffn_internal.h")
 
 
 def kernel_source_hash() -> str:
@@ -270,6 +271,7 @@ def run_dense(cfg, steps, warmup, hip, torch, ffn, synth, workload):
                 k1_std_ms=float(np.std(k1)), k2_ms=float(np.mean(k2)), flops=flops, bytes=nbytes,
                 warm_ms_per_step=warm_ms / steps, settled_ms_per_step=settled_ms / steps,
                 settled_after_calls=max(done, SETTLE_CALLS), rotate=R,
+                family=None if gated else ffn.ffn_forward_family(cfg.M, cfg.N, cfg.O, cfg.P, code),
                 inputs=(X, W1, b1, W2, b2))
 
 
@@ -569,16 +571,24 @@ def main():
         if head.M <= 16 and head.dtype == "bf16":
             value = r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
             unit = "GB/s"
-            # layer 1 and layer 2 each stream their own weights: count each layer's own bytes
-            # (the gated first layer streams Wg and Wu and has no bias)
-            if isinstance(head, workload.Gated):
+            if r["family"] == ffn.VARIANT_DECODE:
+                # the streaming kernel reads X, W1, b1 and W2 and writes the 8 slice
+                # partials of Y (16 rows x P fp32 each); the slice reduction follows
+                k1_bytes = (2 * (head.M * head.N + head.N * head.O + head.O + head.O * head.P)
+                            + 8 * 16 * head.P * 4)
+                kname = "decode streaming kernel (both layers, H through each XCD's L2)"
+            elif isinstance(head, workload.Gated):
+                # skinny layers: layer 1 streams Wg and Wu (no bias) and writes H
                 k1_bytes = 2 * (head.M * head.N + 2 * head.N * head.O + head.M * head.O)
+                kname = "gated skinny layer 1 (stream + ordered reduce)"
             else:
                 k1_bytes = 2 * (head.M * head.N + head.N * head.O + head.O + head.M * head.O)
+                kname = "skinny layer 1 (stream + ordered reduce)"
             ach = k1_bytes / (r["k1_ms"] * 1e-3) / 1e9
-            roof = {"bound": "hbm", "kernel": "skinny layer 1 (stream + ordered reduce)", "achieved": ach,
+            roof = {"bound": "hbm", "kernel": kname, "achieved": ach,
                     "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": ach / PEAK_HBM_GBS,
-                    "traffic": recorded_traffic(head.name), "kernel_us": 1e3 * r["k1_ms"]}
+                    "traffic": recorded_traffic(head.name), "kernel_us": 1e3 * r["k1_ms"],
+                    "second_kernel_us": 1e3 * r["k2_ms"]}
         else:
             value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
             unit = "TFLOP/s"
@@ -596,7 +606,8 @@ def main():
             "us_per_call": 1e3 * d["ms_per_step"],
             "GB_per_s": d["bytes"] / (d["ms_per_step"] * 1e-3) / 1e9,
             "frac_hbm_peak": d["bytes"] / (d["ms_per_step"] * 1e-3) / 1e9 / PEAK_HBM_GBS,
-            "layer1_us": 1e3 * d["k1_ms"], "layer2_us": 1e3 * d["k2_ms"],
+            "path": "decode stream" if d["family"] == ffn.VARIANT_DECODE else "skinny layers",
+            "kernel1_us": 1e3 * d["k1_ms"], "kernel2_us": 1e3 * d["k2_ms"],
             "kernels_GB_per_s": d["bytes"] / ((d["k1_ms"] + d["k2_ms"]) * 1e-3) / 1e9,
             "rotate": d["rotate"], "warm_us_per_call": 1e3 * d["warm_ms_per_step"],
             "settled_us_per_call": 1e3 * d["settled_ms_per_step"]}

@@ -97,6 +97,13 @@ int ffn_forward(const void* X, const void* W1, const void* b1, const void* W2, c
                 void* Y, int64_t M, int64_t N, int64_t O, int64_t P, int dtype, int act1,
                 int act2, void* workspace, size_t workspace_bytes, void* stream);
 
+/* The kernel family (FFN_VARIANT_FUSED, _SKINNY, _F32 or _DECODE) that
+ * ffn_forward_ex runs for this shape, dtype and variant on the current
+ * device; AUTO resolves as described at ffn_variant_t.  Returns a negative
+ * FFN_E* code for an invalid shape, dtype or variant; it does not check that
+ * a forced family supports the shape. */
+int ffn_forward_family(int64_t M, int64_t N, int64_t O, int64_t P, int dtype, int variant);
+
 /* As ffn_forward, with the kernel family forced (FFN_VARIANT_*). */
 int ffn_forward_ex(const void* X, const void* W1, const void* b1, const void* W2,
                    const void* b2, void* Y, int64_t M, int64_t N, int64_t O, int64_t P,

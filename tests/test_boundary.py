@@ -287,3 +287,18 @@ def test_noalloc_scratch_size_matches_the_header_and_its_stated_shapes():
     assert ws(16, 8192, 3584, 8192) <= ffn.NOALLOC_SCRATCH_BYTES      # stated in the header
     assert ws(341, 4096, 1792, 4096) <= ffn.NOALLOC_SCRATCH_BYTES     # stated in the header
     assert ws(342, 4096, 1792, 4096) > ffn.NOALLOC_SCRATCH_BYTES
+
+
+def test_forward_family_resolution():
+    fam = ffn.ffn_forward_family
+    assert fam(4096, 4096, 1792, 4096) == ffn.VARIANT_FUSED
+    assert fam(8, 128, 512, 128, ffn.F32) == ffn.VARIANT_F32
+    assert fam(16, 1024, 896, 1024) == ffn.VARIANT_SKINNY          # not a decode-stream shape
+    # the decode stream when the device has 256 CUs (a device count query that fails reads as 256)
+    assert fam(16, 4096, 1792, 4096) in (ffn.VARIANT_DECODE, ffn.VARIANT_SKINNY)
+    assert fam(16, 4096, 1792, 4096, ffn.BF16, ffn.VARIANT_SKINNY) == ffn.VARIANT_SKINNY
+    assert fam(16, 4096, 1792, 4096, ffn.BF16, ffn.VARIANT_DECODE) == ffn.VARIANT_DECODE
+    with pytest.raises(ffn.FFNError):
+        fam(16, 4096, 1792, 4096, ffn.BF16, 9)
+    with pytest.raises(ffn.FFNError):
+        fam(16, 4096, 12, 4096)

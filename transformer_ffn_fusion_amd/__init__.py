@@ -19,6 +19,7 @@ __all__ = [
     "F32", "BF16", "ACT_NONE", "ACT_RELU", "ACT_GELU_TANH",
     "VARIANT_AUTO", "VARIANT_FUSED", "VARIANT_SKINNY", "VARIANT_F32", "VARIANT_DECODE",
     "FFNError", "lib", "lib_path", "ffn_workspace_size", "ffn_forward", "ffn_forward_ex",
+    "ffn_forward_family",
     "ffn_forward_noalloc", "NOALLOC_SCRATCH_BYTES",
     "moe_workspace_size", "moe_route", "moe_ffn_forward", "ffn_last_error", "workspace",
 ]
@@ -52,6 +53,8 @@ def lib():
         L.ffn_workspace_size.restype = sz
         L.ffn_workspace_size_ex.argtypes = [i64, i64, i64, i64, i32, i32]
         L.ffn_workspace_size_ex.restype = sz
+        L.ffn_forward_family.argtypes = [i64, i64, i64, i64, i32, i32]
+        L.ffn_forward_family.restype = i32
         L.ffn_forward.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, vp, sz, vp]
         L.ffn_forward.restype = i32
         L.ffn_forward_ex.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32, i32, i32, i32,
@@ -205,6 +208,15 @@ def ffn_workspace_size(M, N, O, P, dtype=BF16, variant=VARIANT_AUTO) -> int:
 
 def moe_workspace_size(M, E, k, N, O, P, dtype=BF16) -> int:
     return lib().moe_workspace_size(M, E, k, N, O, P, dtype)
+
+
+def ffn_forward_family(M, N, O, P, dtype=BF16, variant=VARIANT_AUTO) -> int:
+    """The kernel family (VARIANT_FUSED, _SKINNY, _F32 or _DECODE) that ``ffn_forward_ex``
+    runs for this shape on the current device."""
+    rc = lib().ffn_forward_family(M, N, O, P, dtype, variant)
+    if rc < 0:
+        raise FFNError(rc, ffn_last_error())
+    return rc
 
 
 def workspace(nbytes: int, device="cuda"):

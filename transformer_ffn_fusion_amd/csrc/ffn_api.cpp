@@ -246,6 +246,19 @@ size_t ffn_workspace_size_ex(int64_t M, int64_t N, int64_t O, int64_t P, int dty
     return dense_layout(M, N, O, P, v).total;
 }
 
+int ffn_forward_family(int64_t M, int64_t N, int64_t O, int64_t P, int dtype, int variant) {
+    int rc = check_dims(M, N, O, P);
+    if (rc) return rc;
+    if (dtype != FFN_F32 && dtype != FFN_BF16) return fail(FFN_EINVAL, "unknown dtype %d", dtype);
+    if (variant < FFN_VARIANT_AUTO || variant > FFN_VARIANT_DECODE)
+        return fail(FFN_EINVAL, "unknown variant %d", variant);
+    const int v = resolve_variant(variant, dtype, M);
+    if (variant == FFN_VARIANT_AUTO && v == FFN_VARIANT_SKINNY &&
+        ffn::decode_stream_shape(M, N, O, P) && ffn::device_cus() == 256)
+        return FFN_VARIANT_DECODE;
+    return v;
+}
+
 size_t ffn_workspace_size(int64_t M, int64_t N, int64_t O, int64_t P, int dtype) {
     return ffn_workspace_size_ex(M, N, O, P, dtype, FFN_VARIANT_AUTO);
 }
@@ -320,9 +333,7 @@ static int dense_forward(const void* X, const void* W1, const void* b1, const vo
         rc = launched(ffn::launch_reduce_splits(part, S, b2, 1, Y, 1, M, P, act2, st),
                       "split reduction kernel");
         if (rc) return rc;
-    } else if (v == FFN_VARIANT_DECODE ||
-               (variant == FFN_VARIANT_AUTO && ffn::decode_stream_shape(M, N, O, P) &&
-                ffn::device_cus() == 256)) {
+    } else if (ffn_forward_family(M, N, O, P, dtype, variant) == FFN_VARIANT_DECODE) {
         const uint64_t epoch = next_epoch();
         rc = launched(ffn::launch_decode_stream((const uint16_t*)X, (const uint16_t*)W1,
                                                 (const uint16_t*)b1, (const uint16_t*)W2, ws, M,
