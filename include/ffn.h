@@ -23,8 +23,9 @@
  *    keeps a pointer after the call returns.
  *  - Workspace.  Query the size with the matching *_workspace_size call.
  *    The workspace holds only per-call intermediates (split partials, the
- *    decode shape's H, the routing tables); it needs no initialisation and
- *    keeps nothing between calls.  Calls that share a workspace must be
+ *    decode shape's H, the routing tables, the decode stream's flags, which
+ *    carry a number that is new for every call); it needs no initialisation
+ *    and keeps nothing between calls.  Calls that share a workspace must be
  *    ordered (same stream).
  *  - Asynchrony.  Calls only enqueue work on `stream` (a hipStream_t; NULL is
  *    the default stream) and return without synchronising.
