@@ -271,7 +271,8 @@ def run_dense(cfg, steps, warmup, hip, torch, ffn, synth, workload):
                 k1_std_ms=float(np.std(k1)), k2_ms=float(np.mean(k2)), flops=flops, bytes=nbytes,
                 warm_ms_per_step=warm_ms / steps, settled_ms_per_step=settled_ms / steps,
                 settled_after_calls=max(done, SETTLE_CALLS), rotate=R,
-                family=None if gated else ffn.ffn_forward_family(cfg.M, cfg.N, cfg.O, cfg.P, code),
+                # the SwiGLU form resolves its family by the same rule as the dense one
+                family=ffn.ffn_forward_family(cfg.M, cfg.N, cfg.O, cfg.P, code),
                 inputs=(X, W1, b1, W2, b2))
 
 
@@ -571,7 +572,13 @@ def main():
         if head.M <= 16 and head.dtype == "bf16":
             value = r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
             unit = "GB/s"
-            if r["family"] == ffn.VARIANT_DECODE:
+            if r["family"] == ffn.VARIANT_DECODE and isinstance(head, workload.Gated):
+                # the gated streaming kernel reads X, Wg, Wu and Wd and writes the 8
+                # slice partials of Y (16 rows x P fp32 each)
+                k1_bytes = (2 * (head.M * head.N + 2 * head.N * head.O + head.O * head.P)
+                            + 8 * 16 * head.P * 4)
+                kname = "gated decode streaming kernel (both layers, H through each XCD's L2)"
+            elif r["family"] == ffn.VARIANT_DECODE:
                 # the streaming kernel reads X, W1, b1 and W2 and writes the 8 slice
                 # partials of Y (16 rows x P fp32 each); the slice reduction follows
                 k1_bytes = (2 * (head.M * head.N + head.N * head.O + head.O + head.O * head.P)

@@ -60,7 +60,8 @@ typedef enum { FFN_ACT_NONE = 0, FFN_ACT_RELU = 1, FFN_ACT_GELU_TANH = 2 } ffn_a
 /* Kernel family.  AUTO picks DECODE for bf16 with M <= 16 where it applies
  * (N = P = 4096, O a multiple of 256 up to 2048, a device of 256 CUs), SKINNY
  * for other bf16 shapes with M <= 16, FUSED for other bf16 shapes and F32 for
- * fp32 data; the others force a family (tests).  SwiGLU has no DECODE form.
+ * fp32 data; the others force a family (tests).  The SwiGLU entry points
+ * resolve AUTO by the same rule (their DECODE form streams Wg, Wu and Wd).
  * DECODE (the dense form of the tensor-parallelism post, brunomaga.github.io,
  * "Megatron-LM tensor parallelism", at decode batch sizes): one kernel
  * streams W1 and W2 together, cuts the hidden dimension into one slice per

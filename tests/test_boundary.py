@@ -137,7 +137,9 @@ def _swiglu(X=FAKE, Wg=FAKE, Wu=FAKE, Wd=FAKE, Y=FAKE2, M=64, N=64, O=256, P=64,
     (dict(Wd=FAKE + 4), E_ALIGN),
     (dict(variant=ffn.VARIANT_SKINNY, M=17), E_UNSUP),
     (dict(dtype=ffn.F32, variant=ffn.VARIANT_SKINNY), E_UNSUP),
-    (dict(variant=ffn.VARIANT_DECODE, M=16, N=4096, O=1792, P=4096), E_UNSUP),
+    (dict(variant=ffn.VARIANT_DECODE, M=16, N=4096, O=1920, P=4096), E_UNSUP),
+    (dict(variant=ffn.VARIANT_DECODE, M=16, N=2048, O=1792, P=4096), E_UNSUP),
+    (dict(variant=ffn.VARIANT_DECODE, M=16, N=4096, O=1792, P=4096), E_WS),
     (dict(), E_WS),
 ])
 def test_swiglu_rejects(kw, code):
@@ -302,3 +304,13 @@ def test_forward_family_resolution():
         fam(16, 4096, 1792, 4096, ffn.BF16, 9)
     with pytest.raises(ffn.FFNError):
         fam(16, 4096, 12, 4096)
+
+
+def test_gated_decode_stream_workspace_sizes():
+    S = ffn.ffn_swiglu_workspace_size
+    dec = S(16, 4096, 1792, 4096, ffn.BF16, ffn.VARIANT_DECODE)
+    # gate and up K-block partials, H, slice partials, flags, status
+    assert dec == 2 * 256 * 16 * 224 * 4 + 16 * 1792 * 2 + 8 * 16 * 4096 * 4 + 2 * 256 * 8 + 256
+    assert S(16, 4096, 1792, 4096) == max(dec, S(16, 4096, 1792, 4096, ffn.BF16, ffn.VARIANT_SKINNY))
+    assert S(16, 4096, 1920, 4096, ffn.BF16, ffn.VARIANT_DECODE) == 0
+    assert _swiglu(M=16, N=4096, O=1792, P=4096, variant=ffn.VARIANT_DECODE, wsb=dec - 1) == E_WS

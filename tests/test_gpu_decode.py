@@ -122,3 +122,46 @@ def test_decode_stream_is_the_default_and_matches_skinny():
         compare(host_f64(Y), ref, BF16_TOL, f"variant {v}")
         outs[v] = Y
     assert torch.equal(outs[ffn.VARIANT_AUTO], outs[ffn.VARIANT_DECODE])
+
+
+# ---------------------------------------------------------------- gated (SwiGLU) form
+
+def _swiglu(M, N, O, P, seed, variant, ws=None, repeat=1):
+    import torch
+    X, Wg, Wu, Wd = synth.swiglu_inputs(M, N, O, P, seed=seed)
+    dev = [dev_bf16(a) for a in (X, Wg, Wu, Wd)]
+    if ws is None:
+        ws = ffn.workspace(ffn.ffn_swiglu_workspace_size(M, N, O, P, ffn.BF16, variant))
+    outs = []
+    for _ in range(repeat):
+        Y = torch.empty((M, P), dtype=torch.bfloat16, device="cuda")
+        ffn.ffn_swiglu_forward(*dev, Y, variant, ws)
+        torch.cuda.synchronize()
+        outs.append(Y)
+    return outs, oracle.swiglu(X, Wg, Wu, Wd)
+
+
+@pytest.mark.parametrize("shape", [
+    (16, 4096, 1792, 4096),   # the SwiGLU decode shard
+    (3, 4096, 512, 4096),
+    (9, 4096, 2048, 4096),
+])
+def test_gated_decode_stream_shapes(shape):
+    M, N, O, P = shape
+    log(f"case gated decode stream {shape}")
+    outs, ref = _swiglu(M, N, O, P, seed=M + O, variant=ffn.VARIANT_DECODE, repeat=2)
+    compare(host_f64(outs[0]), ref, BF16_TOL, f"gated decode stream {shape}")
+    import torch
+    assert torch.equal(outs[0], outs[1]), "two calls differ"
+
+
+def test_gated_decode_stream_is_the_default_and_matches_skinny():
+    import torch
+    c = workload.SWIGLU_DECODE
+    log(f"case gated decode stream vs skinny ({c.name})")
+    got = {}
+    for v in (ffn.VARIANT_AUTO, ffn.VARIANT_DECODE, ffn.VARIANT_SKINNY):
+        outs, ref = _swiglu(c.M, c.N, c.O, c.P, seed=51, variant=v)
+        compare(host_f64(outs[0]), ref, BF16_TOL, f"variant {v}")
+        got[v] = outs[0]
+    assert torch.equal(got[ffn.VARIANT_AUTO], got[ffn.VARIANT_DECODE])

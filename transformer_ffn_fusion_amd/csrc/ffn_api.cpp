@@ -101,7 +101,7 @@ DenseLayout dense_layout(int64_t M, int64_t N, int64_t O, int64_t P, int variant
         const int64_t S = (O + ffn::kF32Chunk - 1) / ffn::kF32Chunk;
         L.total = align_up((size_t)S * M * P * sizeof(float));
     } else if (variant == FFN_VARIANT_DECODE) {
-        L.total = ffn::decode_stream_layout(O, P).total;
+        L.total = ffn::decode_stream_layout(O, P, false).total;
     } else {  // skinny; AUTO may run the decode stream instead, so the size covers both
         size_t off = 0;
         L.part1 = off;
@@ -112,7 +112,7 @@ DenseLayout dense_layout(int64_t M, int64_t N, int64_t O, int64_t P, int variant
         off += align_up(sizeof(float) * ffn::skinny_partial_floats(O, P));
         L.total = off;
         if (ffn::decode_stream_shape(M, N, O, P)) {
-            const size_t d = ffn::decode_stream_layout(O, P).total;
+            const size_t d = ffn::decode_stream_layout(O, P, false).total;
             if (d > L.total) L.total = d;
         }
     }
@@ -134,7 +134,9 @@ SwigluLayout swiglu_layout(int64_t M, int64_t N, int64_t O, int64_t P, int varia
     } else if (variant == FFN_VARIANT_F32) {
         const int64_t S = (O + ffn::kF32Chunk - 1) / ffn::kF32Chunk;
         L.total = align_up((size_t)S * M * P * sizeof(float));
-    } else {
+    } else if (variant == FFN_VARIANT_DECODE) {
+        L.total = ffn::decode_stream_layout(O, P, true).total;
+    } else {  // skinny; AUTO may run the decode stream instead, so the size covers both
         size_t off = 0;
         L.part_g = off;
         off += align_up(sizeof(float) * ffn::skinny_gated_partial_floats(N, O));
@@ -145,6 +147,10 @@ SwigluLayout swiglu_layout(int64_t M, int64_t N, int64_t O, int64_t P, int varia
         L.part2 = off;
         off += align_up(sizeof(float) * ffn::skinny_partial_floats(O, P));
         L.total = off;
+        if (ffn::decode_stream_shape(M, N, O, P)) {
+            const size_t d = ffn::decode_stream_layout(O, P, true).total;
+            if (d > L.total) L.total = d;
+        }
     }
     if (L.total == 0) L.total = kAlign;
     return L;
@@ -335,14 +341,14 @@ static int dense_forward(const void* X, const void* W1, const void* b1, const vo
         if (rc) return rc;
     } else if (ffn_forward_family(M, N, O, P, dtype, variant) == FFN_VARIANT_DECODE) {
         const uint64_t epoch = next_epoch();
-        rc = launched(ffn::launch_decode_stream((const uint16_t*)X, (const uint16_t*)W1,
+        rc = launched(ffn::launch_decode_stream((const uint16_t*)X, (const uint16_t*)W1, nullptr,
                                                 (const uint16_t*)b1, (const uint16_t*)W2, ws, M,
                                                 O, P, act1, epoch, st),
                       "decode streaming kernel");
         if (rc) return rc;
         if ((rc = mark(events, n_events, 1, st))) return rc;
         rc = launched(ffn::launch_decode_reduce((const uint16_t*)b2, (uint16_t*)Y, ws, M, O, P,
-                                                act2, epoch, st),
+                                                act2, epoch, false, st),
                       "decode slice reduction");
         if (rc) return rc;
     } else {
@@ -482,7 +488,9 @@ size_t ffn_swiglu_workspace_size(int64_t M, int64_t N, int64_t O, int64_t P, int
     if (check_dims(M, N, O, P) != FFN_OK) return 0;
     if (dtype != FFN_F32 && dtype != FFN_BF16) return 0;
     const int v = resolve_variant(variant, dtype, M);
-    if (v < FFN_VARIANT_FUSED || v > FFN_VARIANT_F32) return 0;
+    if (v < FFN_VARIANT_FUSED || v > FFN_VARIANT_DECODE) return 0;
+    if (v == FFN_VARIANT_DECODE && (dtype != FFN_BF16 || !ffn::decode_stream_shape(M, N, O, P)))
+        return 0;
     return swiglu_layout(M, N, O, P, v).total;
 }
 
@@ -496,8 +504,6 @@ static int swiglu_forward(const void* X, const void* Wg, const void* Wu, const v
     if (dtype != FFN_F32 && dtype != FFN_BF16) return fail(FFN_EINVAL, "unknown dtype %d", dtype);
     if (variant < FFN_VARIANT_AUTO || variant > FFN_VARIANT_DECODE)
         return fail(FFN_EINVAL, "unknown variant %d", variant);
-    if (variant == FFN_VARIANT_DECODE)
-        return fail(FFN_EUNSUPPORTED, "the SwiGLU form has no decode-stream variant");
     if (!Wu) return fail(FFN_EINVAL, "Wu must not be NULL");
     if (!aligned16(Wu)) return fail(FFN_EALIGN, "Wu is not 16-byte aligned");
     rc = check_common_ptrs(X, Wg, nullptr, Wd, nullptr, Y, workspace, M);
@@ -508,6 +514,16 @@ static int swiglu_forward(const void* X, const void* Wg, const void* Wu, const v
     if (v == FFN_VARIANT_SKINNY && M > ffn::kSkinnyMaxM)
         return fail(FFN_EUNSUPPORTED, "the skinny variant takes M <= %d (got %lld)",
                     ffn::kSkinnyMaxM, (long long)M);
+    if (v == FFN_VARIANT_DECODE) {
+        if (dtype != FFN_BF16 || !ffn::decode_stream_shape(M, N, O, P))
+            return fail(FFN_EUNSUPPORTED,
+                        "the decode variant takes bf16, M <= 16, N = P = 4096 and O a multiple "
+                        "of 256 up to 2048 (got %lld x %lld x %lld x %lld)",
+                        (long long)M, (long long)N, (long long)O, (long long)P);
+        if (ffn::device_cus() != 256)
+            return fail(FFN_EUNSUPPORTED, "the decode variant needs a device of 256 CUs (has %d)",
+                        ffn::device_cus());
+    }
     const SwigluLayout L = swiglu_layout(M, N, O, P, v);
     if (workspace_bytes < L.total)
         return fail(FFN_EWORKSPACE, "workspace has %zu bytes, needs %zu", workspace_bytes, L.total);
@@ -539,6 +555,20 @@ static int swiglu_forward(const void* X, const void* Wg, const void* Wu, const v
         if ((rc = mark(events, n_events, 1, st))) return rc;
         rc = launched(ffn::launch_reduce_splits(part, S, nullptr, 1, Y, 1, M, P, FFN_ACT_NONE, st),
                       "split reduction kernel");
+        if (rc) return rc;
+    } else if (v == FFN_VARIANT_DECODE ||
+               (variant == FFN_VARIANT_AUTO && ffn::decode_stream_shape(M, N, O, P) &&
+                ffn::device_cus() == 256)) {
+        const uint64_t epoch = next_epoch();
+        rc = launched(ffn::launch_decode_stream((const uint16_t*)X, (const uint16_t*)Wg,
+                                                (const uint16_t*)Wu, nullptr, (const uint16_t*)Wd,
+                                                ws, M, O, P, FFN_ACT_NONE, epoch, st),
+                      "gated decode streaming kernel");
+        if (rc) return rc;
+        if ((rc = mark(events, n_events, 1, st))) return rc;
+        rc = launched(ffn::launch_decode_reduce(nullptr, (uint16_t*)Y, ws, M, O, P, FFN_ACT_NONE,
+                                                epoch, true, st),
+                      "decode slice reduction");
         if (rc) return rc;
     } else {
         uint16_t* H = reinterpret_cast<uint16_t*>(ws + L.h);

@@ -26,6 +26,13 @@
 //  * a second kernel sums the 8 slice partials of Y in ascending slice order,
 //    adds b2 and applies act2 (one rounding to bf16).
 //
+// The gated form (SwiGLU: the same post, section "Benchmarks";
+// H = silu(X Wg) * (X Wu), no biases) runs 12 waves per workgroup: waves 0-3
+// the gate product over Wg, waves 4-7 the up product over Wu (each with its
+// own K-block partials), waves 8-11 layer 2 over Wd; the gate and up sums of
+// an element meet in one thread, which forms silu(gate) * up before the
+// single rounding of H.
+//
 // The 256 workgroups fit the 256 CUs at once, so the whole grid is resident
 // while any of it waits.  Waits are between workgroups of one XCD: a producer's
 // stores are complete in the L2 (s_waitcnt vmcnt(0): the L1 is write-through)
@@ -55,19 +62,18 @@ constexpr int kKRows = kDecodeN / kPerXcd;  // layer-1 K rows per workgroup (128
 constexpr int kPCols = kDecodeP / kPerXcd;  // layer-2 output columns per workgroup (128)
 constexpr int kSpin = 1 << 20;              // polls before a wait gives up (~1 s)
 constexpr int kCpolSc1 = 16;                // buffer cache-policy bits: sc1 (device scope)
-// W2's loads start with the kernel (false) or once layer 1's MFMAs are done,
-// leaving the first microseconds of bandwidth to W1 (true)
-constexpr bool kW2AfterLayer1 = false;
 static_assert(kKRows == 4 * 32, "one 32-deep MFMA step per wave of a layer-1 workgroup");
 static_assert(kPCols == 128, "a layer-2 workgroup covers one 128-column load block");
 static_assert(16 * kPCols / 4 == 2 * kThreads, "one float4 of the slice partial per thread");
 
 struct DecodeArgs {
     const uint16_t* X;
-    const uint16_t* W1;
+    const uint16_t* W1;   // gated form: the gate matrix Wg
+    const uint16_t* W1u;  // gated form: the up matrix Wu
     const uint16_t* b1;
     const uint16_t* W2;
     float* part1;       // [256][16][ox]: K-block partials of layer 1, by (x, j)
+    float* part1u;      // gated form: the same for the up product
     uint16_t* H;        // [16][O]
     float* part2;       // [8][16][P]: slice partials of layer 2
     uint64_t* flags;    // [2][256]: K block written, H columns written
@@ -119,25 +125,31 @@ __device__ __forceinline__ void fail(uint64_t* status, uint64_t epoch) {
         __hip_atomic_store(status, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One workgroup of 8 waves per CU, workgroup b on XCD x = b mod 8 with index
-// j = b / 8 there.  Waves 0-3 compute layer 1 of K block j over slice x: wave
-// w takes K rows [128 j + 32 w, +32); lane (g, c) loads rows +8g .. +8g+7 of
-// the 8 columns 8c .. 8c+7 of each 128-column block of the slice, transposes
-// them in registers into the MFMA's k-contiguous operand and multiplies the
-// matching X fragment.  Waves 4-7 hold the workgroup's part of W2 (slice x's
-// rows, output columns [128 j, +128)): wave 4 + w takes the slice's 32-row K
-// steps w and w + 4 (when there is one).  Only waves 0-3 store and then wait
-// for their stores (s_waitcnt vmcnt(0)), so those waits never include the W2
-// stream of waves 4-7.
-__global__ __launch_bounds__(2 * kThreads) void decode_stream_kernel(DecodeArgs a) {
-    __shared__ __attribute__((aligned(16))) float red[4 * 16 * 256];
+// One workgroup per CU, workgroup b on XCD x = b mod 8 with index j = b / 8
+// there.  The layer-1 waves compute layer 1 of K block j over slice x: wave
+// w of a group of four takes K rows [128 j + 32 w, +32); lane (g, c) loads
+// rows +8g .. +8g+7 of the 8 columns 8c .. 8c+7 of each 128-column block of
+// the slice, transposes them in registers into the MFMA's k-contiguous
+// operand and multiplies the matching X fragment.  Plain form: waves 0-3
+// (W1); gated form (SwiGLU, the kernel-fusion post's "Benchmarks" section:
+// H = silu(X Wg) * X Wu, no biases): waves 0-3 the gate product (Wg), waves
+// 4-7 the up product (Wu).  The last four waves hold the workgroup's part of
+// W2 (slice x's rows, output columns [128 j, +128)): wave w of them takes the
+// slice's 32-row K steps w and w + 4 (when there is one).  Only layer-1
+// waves store and then wait for their stores (s_waitcnt vmcnt(0)), so those
+// waits never include the W2 stream of the layer-2 waves.
+template <bool kGated>
+__global__ __launch_bounds__((kGated ? 3 : 2) * kThreads) void decode_stream_kernel(DecodeArgs a) {
+    constexpr int kL1Waves = kGated ? 8 : 4;
+    __shared__ __attribute__((aligned(16))) float red[(kGated ? 2 : 1) * 4 * 16 * 256];
     __shared__ int ok_lds;
     const int tid = threadIdx.x;
     const int wave = tid >> 6;
     const int lane = tid & 63;
     const int g = lane >> 4;
     const int c = lane & 15;
-    const bool l1 = wave < 4;   // layer-1 waves; waves 4-7 run layer 2
+    const bool l1 = wave < kL1Waves;     // layer-1 waves; the last four run layer 2
+    const bool up = kGated && wave >= 4 && wave < 8;
     const int w = wave & 3;
     const int x = blockIdx.x % kXcds;
     const int j = blockIdx.x / kXcds;
@@ -145,11 +157,25 @@ __global__ __launch_bounds__(2 * kThreads) void decode_stream_kernel(DecodeArgs 
     const int nks = ox / 32;    // 32-row K steps of layer 2 (the slice's rows)
     const int64_t O = a.O;
     const int64_t P = a.P;
-    if (xcc_id() != x) fail(a.status, a.epoch);   // the exchange would not be coherent
+    float* myred = red + (up ? 4 * 16 * 256 : 0);   // this wave's product's LDS sums
+    if (xcc_id() != x) fail(a.status, a.epoch);    // the exchange would not be coherent
 
     uint4 wr[2][8];
     uint4 af = zero16();
-    auto load_w2 = [&]() {
+    if (l1) {
+        const int64_t k = (int64_t)j * kKRows + 32 * w + 8 * g;
+        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X, a.M * kDecodeN * 2);
+        const __amdgpu_buffer_rsrc_t rw = make_rsrc(up ? a.W1u : a.W1, kDecodeN * O * 2);
+        af = bload16(rx, c < a.M ? (uint32_t)((c * kDecodeN + k) * 2) : kOOB);
+#pragma unroll
+        for (int cb = 0; cb < 2; ++cb) {
+            const int cl = cb * 128 + 8 * c;   // column inside the slice
+            const int64_t col = (int64_t)x * ox + cl;
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+                wr[cb][i] = bload16(rw, cl < ox ? (uint32_t)(((k + i) * O + col) * 2) : kOOB);
+        }
+    } else {
         const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.W2, O * P * 2);
         const int64_t col = (int64_t)j * kPCols + 8 * c;
 #pragma unroll
@@ -160,25 +186,9 @@ __global__ __launch_bounds__(2 * kThreads) void decode_stream_kernel(DecodeArgs 
             for (int i = 0; i < 8; ++i)
                 wr[s][i] = bload16(rw, ks < nks ? (uint32_t)(((n + i) * P + col) * 2) : kOOB);
         }
-    };
-    if (l1) {
-        const int64_t k = (int64_t)j * kKRows + 32 * w + 8 * g;
-        const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X, a.M * kDecodeN * 2);
-        const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.W1, kDecodeN * O * 2);
-        af = bload16(rx, c < a.M ? (uint32_t)((c * kDecodeN + k) * 2) : kOOB);
-#pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            const int cl = cb * 128 + 8 * c;   // column inside the slice
-            const int64_t col = (int64_t)x * ox + cl;
-#pragma unroll
-            for (int i = 0; i < 8; ++i)
-                wr[cb][i] = bload16(rw, cl < ox ? (uint32_t)(((k + i) * O + col) * 2) : kOOB);
-        }
-    } else if (!kW2AfterLayer1) {
-        load_w2();
     }
 
-    // ---- layer 1: this K block's share of slice x of X W1
+    // ---- layer 1: this K block's share of slice x of X W1 (gated: of X Wg and X Wu)
     if (l1) {
         floatx4_t acc[2][8];
 #pragma unroll
@@ -189,12 +199,12 @@ __global__ __launch_bounds__(2 * kThreads) void decode_stream_kernel(DecodeArgs 
             for (int q = 0; q < 8; ++q)
                 acc[cb][q] = mfma16x16x32(af, cv[q], floatx4_t{0.f, 0.f, 0.f, 0.f});
         }
-        // acc[cb][q][r] = wave w's share of H[4g + r][cb * 128 + 8c + q]
+        // acc[cb][q][r] = wave w's share of [4g + r][cb * 128 + 8c + q]
 #pragma unroll
         for (int cb = 0; cb < 2; ++cb)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
-                float* dst = red + (w * 16 + 4 * g + r) * 256 + cb * 128 + 8 * c;
+                float* dst = myred + (w * 16 + 4 * g + r) * 256 + cb * 128 + 8 * c;
                 *reinterpret_cast<float4*>(dst) =
                     make_float4(acc[cb][0][r], acc[cb][1][r], acc[cb][2][r], acc[cb][3][r]);
                 *reinterpret_cast<float4*>(dst + 4) =
@@ -202,14 +212,13 @@ __global__ __launch_bounds__(2 * kThreads) void decode_stream_kernel(DecodeArgs 
             }
     }
     __syncthreads();
-    if (!l1 && kW2AfterLayer1) load_w2();
     if (l1) {
         // the K block's partial: the four waves' 32-row sums added in wave order
-        float* mine = a.part1 + (int64_t)(x * kPerXcd + j) * 16 * ox;
-        for (int e = 4 * tid; e < 16 * ox; e += 4 * kThreads) {
+        float* mine = (up ? a.part1u : a.part1) + (int64_t)(x * kPerXcd + j) * 16 * ox;
+        for (int e = 4 * (tid & (kThreads - 1)); e < 16 * ox; e += 4 * kThreads) {
             const int m = e / ox;
             const int cl = e - m * ox;
-            const float* s = red + m * 256 + cl;
+            const float* s = myred + m * 256 + cl;
             const float4 s0 = *reinterpret_cast<const float4*>(s);
             const float4 s1 = *reinterpret_cast<const float4*>(s + 16 * 256);
             const float4 s2 = *reinterpret_cast<const float4*>(s + 2 * 16 * 256);
@@ -224,37 +233,62 @@ __global__ __launch_bounds__(2 * kThreads) void decode_stream_kernel(DecodeArgs 
     set_flag(a.flags + x * kPerXcd + j, a.epoch);
 
     // ---- every K block of slice x is in the L2: finish 1/32 of slice x of H
-    // (16 * ox / 32 consecutive elements of the row-major [16][ox] slice, four
-    // per thread: each element's 32 K-block partials added in ascending order)
+    // (16 * ox / 32 consecutive elements of the row-major [16][ox] slice, kEl
+    // per thread: each element's 32 K-block partials added in ascending order;
+    // gated: wave 0 sums the gate partials, wave 1 the up partials, two
+    // elements per thread so that 32 loads in flight fit the registers of 12 waves)
     const bool ok1 = wait_flags(a.flags + x * kPerXcd, a.epoch, &ok_lds);
-    if (tid < ox / 8) {   // wave 0: no loads of its own outstanding
-        const int e = j * (ox / 2) + 4 * tid;
-        const int m = e / ox;
-        const int cl = e - m * ox;
-        const __amdgpu_buffer_rsrc_t rp =
-            make_rsrc(a.part1 + (int64_t)(x * kPerXcd) * 16 * ox, (int64_t)kPerXcd * 16 * ox * 4);
-        float4 t[kPerXcd];
+    {
+        constexpr int kEl = kGated ? 2 : 4;
+        typedef float vec_t __attribute__((ext_vector_type(kEl)));
+        const int rt = tid & 63;         // waves 0-1: no loads of their own outstanding
+        const bool rsum = rt < ox / (2 * kEl) && (wave == 0 || (kGated && wave == 1));
+        const int e = j * (ox / 2) + kEl * rt;
+        vec_t v = {};
+        if (rsum) {
+            const float* src = wave == 1 ? a.part1u : a.part1;
+            const __amdgpu_buffer_rsrc_t rp = make_rsrc(src + (int64_t)(x * kPerXcd) * 16 * ox,
+                                                        (int64_t)kPerXcd * 16 * ox * 4);
+            vec_t t[kPerXcd];
 #pragma unroll
-        for (int q = 0; q < kPerXcd; ++q)   // written by other CUs: device-scope (sc1) loads
-            t[q] = __builtin_bit_cast(float4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                  rp, (uint32_t)((q * 16 * ox + e) * 4), 0, kCpolSc1));
-        float v[4] = {t[0].x, t[0].y, t[0].z, t[0].w};
+            for (int q = 0; q < kPerXcd; ++q) {   // written by other CUs: device-scope (sc1) loads
+                const uint32_t off = (uint32_t)((q * 16 * ox + e) * 4);
+                if constexpr (kEl == 4)
+                    t[q] = __builtin_bit_cast(vec_t, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kCpolSc1));
+                else
+                    t[q] = __builtin_bit_cast(vec_t, __builtin_amdgcn_raw_buffer_load_b64(rp, off, 0, kCpolSc1));
+            }
+            v = t[0];
 #pragma unroll
-        for (int q = 1; q < kPerXcd; ++q) {
-            v[0] += t[q].x;
-            v[1] += t[q].y;
-            v[2] += t[q].z;
-            v[3] += t[q].w;
+            for (int q = 1; q < kPerXcd; ++q) v += t[q];
         }
-        const int64_t col = (int64_t)x * ox + cl;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            if (a.b1) v[i] += bf16_to_f32(a.b1[col + i]);
-            v[i] = ok1 ? apply_act(a.act1, v[i]) : __builtin_nanf("");
+        if constexpr (kGated) {
+            // the up sums go to wave 0 through LDS (red is free again: every
+            // layer-1 wave finished reading it before the flag above)
+            if (rsum && wave == 1) *reinterpret_cast<vec_t*>(red + kEl * rt) = v;
+            __syncthreads();
         }
-        *reinterpret_cast<uint2*>(a.H + m * O + col) =
-            make_uint2(pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3]));
-        wait_vmcnt<0>();
+        if (rsum && wave == 0) {
+            const int m = e / ox;
+            const int64_t col = (int64_t)x * ox + (e - m * ox);
+            float h[kEl];
+            if constexpr (kGated) {
+                const vec_t u = *reinterpret_cast<const vec_t*>(red + kEl * rt);
+#pragma unroll
+                for (int i = 0; i < kEl; ++i) h[i] = ok1 ? silu(v[i]) * u[i] : __builtin_nanf("");
+            } else {
+#pragma unroll
+                for (int i = 0; i < kEl; ++i) {
+                    float z = v[i];
+                    if (a.b1) z += bf16_to_f32(a.b1[col + i]);
+                    h[i] = ok1 ? apply_act(a.act1, z) : __builtin_nanf("");
+                }
+            }
+            uint32_t* dst = reinterpret_cast<uint32_t*>(a.H + m * O + col);
+#pragma unroll
+            for (int i = 0; i < kEl / 2; ++i) dst[i] = pack_bf16x2(h[2 * i], h[2 * i + 1]);
+            wait_vmcnt<0>();
+        }
     }
     if (!ok1) fail(a.status, a.epoch);
     __syncthreads();
@@ -291,20 +325,20 @@ __global__ __launch_bounds__(2 * kThreads) void decode_stream_kernel(DecodeArgs 
     }
     __syncthreads();
     // slice x's partial of Y: the four layer-2 waves' sums added in wave order
-    // (16 x 128 values, four per thread)
-    {
-        const int m = tid / (kPCols / 4);
-        const int cl = (tid - m * (kPCols / 4)) * 4;
-        const float* s = red + m * 128 + cl;
+    // (16 x 128 values, four per thread of the first 512)
+    if (tid < 2 * kThreads) {
+        const int mm = tid / (kPCols / 4);
+        const int cc = (tid - mm * (kPCols / 4)) * 4;
+        const float* s = red + mm * 128 + cc;
         const float4 s0 = *reinterpret_cast<const float4*>(s);
         const float4 s1 = *reinterpret_cast<const float4*>(s + 16 * 128);
         const float4 s2 = *reinterpret_cast<const float4*>(s + 2 * 16 * 128);
         const float4 s3 = *reinterpret_cast<const float4*>(s + 3 * 16 * 128);
-        float4 v = make_float4(((s0.x + s1.x) + s2.x) + s3.x, ((s0.y + s1.y) + s2.y) + s3.y,
+        float4 y = make_float4(((s0.x + s1.x) + s2.x) + s3.x, ((s0.y + s1.y) + s2.y) + s3.y,
                                ((s0.z + s1.z) + s2.z) + s3.z, ((s0.w + s1.w) + s2.w) + s3.w);
-        if (!ok2) v = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
+        if (!ok2) y = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
                                   __builtin_nanf(""));
-        *reinterpret_cast<float4*>(a.part2 + ((int64_t)x * 16 + m) * P + (int64_t)j * kPCols + cl) = v;
+        *reinterpret_cast<float4*>(a.part2 + ((int64_t)x * 16 + mm) * P + (int64_t)j * kPCols + cc) = y;
     }
     if (!ok2) fail(a.status, a.epoch);
 }
@@ -355,7 +389,7 @@ bool decode_stream_shape(int64_t M, int64_t N, int64_t O, int64_t P) {
            O >= 256 && O <= 2048;
 }
 
-DecodeStreamLayout decode_stream_layout(int64_t O, int64_t P) {
+DecodeStreamLayout decode_stream_layout(int64_t O, int64_t P, bool gated) {
     DecodeStreamLayout L;
     size_t off = 0;
     auto take = [&off](size_t bytes) {
@@ -363,7 +397,9 @@ DecodeStreamLayout decode_stream_layout(int64_t O, int64_t P) {
         off += (bytes + 255) & ~(size_t)255;
         return at;
     };
-    L.part1 = take(sizeof(float) * kRoleWgs * 16 * (size_t)(O / kXcds));
+    const size_t part1 = sizeof(float) * kRoleWgs * 16 * (size_t)(O / kXcds);
+    L.part1 = take(part1);
+    L.part1u = gated ? take(part1) : L.part1;
     L.h = take(sizeof(uint16_t) * 16 * (size_t)O);
     L.part2 = take(sizeof(float) * kXcds * 16 * (size_t)P);
     L.flags = take(sizeof(uint64_t) * 2 * kRoleWgs);
@@ -372,16 +408,20 @@ DecodeStreamLayout decode_stream_layout(int64_t O, int64_t P) {
     return L;
 }
 
-hipError_t launch_decode_stream(const uint16_t* X, const uint16_t* W1, const uint16_t* b1,
-                                const uint16_t* W2, char* ws, int64_t M, int64_t O, int64_t P,
-                                int act1, uint64_t epoch, hipStream_t stream) {
-    const DecodeStreamLayout L = decode_stream_layout(O, P);
+hipError_t launch_decode_stream(const uint16_t* X, const uint16_t* W1, const uint16_t* W1u,
+                                const uint16_t* b1, const uint16_t* W2, char* ws, int64_t M,
+                                int64_t O, int64_t P, int act1, uint64_t epoch,
+                                hipStream_t stream) {
+    const bool gated = W1u != nullptr;
+    const DecodeStreamLayout L = decode_stream_layout(O, P, gated);
     DecodeArgs a;
     a.X = X;
     a.W1 = W1;
+    a.W1u = W1u;
     a.b1 = b1;
     a.W2 = W2;
     a.part1 = reinterpret_cast<float*>(ws + L.part1);
+    a.part1u = reinterpret_cast<float*>(ws + L.part1u);
     a.H = reinterpret_cast<uint16_t*>(ws + L.h);
     a.part2 = reinterpret_cast<float*>(ws + L.part2);
     a.flags = reinterpret_cast<uint64_t*>(ws + L.flags);
@@ -392,13 +432,19 @@ hipError_t launch_decode_stream(const uint16_t* X, const uint16_t* W1, const uin
     a.ox = (int)(O / kXcds);
     a.act1 = act1;
     a.epoch = epoch;
-    hipLaunchKernelGGL(decode_stream_kernel, dim3(kRoleWgs), dim3(2 * kThreads), 0, stream, a);
+    if (gated)
+        hipLaunchKernelGGL(decode_stream_kernel<true>, dim3(kRoleWgs), dim3(3 * kThreads), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL(decode_stream_kernel<false>, dim3(kRoleWgs), dim3(2 * kThreads), 0,
+                           stream, a);
     return hipGetLastError();
 }
 
 hipError_t launch_decode_reduce(const uint16_t* b2, uint16_t* Y, char* ws, int64_t M, int64_t O,
-                                int64_t P, int act2, uint64_t epoch, hipStream_t stream) {
-    const DecodeStreamLayout L = decode_stream_layout(O, P);
+                                int64_t P, int act2, uint64_t epoch, bool gated,
+                                hipStream_t stream) {
+    const DecodeStreamLayout L = decode_stream_layout(O, P, gated);
     const int64_t nvec = M * (P / 4);
     hipLaunchKernelGGL(decode_reduce_kernel, dim3((unsigned)((nvec + 63) / 64)), dim3(64), 0,
                        stream, reinterpret_cast<const float*>(ws + L.part2),

@@ -94,14 +94,17 @@ constexpr int64_t kDecodeN = 4096;
 constexpr int64_t kDecodeP = 4096;
 bool decode_stream_shape(int64_t M, int64_t N, int64_t O, int64_t P);
 struct DecodeStreamLayout {   // workspace byte offsets, 256-byte aligned
-    size_t part1, h, part2, flags, status, total;
+    size_t part1, part1u, h, part2, flags, status, total;
 };
-DecodeStreamLayout decode_stream_layout(int64_t O, int64_t P);
-hipError_t launch_decode_stream(const uint16_t* X, const uint16_t* W1, const uint16_t* b1,
-                                const uint16_t* W2, char* ws, int64_t M, int64_t O, int64_t P,
-                                int act1, uint64_t epoch, hipStream_t stream);
+DecodeStreamLayout decode_stream_layout(int64_t O, int64_t P, bool gated);
+// W1u != nullptr: the gated (SwiGLU) form, W1 = Wg, W1u = Wu, W2 = Wd, no bias
+hipError_t launch_decode_stream(const uint16_t* X, const uint16_t* W1, const uint16_t* W1u,
+                                const uint16_t* b1, const uint16_t* W2, char* ws, int64_t M,
+                                int64_t O, int64_t P, int act1, uint64_t epoch,
+                                hipStream_t stream);
 hipError_t launch_decode_reduce(const uint16_t* b2, uint16_t* Y, char* ws, int64_t M, int64_t O,
-                                int64_t P, int act2, uint64_t epoch, hipStream_t stream);
+                                int64_t P, int act2, uint64_t epoch, bool gated,
+                                hipStream_t stream);
 
 // ---- skinny (M <= 16) bf16 layer with a fixed-order split-K reduction
 
