@@ -308,6 +308,16 @@ int ffn_ceiling_read(const void* src, size_t bytes, void* sink, size_t sink_byte
  * the number of the first failed check.  Makes no HIP call. */
 int ffn_selftest_layout(void);
 
+/* Self-test of the decode stream's failure path (FFN_VARIANT_DECODE): as
+ * ffn_forward_ex with that variant and bf16 data, but the workgroups' flags
+ * never hold the call's number and every wait gives up after 64 polls, so
+ * the call must write NaN to every element of Y (what a wait that expires in
+ * a real call does).  Every kernel ends normally.  For tests only. */
+int ffn_selftest_decode_expiry(const void* X, const void* W1, const void* b1, const void* W2,
+                               const void* b2, void* Y, int64_t M, int64_t N, int64_t O,
+                               int64_t P, int act1, int act2, void* workspace,
+                               size_t workspace_bytes, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -314,3 +314,14 @@ def test_gated_decode_stream_workspace_sizes():
     assert S(16, 4096, 1792, 4096) == max(dec, S(16, 4096, 1792, 4096, ffn.BF16, ffn.VARIANT_SKINNY))
     assert S(16, 4096, 1920, 4096, ffn.BF16, ffn.VARIANT_DECODE) == 0
     assert _swiglu(M=16, N=4096, O=1792, P=4096, variant=ffn.VARIANT_DECODE, wsb=dec - 1) == E_WS
+
+
+def test_decode_expiry_selftest_checks_its_arguments():
+    L = ffn.lib()
+    # not a decode-stream shape: refused on the host before any launch
+    rc = L.ffn_selftest_decode_expiry(FAKE, FAKE, None, FAKE, None, FAKE2, 16, 1024, 896, 1024, 2, 0,
+                                      FAKE, 1 << 30, None)
+    assert rc == E_UNSUP, (rc, ffn.ffn_last_error())
+    rc = L.ffn_selftest_decode_expiry(FAKE, FAKE, None, FAKE, None, FAKE2, 16, 4096, 1792, 4096, 2, 0,
+                                      FAKE, 0, None)
+    assert rc == E_WS, (rc, ffn.ffn_last_error())

@@ -165,3 +165,29 @@ def test_gated_decode_stream_is_the_default_and_matches_skinny():
         compare(host_f64(outs[0]), ref, BF16_TOL, f"variant {v}")
         got[v] = outs[0]
     assert torch.equal(got[ffn.VARIANT_AUTO], got[ffn.VARIANT_DECODE])
+
+
+def test_decode_stream_expired_wait_poisons_output():
+    """The failure path, forced from the host: the self-test entry point runs the
+    call with flags that never match and waits of 64 polls, so every wait
+    expires; Y must be NaN everywhere, and the next call on the same workspace
+    must be right again."""
+    import torch
+    c = workload.DECODE
+    log(f"case decode stream, expired waits ({c.name})")
+    host = _inputs(c.M, c.N, c.O, c.P, seed=61)
+    X, W1, b1, W2, b2 = _dev(host)
+    Y = torch.zeros((c.M, c.P), dtype=torch.bfloat16, device="cuda")
+    ws = ffn.workspace(ffn.ffn_workspace_size(c.M, c.N, c.O, c.P, ffn.BF16, ffn.VARIANT_DECODE))
+    stream = torch.cuda.current_stream().cuda_stream
+    rc = ffn.lib().ffn_selftest_decode_expiry(X.data_ptr(), W1.data_ptr(), b1.data_ptr(),
+                                              W2.data_ptr(), b2.data_ptr(), Y.data_ptr(), c.M, c.N,
+                                              c.O, c.P, ffn.ACT_GELU_TANH, ffn.ACT_NONE,
+                                              ws.data_ptr(), ws.numel(), stream)
+    assert rc == 0, ffn.ffn_last_error()
+    torch.cuda.synchronize()
+    assert bool(torch.isnan(Y.float()).all()), "an expired wait must poison every element"
+    Y2 = torch.empty_like(Y)
+    _call([X, W1, b1, W2, b2], Y2, ws)
+    torch.cuda.synchronize()
+    compare(host_f64(Y2), _ref(host), BF16_TOL, "the call after the expired one")

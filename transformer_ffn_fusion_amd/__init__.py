@@ -101,6 +101,9 @@ def lib():
         L.ffn_last_error.restype = ctypes.c_char_p
         L.ffn_version.restype = i32
         L.ffn_selftest_layout.restype = i32
+        L.ffn_selftest_decode_expiry.argtypes = [vp, vp, vp, vp, vp, vp, i64, i64, i64, i64, i32,
+                                                 i32, vp, sz, vp]
+        L.ffn_selftest_decode_expiry.restype = i32
         L.ffn_ceiling_sink_bytes.argtypes = []
         L.ffn_ceiling_sink_bytes.restype = sz
         L.ffn_ceiling_mfma.argtypes = [vp, sz, i32, ctypes.POINTER(ctypes.c_double), vp]

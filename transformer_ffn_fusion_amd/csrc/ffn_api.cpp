@@ -279,7 +279,8 @@ static int mark(void** events, int n_events, int i, hipStream_t st) {
 static int dense_forward(const void* X, const void* W1, const void* b1, const void* W2,
                          const void* b2, void* Y, int64_t M, int64_t N, int64_t O, int64_t P,
                          int dtype, int act1, int act2, int variant, void* workspace,
-                         size_t workspace_bytes, void* stream, void** events, int n_events) {
+                         size_t workspace_bytes, void* stream, void** events, int n_events,
+                         bool expire = false) {
     if (events && n_events < 3) return fail(FFN_EINVAL, "traced calls take at least 3 events");
     int rc = check_dims(M, N, O, P);
     if (rc) return rc;
@@ -343,7 +344,7 @@ static int dense_forward(const void* X, const void* W1, const void* b1, const vo
         const uint64_t epoch = next_epoch();
         rc = launched(ffn::launch_decode_stream((const uint16_t*)X, (const uint16_t*)W1, nullptr,
                                                 (const uint16_t*)b1, (const uint16_t*)W2, ws, M,
-                                                O, P, act1, epoch, st),
+                                                O, P, act1, epoch, st, expire),
                       "decode streaming kernel");
         if (rc) return rc;
         if ((rc = mark(events, n_events, 1, st))) return rc;
@@ -867,6 +868,14 @@ int ffn_ceiling_read(const void* src, size_t bytes, void* sink, size_t sink_byte
                                                reinterpret_cast<hipStream_t>(stream)),
                       "read ceiling kernel");
     return rc ? rc : ok();
+}
+
+int ffn_selftest_decode_expiry(const void* X, const void* W1, const void* b1, const void* W2,
+                               const void* b2, void* Y, int64_t M, int64_t N, int64_t O,
+                               int64_t P, int act1, int act2, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+    return dense_forward(X, W1, b1, W2, b2, Y, M, N, O, P, FFN_BF16, act1, act2,
+                         FFN_VARIANT_DECODE, workspace, workspace_bytes, stream, nullptr, 0, true);
 }
 
 int ffn_selftest_layout(void) {

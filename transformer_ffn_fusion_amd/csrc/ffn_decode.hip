@@ -81,7 +81,9 @@ struct DecodeArgs {
     int64_t M, O, P;
     int ox;             // hidden columns per XCD slice (O / 8)
     int act1;
+    int spin;           // polls before a wait gives up
     uint64_t epoch;
+    uint64_t flag_xor;  // 0; nonzero only in the self-test of the expiry path
 };
 
 __device__ __forceinline__ int xcc_id() {
@@ -91,19 +93,19 @@ __device__ __forceinline__ int xcc_id() {
 
 // Marks this workgroup's step done.  All of its stores must be complete
 // (every thread: s_waitcnt vmcnt(0), then a workgroup barrier) before.
-__device__ __forceinline__ void set_flag(uint64_t* flag, uint64_t epoch) {
+__device__ __forceinline__ void set_flag(uint64_t* flag, uint64_t value) {
     if (threadIdx.x == 0)
-        __hip_atomic_store(flag, epoch, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        __hip_atomic_store(flag, value, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
 }
 
 // Waits until the 32 flags of one XCD hold `epoch` (wave 0 polls, one flag
 // per lane, with device-scope loads that skip the L1).  Returns false if the
 // wait expired.
-__device__ bool wait_flags(const uint64_t* flags, uint64_t epoch, int* ok_lds) {
+__device__ bool wait_flags(const uint64_t* flags, uint64_t epoch, int spin, int* ok_lds) {
     if (threadIdx.x < 64) {
         const int lane = threadIdx.x;
         bool done = false;
-        for (int it = 0; it < kSpin; ++it) {
+        for (int it = 0; it < spin; ++it) {
             const uint64_t v = lane < kPerXcd
                                    ? __hip_atomic_load(flags + lane, __ATOMIC_RELAXED,
                                                        __HIP_MEMORY_SCOPE_AGENT)
@@ -230,14 +232,14 @@ __global__ __launch_bounds__((kGated ? 3 : 2) * kThreads) void decode_stream_ker
         wait_vmcnt<0>();
     }
     __syncthreads();
-    set_flag(a.flags + x * kPerXcd + j, a.epoch);
+    set_flag(a.flags + x * kPerXcd + j, a.epoch ^ a.flag_xor);
 
     // ---- every K block of slice x is in the L2: finish 1/32 of slice x of H
     // (16 * ox / 32 consecutive elements of the row-major [16][ox] slice, kEl
     // per thread: each element's 32 K-block partials added in ascending order;
     // gated: wave 0 sums the gate partials, wave 1 the up partials, two
     // elements per thread so that 32 loads in flight fit the registers of 12 waves)
-    const bool ok1 = wait_flags(a.flags + x * kPerXcd, a.epoch, &ok_lds);
+    const bool ok1 = wait_flags(a.flags + x * kPerXcd, a.epoch, a.spin, &ok_lds);
     {
         constexpr int kEl = kGated ? 2 : 4;
         typedef float vec_t __attribute__((ext_vector_type(kEl)));
@@ -292,10 +294,10 @@ __global__ __launch_bounds__((kGated ? 3 : 2) * kThreads) void decode_stream_ker
     }
     if (!ok1) fail(a.status, a.epoch);
     __syncthreads();
-    set_flag(a.flags + kRoleWgs + x * kPerXcd + j, a.epoch);
+    set_flag(a.flags + kRoleWgs + x * kPerXcd + j, a.epoch ^ a.flag_xor);
 
     // ---- slice x of H is complete: layer 2 over it
-    const bool ok2 = wait_flags(a.flags + kRoleWgs + x * kPerXcd, a.epoch, &ok_lds);
+    const bool ok2 = wait_flags(a.flags + kRoleWgs + x * kPerXcd, a.epoch, a.spin, &ok_lds);
     if (!l1) {
         const __amdgpu_buffer_rsrc_t rh = make_rsrc(a.H, 16 * O * 2);
         floatx4_t acc[8];
@@ -411,7 +413,7 @@ DecodeStreamLayout decode_stream_layout(int64_t O, int64_t P, bool gated) {
 hipError_t launch_decode_stream(const uint16_t* X, const uint16_t* W1, const uint16_t* W1u,
                                 const uint16_t* b1, const uint16_t* W2, char* ws, int64_t M,
                                 int64_t O, int64_t P, int act1, uint64_t epoch,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool expire) {
     const bool gated = W1u != nullptr;
     const DecodeStreamLayout L = decode_stream_layout(O, P, gated);
     DecodeArgs a;
@@ -432,6 +434,9 @@ hipError_t launch_decode_stream(const uint16_t* X, const uint16_t* W1, const uin
     a.ox = (int)(O / kXcds);
     a.act1 = act1;
     a.epoch = epoch;
+    // the expiry self-test: flags that never hold the epoch, waits of 64 polls
+    a.spin = expire ? 64 : kSpin;
+    a.flag_xor = expire ? 1 : 0;
     if (gated)
         hipLaunchKernelGGL(decode_stream_kernel<true>, dim3(kRoleWgs), dim3(3 * kThreads), 0,
                            stream, a);

@@ -97,11 +97,12 @@ struct DecodeStreamLayout {   // workspace byte offsets, 256-byte aligned
     size_t part1, part1u, h, part2, flags, status, total;
 };
 DecodeStreamLayout decode_stream_layout(int64_t O, int64_t P, bool gated);
-// W1u != nullptr: the gated (SwiGLU) form, W1 = Wg, W1u = Wu, W2 = Wd, no bias
+// W1u != nullptr: the gated (SwiGLU) form, W1 = Wg, W1u = Wu, W2 = Wd, no bias.
+// expire: the self-test of the failure path (every wait expires, Y becomes NaN).
 hipError_t launch_decode_stream(const uint16_t* X, const uint16_t* W1, const uint16_t* W1u,
                                 const uint16_t* b1, const uint16_t* W2, char* ws, int64_t M,
                                 int64_t O, int64_t P, int act1, uint64_t epoch,
-                                hipStream_t stream);
+                                hipStream_t stream, bool expire = false);
 hipError_t launch_decode_reduce(const uint16_t* b2, uint16_t* Y, char* ws, int64_t M, int64_t O,
                                 int64_t P, int act2, uint64_t epoch, bool gated,
                                 hipStream_t stream);
