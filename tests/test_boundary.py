@@ -94,10 +94,10 @@ def test_workspace_one_byte_short_is_rejected():
 
 
 def test_decode_stream_workspace_sizes():
-    # [256][16][O/8] fp32 K-block partials, 16 x O bf16 H, [8][16][P] fp32 slice
+    # [8][16][16][O/8] fp32 K-block partials, 16 x O bf16 H, [8][16][P] fp32 slice
     # partials, 2 x 256 flags and a status word, each region 256-byte aligned
     dec = ffn.ffn_workspace_size(16, 4096, 1792, 4096, ffn.BF16, ffn.VARIANT_DECODE)
-    assert dec == 256 * 16 * 224 * 4 + 16 * 1792 * 2 + 8 * 16 * 4096 * 4 + 2 * 256 * 8 + 256
+    assert dec == 128 * 16 * 224 * 4 + 16 * 1792 * 2 + 8 * 16 * 4096 * 4 + 2 * 256 * 8 + 256
     skinny_only = ffn.ffn_workspace_size(16, 4096, 1792, 4096, ffn.BF16, ffn.VARIANT_SKINNY)
     auto = ffn.ffn_workspace_size(16, 4096, 1792, 4096)
     assert auto == max(dec, skinny_only)          # AUTO may take either path
@@ -310,7 +310,7 @@ def test_gated_decode_stream_workspace_sizes():
     S = ffn.ffn_swiglu_workspace_size
     dec = S(16, 4096, 1792, 4096, ffn.BF16, ffn.VARIANT_DECODE)
     # gate and up K-block partials, H, slice partials, flags, status
-    assert dec == 2 * 256 * 16 * 224 * 4 + 16 * 1792 * 2 + 8 * 16 * 4096 * 4 + 2 * 256 * 8 + 256
+    assert dec == 2 * 128 * 16 * 224 * 4 + 16 * 1792 * 2 + 8 * 16 * 4096 * 4 + 2 * 256 * 8 + 256
     assert S(16, 4096, 1792, 4096) == max(dec, S(16, 4096, 1792, 4096, ffn.BF16, ffn.VARIANT_SKINNY))
     assert S(16, 4096, 1920, 4096, ffn.BF16, ffn.VARIANT_DECODE) == 0
     assert _swiglu(M=16, N=4096, O=1792, P=4096, variant=ffn.VARIANT_DECODE, wsb=dec - 1) == E_WS

@@ -13,11 +13,12 @@
 // stays inside one XCD:
 //
 //  * 256 workgroups of 8 waves, one per CU; workgroup (x, j) (x = b mod 8,
-//    j = b / 8) runs on XCD x.  Its waves 0-3 multiply rows [128 j, +128) of
-//    X and W1 over slice x's columns and write that K block's fp32 partial;
-//    once all 32 K blocks of the slice are in the XCD's L2, the workgroup sums
-//    1/32 of the slice's elements over the 32 K blocks in ascending order,
-//    adds b1, applies act1 and writes them to H in bf16 (one rounding);
+//    j = b / 8) runs on XCD x.  Its waves 0-3 multiply rows [256 (j / 2),
+//    +256) of X and W1 over one half (j mod 2) of slice x's columns and write
+//    that K block's fp32 partial of the half; once all 16 K blocks of the
+//    slice are in the XCD's L2, the workgroup sums 1/32 of the slice's
+//    elements over the 16 K blocks in ascending order, adds b1, applies act1
+//    and writes them to H in bf16 (one rounding);
 //  * its waves 4-7 load the workgroup's part of W2 (slice x's rows, output
 //    columns [128 j, 128 j + 128)) into registers as soon as they start --
 //    W2 does not depend on H, so both weights stream from the first
@@ -58,11 +59,12 @@ constexpr int kXcds = 8;
 constexpr int kPerXcd = 32;                 // workgroups on one XCD
 constexpr int kRoleWgs = kXcds * kPerXcd;   // 256 workgroups in all
 constexpr int kThreads = 256;               // threads of the four waves of one role
-constexpr int kKRows = kDecodeN / kPerXcd;  // layer-1 K rows per workgroup (128)
+constexpr int kKBlocks = kPerXcd / 2;       // layer-1 K blocks per slice (each in two column halves)
+constexpr int kKRows = kDecodeN / kKBlocks; // layer-1 K rows per workgroup (256)
 constexpr int kPCols = kDecodeP / kPerXcd;  // layer-2 output columns per workgroup (128)
 constexpr int kSpin = 1 << 20;              // polls before a wait gives up (~1 s)
 constexpr int kCpolSc1 = 16;                // buffer cache-policy bits: sc1 (device scope)
-static_assert(kKRows == 4 * 32, "one 32-deep MFMA step per wave of a layer-1 workgroup");
+static_assert(kKRows == 4 * 2 * 32, "two 32-deep MFMA steps per wave of a layer-1 workgroup");
 static_assert(kPCols == 128, "a layer-2 workgroup covers one 128-column load block");
 static_assert(16 * kPCols / 4 == 2 * kThreads, "one float4 of the slice partial per thread");
 
@@ -72,7 +74,7 @@ struct DecodeArgs {
     const uint16_t* W1u;  // gated form: the up matrix Wu
     const uint16_t* b1;
     const uint16_t* W2;
-    float* part1;       // [256][16][ox]: K-block partials of layer 1, by (x, j)
+    float* part1;       // [8][16][16][ox]: K-block partials of layer 1, by (x, K block)
     float* part1u;      // gated form: the same for the up product
     uint16_t* H;        // [16][O]
     float* part2;       // [8][16][P]: slice partials of layer 2
@@ -128,11 +130,12 @@ __device__ __forceinline__ void fail(uint64_t* status, uint64_t epoch) {
 }
 
 // One workgroup per CU, workgroup b on XCD x = b mod 8 with index j = b / 8
-// there.  The layer-1 waves compute layer 1 of K block j over slice x: wave
-// w of a group of four takes K rows [128 j + 32 w, +32); lane (g, c) loads
-// rows +8g .. +8g+7 of the 8 columns 8c .. 8c+7 of each 128-column block of
-// the slice, transposes them in registers into the MFMA's k-contiguous
-// operand and multiplies the matching X fragment.  Plain form: waves 0-3
+// there.  The layer-1 waves compute layer 1 of K block j / 2 over half j mod 2
+// of slice x: wave w of a group of four takes K rows [256 (j / 2) + 64 w,
+// +64) in two 32-row steps; lane (g, c) loads rows +8g .. +8g+7 of each step
+// and the 8 columns 8c .. 8c+7 of the half, transposes them in registers into
+// the MFMA's k-contiguous operand and multiplies the matching X fragment
+// (a 224-column slice: 112-column halves, lanes c = 14, 15 idle).  Plain form: waves 0-3
 // (W1); gated form (SwiGLU, the kernel-fusion post's "Benchmarks" section:
 // H = silu(X Wg) * X Wu, no biases): waves 0-3 the gate product (Wg), waves
 // 4-7 the up product (Wu).  The last four waves hold the workgroup's part of
@@ -163,19 +166,22 @@ __global__ __launch_bounds__((kGated ? 3 : 2) * kThreads) void decode_stream_ker
     if (xcc_id() != x) fail(a.status, a.epoch);    // the exchange would not be coherent
 
     uint4 wr[2][8];
-    uint4 af = zero16();
+    uint4 af[2] = {zero16(), zero16()};
+    const int kb = j >> 1;           // layer 1: K block of kKRows rows ...
+    const int hh = j & 1;            // ... and column half of the slice
+    const int hw = ox / 2;           // columns of a half
     if (l1) {
-        const int64_t k = (int64_t)j * kKRows + 32 * w + 8 * g;
         const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.X, a.M * kDecodeN * 2);
         const __amdgpu_buffer_rsrc_t rw = make_rsrc(up ? a.W1u : a.W1, kDecodeN * O * 2);
-        af = bload16(rx, c < a.M ? (uint32_t)((c * kDecodeN + k) * 2) : kOOB);
+        const int cl = hh * hw + 8 * c;
+        const int64_t col = (int64_t)x * ox + cl;
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
-            const int cl = cb * 128 + 8 * c;   // column inside the slice
-            const int64_t col = (int64_t)x * ox + cl;
+        for (int s = 0; s < 2; ++s) {
+            const int64_t k = (int64_t)kb * kKRows + 64 * w + 32 * s + 8 * g;
+            af[s] = bload16(rx, c < a.M ? (uint32_t)((c * kDecodeN + k) * 2) : kOOB);
 #pragma unroll
             for (int i = 0; i < 8; ++i)
-                wr[cb][i] = bload16(rw, cl < ox ? (uint32_t)(((k + i) * O + col) * 2) : kOOB);
+                wr[s][i] = bload16(rw, 8 * c < hw ? (uint32_t)(((k + i) * O + col) * 2) : kOOB);
         }
     } else {
         const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.W2, O * P * 2);
@@ -192,40 +198,37 @@ __global__ __launch_bounds__((kGated ? 3 : 2) * kThreads) void decode_stream_ker
 
     // ---- layer 1: this K block's share of slice x of X W1 (gated: of X Wg and X Wu)
     if (l1) {
-        floatx4_t acc[2][8];
+        floatx4_t acc[8];
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb) {
+        for (int q = 0; q < 8; ++q) acc[q] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int s = 0; s < 2; ++s) {
             uint4 cv[8];
-            transpose8x8(wr[cb], cv);
+            transpose8x8(wr[s], cv);
 #pragma unroll
-            for (int q = 0; q < 8; ++q)
-                acc[cb][q] = mfma16x16x32(af, cv[q], floatx4_t{0.f, 0.f, 0.f, 0.f});
+            for (int q = 0; q < 8; ++q) acc[q] = mfma16x16x32(af[s], cv[q], acc[q]);
         }
-        // acc[cb][q][r] = wave w's share of [4g + r][cb * 128 + 8c + q]
 #pragma unroll
-        for (int cb = 0; cb < 2; ++cb)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                float* dst = myred + (w * 16 + 4 * g + r) * 256 + cb * 128 + 8 * c;
-                *reinterpret_cast<float4*>(dst) =
-                    make_float4(acc[cb][0][r], acc[cb][1][r], acc[cb][2][r], acc[cb][3][r]);
-                *reinterpret_cast<float4*>(dst + 4) =
-                    make_float4(acc[cb][4][r], acc[cb][5][r], acc[cb][6][r], acc[cb][7][r]);
-            }
+        for (int r = 0; r < 4; ++r) {
+            float* dst = myred + (w * 16 + 4 * g + r) * 256 + 8 * c;
+            *reinterpret_cast<float4*>(dst) = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+            *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4][r], acc[5][r], acc[6][r], acc[7][r]);
+        }
     }
     __syncthreads();
     if (l1) {
-        // the K block's partial: the four waves' 32-row sums added in wave order
-        float* mine = (up ? a.part1u : a.part1) + (int64_t)(x * kPerXcd + j) * 16 * ox;
-        for (int e = 4 * (tid & (kThreads - 1)); e < 16 * ox; e += 4 * kThreads) {
-            const int m = e / ox;
-            const int cl = e - m * ox;
+        // the K block's partial of the half: the four waves' 64-row sums added
+        // in wave order
+        float* mine = (up ? a.part1u : a.part1) + (int64_t)(x * kKBlocks + kb) * 16 * ox + hh * hw;
+        for (int e = 4 * (tid & (kThreads - 1)); e < 16 * hw; e += 4 * kThreads) {
+            const int m = e / hw;
+            const int cl = e - m * hw;
             const float* s = myred + m * 256 + cl;
             const float4 s0 = *reinterpret_cast<const float4*>(s);
             const float4 s1 = *reinterpret_cast<const float4*>(s + 16 * 256);
             const float4 s2 = *reinterpret_cast<const float4*>(s + 2 * 16 * 256);
             const float4 s3 = *reinterpret_cast<const float4*>(s + 3 * 16 * 256);
-            *reinterpret_cast<float4*>(mine + e) =
+            *reinterpret_cast<float4*>(mine + m * ox + cl) =
                 make_float4(((s0.x + s1.x) + s2.x) + s3.x, ((s0.y + s1.y) + s2.y) + s3.y,
                             ((s0.z + s1.z) + s2.z) + s3.z, ((s0.w + s1.w) + s2.w) + s3.w);
         }
@@ -235,13 +238,12 @@ __global__ __launch_bounds__((kGated ? 3 : 2) * kThreads) void decode_stream_ker
     set_flag(a.flags + x * kPerXcd + j, a.epoch ^ a.flag_xor);
 
     // ---- every K block of slice x is in the L2: finish 1/32 of slice x of H
-    // (16 * ox / 32 consecutive elements of the row-major [16][ox] slice, kEl
-    // per thread: each element's 32 K-block partials added in ascending order;
-    // gated: wave 0 sums the gate partials, wave 1 the up partials, two
-    // elements per thread so that 32 loads in flight fit the registers of 12 waves)
+    // (16 * ox / 32 consecutive elements of the row-major [16][ox] slice, four
+    // per thread: each element's 16 K-block partials added in ascending order;
+    // gated: wave 0 sums the gate partials, wave 1 the up partials)
     const bool ok1 = wait_flags(a.flags + x * kPerXcd, a.epoch, a.spin, &ok_lds);
     {
-        constexpr int kEl = kGated ? 2 : 4;
+        constexpr int kEl = 4;
         typedef float vec_t __attribute__((ext_vector_type(kEl)));
         const int rt = tid & 63;         // waves 0-1: no loads of their own outstanding
         const bool rsum = rt < ox / (2 * kEl) && (wave == 0 || (kGated && wave == 1));
@@ -249,20 +251,17 @@ __global__ __launch_bounds__((kGated ? 3 : 2) * kThreads) void decode_stream_ker
         vec_t v = {};
         if (rsum) {
             const float* src = wave == 1 ? a.part1u : a.part1;
-            const __amdgpu_buffer_rsrc_t rp = make_rsrc(src + (int64_t)(x * kPerXcd) * 16 * ox,
-                                                        (int64_t)kPerXcd * 16 * ox * 4);
-            vec_t t[kPerXcd];
+            const __amdgpu_buffer_rsrc_t rp = make_rsrc(src + (int64_t)(x * kKBlocks) * 16 * ox,
+                                                        (int64_t)kKBlocks * 16 * ox * 4);
+            vec_t t[kKBlocks];
 #pragma unroll
-            for (int q = 0; q < kPerXcd; ++q) {   // written by other CUs: device-scope (sc1) loads
+            for (int q = 0; q < kKBlocks; ++q) {   // written by other CUs: device-scope (sc1) loads
                 const uint32_t off = (uint32_t)((q * 16 * ox + e) * 4);
-                if constexpr (kEl == 4)
-                    t[q] = __builtin_bit_cast(vec_t, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kCpolSc1));
-                else
-                    t[q] = __builtin_bit_cast(vec_t, __builtin_amdgcn_raw_buffer_load_b64(rp, off, 0, kCpolSc1));
+                t[q] = __builtin_bit_cast(vec_t, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kCpolSc1));
             }
             v = t[0];
 #pragma unroll
-            for (int q = 1; q < kPerXcd; ++q) v += t[q];
+            for (int q = 1; q < kKBlocks; ++q) v += t[q];
         }
         if constexpr (kGated) {
             // the up sums go to wave 0 through LDS (red is free again: every
@@ -399,7 +398,7 @@ DecodeStreamLayout decode_stream_layout(int64_t O, int64_t P, bool gated) {
         off += (bytes + 255) & ~(size_t)255;
         return at;
     };
-    const size_t part1 = sizeof(float) * kRoleWgs * 16 * (size_t)(O / kXcds);
+    const size_t part1 = sizeof(float) * kXcds * kKBlocks * 16 * (size_t)(O / kXcds);
     L.part1 = take(part1);
     L.part1u = gated ? take(part1) : L.part1;
     L.h = take(sizeof(uint16_t) * 16 * (size_t)O);
