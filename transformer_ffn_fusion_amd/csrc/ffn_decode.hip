@@ -59,7 +59,7 @@ constexpr int kXcds = 8;
 constexpr int kPerXcd = 32;                 // workgroups on one XCD
 constexpr int kRoleWgs = kXcds * kPerXcd;   // 256 workgroups in all
 constexpr int kThreads = 256;               // threads of the four waves of one role
-constexpr int kKBlocks = kPerXcd / 2;       // layer-1 K blocks per slice (each in two column halves)
+constexpr int kKBlocks = kPerXcd / 2;       // layer-1 K blocks per slice (two column halves each)
 constexpr int kKRows = kDecodeN / kKBlocks; // layer-1 K rows per workgroup (256)
 constexpr int kPCols = kDecodeP / kPerXcd;  // layer-2 output columns per workgroup (128)
 constexpr int kSpin = 1 << 20;              // polls before a wait gives up (~1 s)
@@ -134,11 +134,11 @@ __device__ __forceinline__ void fail(uint64_t* status, uint64_t epoch) {
 // of slice x: wave w of a group of four takes K rows [256 (j / 2) + 64 w,
 // +64) in two 32-row steps; lane (g, c) loads rows +8g .. +8g+7 of each step
 // and the 8 columns 8c .. 8c+7 of the half, transposes them in registers into
-// the MFMA's k-contiguous operand and multiplies the matching X fragment
-// (a 224-column slice: 112-column halves, lanes c = 14, 15 idle).  Plain form: waves 0-3
-// (W1); gated form (SwiGLU, the kernel-fusion post's "Benchmarks" section:
-// H = silu(X Wg) * X Wu, no biases): waves 0-3 the gate product (Wg), waves
-// 4-7 the up product (Wu).  The last four waves hold the workgroup's part of
+// the MFMA's k-contiguous operand and multiplies the matching X fragment (a
+// 224-column slice has 112-column halves: lanes c = 14, 15 idle).  Plain
+// form: waves 0-3 (W1); gated form (SwiGLU, the kernel-fusion post's
+// "Benchmarks" section: H = silu(X Wg) * X Wu, no biases): waves 0-3 the gate
+// product (Wg), waves 4-7 the up product (Wu).  The last four waves hold the workgroup's part of
 // W2 (slice x's rows, output columns [128 j, +128)): wave w of them takes the
 // slice's 32-row K steps w and w + 4 (when there is one).  Only layer-1
 // waves store and then wait for their stores (s_waitcnt vmcnt(0)), so those
@@ -211,8 +211,10 @@ __global__ __launch_bounds__((kGated ? 3 : 2) * kThreads) void decode_stream_ker
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
             float* dst = myred + (w * 16 + 4 * g + r) * 256 + 8 * c;
-            *reinterpret_cast<float4*>(dst) = make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
-            *reinterpret_cast<float4*>(dst + 4) = make_float4(acc[4][r], acc[5][r], acc[6][r], acc[7][r]);
+            *reinterpret_cast<float4*>(dst) =
+                make_float4(acc[0][r], acc[1][r], acc[2][r], acc[3][r]);
+            *reinterpret_cast<float4*>(dst + 4) =
+                make_float4(acc[4][r], acc[5][r], acc[6][r], acc[7][r]);
         }
     }
     __syncthreads();
@@ -257,7 +259,8 @@ __global__ __launch_bounds__((kGated ? 3 : 2) * kThreads) void decode_stream_ker
 #pragma unroll
             for (int q = 0; q < kKBlocks; ++q) {   // written by other CUs: device-scope (sc1) loads
                 const uint32_t off = (uint32_t)((q * 16 * ox + e) * 4);
-                t[q] = __builtin_bit_cast(vec_t, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kCpolSc1));
+                t[q] = __builtin_bit_cast(
+                    vec_t, __builtin_amdgcn_raw_buffer_load_b128(rp, off, 0, kCpolSc1));
             }
             v = t[0];
 #pragma unroll
@@ -339,7 +342,8 @@ __global__ __launch_bounds__((kGated ? 3 : 2) * kThreads) void decode_stream_ker
                                ((s0.z + s1.z) + s2.z) + s3.z, ((s0.w + s1.w) + s2.w) + s3.w);
         if (!ok2) y = make_float4(__builtin_nanf(""), __builtin_nanf(""), __builtin_nanf(""),
                                   __builtin_nanf(""));
-        *reinterpret_cast<float4*>(a.part2 + ((int64_t)x * 16 + mm) * P + (int64_t)j * kPCols + cc) = y;
+        float* dst = a.part2 + ((int64_t)x * 16 + mm) * P + (int64_t)j * kPCols + cc;
+        *reinterpret_cast<float4*>(dst) = y;
     }
     if (!ok2) fail(a.status, a.epoch);
 }
