@@ -66,9 +66,14 @@ typedef enum { FFN_ACT_NONE = 0, FFN_ACT_RELU = 1, FFN_ACT_GELU_TANH = 2 } ffn_a
  * "Megatron-LM tensor parallelism", at decode batch sizes): one kernel
  * streams W1 and W2 together, cuts the hidden dimension into one slice per
  * XCD and passes each slice of H between the workgroups of that XCD through
- * its L2; a second kernel sums the 8 slice partials of Y.  Its waits are
- * bounded: if one expires, or the hardware deals workgroups to XCDs
- * otherwise than round-robin, every element of Y is NaN. */
+ * its L2; a second kernel sums the 8 slice partials of Y.  Its 256
+ * workgroups (one per CU) wait on each other, so the first kernel needs the
+ * whole device at once: other kernels that hold CUs meanwhile (another
+ * stream, another process) delay it, and two such calls that run at the
+ * same time can hold each other's CUs.  Every wait is bounded (about a
+ * second): if one expires, or the hardware deals workgroups to XCDs
+ * otherwise than round-robin, every element of Y is NaN rather than wrong.
+ * Order concurrent decode calls on one stream, or force FFN_VARIANT_SKINNY. */
 typedef enum {
     FFN_VARIANT_AUTO = 0,
     FFN_VARIANT_FUSED = 1,   /* bf16, H in LDS, split-O partials + ordered reduce */
