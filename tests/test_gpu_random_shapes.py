@@ -74,6 +74,34 @@ def test_random_dense(M, N, O, P, act1, bias, seed, variant):
     _check(host_f64(Y), ref, f"random dense {(M, N, O, P)}")
 
 
+def _decode_stream_cases(n=8):
+    # the decode stream's shape family: M 1..16, N = P = 4096, O a multiple of 256 up to 2048
+    rng = np.random.default_rng(4096)
+    return [(int(rng.integers(1, 17)), 4096, 256 * int(rng.integers(1, 9)), 4096,
+             ACTS[int(rng.integers(0, 3))], ACTS[int(rng.integers(0, 3))], bool(rng.integers(0, 2)),
+             bool(rng.integers(0, 2)), 500 + i) for i in range(n)]
+
+
+@pytest.mark.parametrize("M,N,O,P,act1,act2,bias,gated,seed", _decode_stream_cases())
+def test_random_decode_stream(M, N, O, P, act1, act2, bias, gated, seed):
+    import torch
+    log(f"case random decode stream {(M, N, O, P)} act1={act1} act2={act2} bias={bias} "
+        f"gated={gated}")
+    Y = torch.empty((M, P), dtype=torch.bfloat16, device="cuda")
+    if gated:
+        X, Wg, Wu, Wd = synth.swiglu_inputs(M, N, O, P, seed=seed)
+        ffn.ffn_swiglu_forward(*(dev_bf16(a) for a in (X, Wg, Wu, Wd)), Y, ffn.VARIANT_DECODE)
+        torch.cuda.synchronize()
+        ref = oracle.swiglu(X, Wg, Wu, Wd)
+    else:
+        X, W1, b1, W2, b2 = synth.dense_inputs(M, N, O, P, seed=seed, with_bias=bias)
+        d = [None if a is None else dev_bf16(a) for a in (X, W1, b1, W2, b2)]
+        ffn.ffn_forward_ex(*d, Y, act1, act2, ffn.VARIANT_DECODE)
+        torch.cuda.synchronize()
+        ref = oracle.ffn(X, W1, b1, W2, b2, act1=ACT_CODE[act1], act2=ACT_CODE[act2])
+    _check(host_f64(Y), ref, f"random decode stream {(M, N, O, P)}")
+
+
 def _swiglu_cases(n=8):
     rng = np.random.default_rng(77)
     return [(int(rng.integers(1, 200)), *(8 * int(rng.integers(1, 160)) for _ in range(3)), 300 + i)
