@@ -165,6 +165,22 @@ __global__ __launch_bounds__((kGated ? 3 : 2) * kThreads) void decode_stream_ker
     float* myred = red + (up ? 4 * 16 * 256 : 0);   // this wave's product's LDS sums
     if (xcc_id() != x) fail(a.status, a.epoch);    // the exchange would not be coherent
 
+    // the elements of H this workgroup finishes after barrier 1: 1/32 of the
+    // row-major [16][ox] slice, four consecutive elements per thread of wave 0
+    // (gated form: wave 1 sums the up partials of the same elements); their b1
+    // values are loaded now, off the chain of dependent steps
+    constexpr int kEl = 4;
+    const int rt = tid & 63;
+    const bool rsum = rt < ox / (2 * kEl) && (wave == 0 || (kGated && wave == 1));
+    const int e = j * (ox / 2) + kEl * rt;
+    const int hm = e / ox;                                  // row of H
+    const int64_t hcol = (int64_t)x * ox + (e - hm * ox);   // first column of H
+    float bias[kEl] = {0.f, 0.f, 0.f, 0.f};
+    if (!kGated && rsum && wave == 0 && a.b1) {
+#pragma unroll
+        for (int i = 0; i < kEl; ++i) bias[i] = bf16_to_f32(a.b1[hcol + i]);
+    }
+
     uint4 wr[2][8];
     uint4 af[2] = {zero16(), zero16()};
     const int kb = j >> 1;           // layer 1: K block of kKRows rows ...
@@ -239,17 +255,12 @@ __global__ __launch_bounds__((kGated ? 3 : 2) * kThreads) void decode_stream_ker
     __syncthreads();
     set_flag(a.flags + x * kPerXcd + j, a.epoch ^ a.flag_xor);
 
-    // ---- every K block of slice x is in the L2: finish 1/32 of slice x of H
-    // (16 * ox / 32 consecutive elements of the row-major [16][ox] slice, four
-    // per thread: each element's 16 K-block partials added in ascending order;
-    // gated: wave 0 sums the gate partials, wave 1 the up partials)
+    // ---- every K block of slice x is in the L2: finish this workgroup's
+    // elements of H (each element's 16 K-block partials added in ascending
+    // order; gated: wave 0 sums the gate partials, wave 1 the up partials)
     const bool ok1 = wait_flags(a.flags + x * kPerXcd, a.epoch, a.spin, &ok_lds);
     {
-        constexpr int kEl = 4;
         typedef float vec_t __attribute__((ext_vector_type(kEl)));
-        const int rt = tid & 63;         // waves 0-1: no loads of their own outstanding
-        const bool rsum = rt < ox / (2 * kEl) && (wave == 0 || (kGated && wave == 1));
-        const int e = j * (ox / 2) + kEl * rt;
         vec_t v = {};
         if (rsum) {
             const float* src = wave == 1 ? a.part1u : a.part1;
@@ -273,8 +284,6 @@ __global__ __launch_bounds__((kGated ? 3 : 2) * kThreads) void decode_stream_ker
             __syncthreads();
         }
         if (rsum && wave == 0) {
-            const int m = e / ox;
-            const int64_t col = (int64_t)x * ox + (e - m * ox);
             float h[kEl];
             if constexpr (kGated) {
                 const vec_t u = *reinterpret_cast<const vec_t*>(red + kEl * rt);
@@ -282,13 +291,10 @@ __global__ __launch_bounds__((kGated ? 3 : 2) * kThreads) void decode_stream_ker
                 for (int i = 0; i < kEl; ++i) h[i] = ok1 ? silu(v[i]) * u[i] : __builtin_nanf("");
             } else {
 #pragma unroll
-                for (int i = 0; i < kEl; ++i) {
-                    float z = v[i];
-                    if (a.b1) z += bf16_to_f32(a.b1[col + i]);
-                    h[i] = ok1 ? apply_act(a.act1, z) : __builtin_nanf("");
-                }
+                for (int i = 0; i < kEl; ++i)
+                    h[i] = ok1 ? apply_act(a.act1, v[i] + bias[i]) : __builtin_nanf("");
             }
-            uint32_t* dst = reinterpret_cast<uint32_t*>(a.H + m * O + col);
+            uint32_t* dst = reinterpret_cast<uint32_t*>(a.H + hm * O + hcol);
 #pragma unroll
             for (int i = 0; i < kEl / 2; ++i) dst[i] = pack_bf16x2(h[2 * i], h[2 * i + 1]);
             wait_vmcnt<0>();
