@@ -1,8 +1,8 @@
 // Exercises the host side of the C ABI (include/ffn.h) without a GPU, for the
 // AddressSanitizer / UndefinedBehaviorSanitizer build run by
 // tests/test_sanitizers.py: the size queries over many shapes, the layout
-// self-check, and every entry point with arguments that the host checks
-// reject before any HIP call.  Exits non-zero on an unexpected return code.
+// self-check, the kernel-family query, and every entry point with arguments
+// that the host checks reject before any HIP call.  Exits non-zero on an unexpected return code.
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -78,6 +78,17 @@ int main() {
     expect(moe_router(X, nullptr, nullptr, 64, 64, 8, 2, nullptr, ids, nullptr, nullptr, nullptr, ws, 1 << 20, nullptr), FFN_EINVAL, "router Wr");
     expect(moe_router(X, W, nullptr, 64, 64, 12, 2, nullptr, ids, nullptr, nullptr, nullptr, ws, 1 << 20, nullptr), FFN_EUNSUPPORTED, "router E % 8");
     expect(moe_ffn_forward_router(X, W, nullptr, 64, 8, 2, W, nullptr, W, nullptr, Y, 64, 448, 64, FFN_BF16, 2, 0, nullptr, nullptr, nullptr, nullptr, nullptr, ws, 16, nullptr), FFN_EWORKSPACE, "moe router workspace");
+    // the decode stream variant: shape and workspace checks, family queries
+    expect(ffn_forward_ex(X, W, nullptr, W, nullptr, Y, 16, 4096, 1920, 4096, FFN_BF16, 2, 0, FFN_VARIANT_DECODE, ws, 1 << 30, nullptr), FFN_EUNSUPPORTED, "decode O");
+    expect(ffn_forward_ex(X, W, nullptr, W, nullptr, Y, 16, 4096, 1792, 4096, FFN_BF16, 2, 0, FFN_VARIANT_DECODE, ws, 16, nullptr), FFN_EWORKSPACE, "decode workspace");
+    expect(ffn_swiglu_forward(X, W, W, W, Y, 16, 4096, 1792, 8192, FFN_BF16, FFN_VARIANT_DECODE, ws, 1 << 30, nullptr), FFN_EUNSUPPORTED, "swiglu decode P");
+    expect(ffn_selftest_decode_expiry(X, W, nullptr, W, nullptr, Y, 16, 1024, 896, 1024, 2, 0, ws, 1 << 30, nullptr), FFN_EUNSUPPORTED, "expiry shape");
+    for (int v = 0; v < 5; ++v) {
+        if (ffn_forward_family(16, 4096, 1792, 4096, FFN_BF16, v) < 0) return 1;
+        if (ffn_forward_family(4096, 4096, 1792, 4096, FFN_BF16, v) < 0) return 1;
+    }
+    expect(ffn_forward_family(16, 4096, 1792, 4096, FFN_BF16, 7), FFN_EINVAL, "family variant");
+    expect(ffn_forward_family(16, 4096, 12, 4096, FFN_BF16, 0), FFN_EUNSUPPORTED, "family shape");
     double flops = 0.0;
     expect(ffn_ceiling_mfma(ws, 0, 1, &flops, nullptr), FFN_EWORKSPACE, "ceiling sink");
     expect(ffn_ceiling_read(X, 24, ws, 1 << 20, nullptr), FFN_EINVAL, "ceiling bytes");
