@@ -34,8 +34,9 @@
  *    returned by ffn_last_error() (per host thread) and leaves every output
  *    untouched.  A failed launch returns FFN_ELAUNCH.
  *  - Shapes.  M >= 1 (M == 0 is a no-op); N, O, P >= 8 and multiples of 8;
- *    N and O below 2^24 and each weight matrix below 2^30 elements (the
- *    kernels use 32-bit byte offsets), else FFN_EUNSUPPORTED.  Any M works
+ *    N and O below 2^24, P below 2^23 and each weight matrix below 2^30
+ *    elements (the kernels use 32-bit byte offsets), else FFN_EUNSUPPORTED.
+ *    Any M works
  *    (partial row tiles are handled).
  *  - Numerics.  bf16 storage, fp32 accumulation; H is rounded to bf16 once,
  *    Y once (round to nearest even).  No floating-point atomics: repeated

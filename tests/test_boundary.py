@@ -53,6 +53,7 @@ def _fwd(X=FAKE, W1=FAKE, b1=None, W2=FAKE, b2=None, Y=FAKE2, M=64, N=64, O=448,
     (dict(M=1 << 20, N=1 << 15, O=1 << 15, P=64), E_UNSUP),
     (dict(N=1 << 24, O=8, P=8), E_UNSUP),    # a 64-row X tile past 32-bit offsets
     (dict(M=16, N=8, O=1 << 24, P=8), E_UNSUP),   # 16 rows of H past 32-bit offsets
+    (dict(M=64, N=8, O=8, P=1 << 23), E_UNSUP),   # a 64-row tile of partials past 32-bit offsets
     (dict(W1=None), E_INVAL),
     (dict(Y=None), E_INVAL),
     (dict(ws=None), E_INVAL),

@@ -62,6 +62,9 @@ int check_dims(int64_t M, int64_t N, int64_t O, int64_t P) {
     if (N >= ((int64_t)1 << 24) || O >= ((int64_t)1 << 24))
         return fail(FFN_EUNSUPPORTED, "N and O must be below 2^24 (got %lld, %lld)", (long long)N,
                     (long long)O);
+    // ... and a 64-row tile of the packed split partials (64 * P * 3 bytes)
+    if (P >= ((int64_t)1 << 23))
+        return fail(FFN_EUNSUPPORTED, "P must be below 2^23 (got %lld)", (long long)P);
     return FFN_OK;
 }
 

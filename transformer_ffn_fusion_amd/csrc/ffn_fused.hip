@@ -118,7 +118,6 @@ struct FusedArgs {
     int act1;
     int cus;              // compute units of the device (grouped form: tail splitting)
     bool part_wt;         // partials written through to the memory-side cache (sc1)
-    bool part_rsrc;       // a split's plane is below 2^31 bytes (32-bit buffer offsets)
     GroupedRows g;
 };
 
@@ -594,9 +593,14 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
         }
     };
 
-    char* const part_plane = a.part + (int64_t)s * a.rows_out * P * kPartBytes;
-    const int64_t part_lane = ((row0 + 4 * lg) * P + 64 * wc + 4 * li) * kPartBytes;
-    const __amdgpu_buffer_rsrc_t rpart = make_rsrc(part_plane, a.rows_out * P * kPartBytes);
+    // Partial stores.  The resource spans this tile's valid rows of the
+    // split's plane, so the stores of rows past them fall outside it and are
+    // dropped by the range check, and lanes whose columns lie past P store at
+    // kOOB; the offsets are relative to the tile, so they stay below 2^31
+    // whatever the plane's size.
+    char* const part_tile = a.part + ((int64_t)s * a.rows_out + row0) * P * kPartBytes;
+    const __amdgpu_buffer_rsrc_t rpart = make_rsrc(part_tile, (int64_t)valid * P * kPartBytes);
+    const uint32_t part_lane = (uint32_t)(((4 * lg) * P + 64 * wc + 4 * li) * kPartBytes);
     uint2 RA[8], RB[8];
     load2(0, RA);
     load2(1, RB);   // the stage count is even
@@ -607,28 +611,34 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
         // pass complete: lane holds rows 16 fm + 4 lg + r, columns 4 li .. 4 li + 3
         const int64_t pd = st / Cfg::kKS;
         const int64_t pt = pass0 + (pd + rotp < npl ? pd + rotp : pd + rotp - npl);
-        if (pt * kBN2 + 64 * wc + 4 * li < P) {
+        // the row stride passes through an empty asm statement so that the
+        // sixteen row offsets are formed here, not held across the loop
+        uint32_t rowb = (uint32_t)(P * kPartBytes);
+        asm volatile("" : "+s"(rowb));
+        const uint32_t vo = pt * kBN2 + 64 * wc + 4 * li < P
+                                ? part_lane + (uint32_t)(pt * kBN2 * kPartBytes) : kOOB;
+        uint32_t w[4][4][3];
+#pragma unroll
+        for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                pack_f24x4(acc2[0][fm][r], acc2[1][fm][r], acc2[2][fm][r], acc2[3][fm][r], w[fm][r]);
+        if (a.part_wt) {   // written through to the MALL
 #pragma unroll
             for (int fm = 0; fm < 4; ++fm)
 #pragma unroll
-                for (int r = 0; r < 4; ++r) {
-                    if (16 * fm + 4 * lg + r >= valid) continue;
-                    uint32_t w[3];
-                    pack_f24x4(acc2[0][fm][r], acc2[1][fm][r], acc2[2][fm][r], acc2[3][fm][r], w);
-                    const int64_t o = part_lane + ((int64_t)(16 * fm + r) * P + pt * kBN2) * kPartBytes;
-                    if (a.part_wt)   // written through to the MALL
-                        __builtin_amdgcn_raw_buffer_store_b96(uint32x3_t{w[0], w[1], w[2]}, rpart,
-                                                              (uint32_t)o, 0, kCpolSc1);
-                    else if (a.part_rsrc)   // streamed: read once, by the reduction
-                        __builtin_amdgcn_raw_buffer_store_b96(uint32x3_t{w[0], w[1], w[2]}, rpart,
-                                                              (uint32_t)o, 0, kCpolNt);
-                    else {   // a plane past 2^31 bytes: 64-bit addresses, streamed
-                        uint32_t* d = reinterpret_cast<uint32_t*>(part_plane + o);
-                        __builtin_nontemporal_store(w[0], d);
-                        __builtin_nontemporal_store(w[1], d + 1);
-                        __builtin_nontemporal_store(w[2], d + 2);
-                    }
-                }
+                for (int r = 0; r < 4; ++r)
+                    __builtin_amdgcn_raw_buffer_store_b96(
+                        uint32x3_t{w[fm][r][0], w[fm][r][1], w[fm][r][2]}, rpart,
+                        vo + (uint32_t)(16 * fm + r) * rowb, 0, kCpolSc1);
+        } else {           // streamed: read once, by the reduction
+#pragma unroll
+            for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    __builtin_amdgcn_raw_buffer_store_b96(
+                        uint32x3_t{w[fm][r][0], w[fm][r][1], w[fm][r][2]}, rpart,
+                        vo + (uint32_t)(16 * fm + r) * rowb, 0, kCpolNt);
         }
 #pragma unroll
         for (int j = 0; j < 4; ++j)
@@ -717,8 +727,7 @@ hipError_t launch_fused_impl(const FusedArgs& a, int64_t units, hipStream_t stre
     const int64_t grid = units + (G ? a.cus + 64 : 0);
     const int64_t plane_bytes = a.rows_out * a.P * kPartBytes;
     FusedArgs b = a;
-    b.part_rsrc = plane_bytes < (1ll << 31);
-    b.part_wt = b.part_rsrc && (int64_t)a.splits * plane_bytes <= kMallBytes;
+    b.part_wt = (int64_t)a.splits * plane_bytes <= kMallBytes;
     hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), Cfg::kLds, stream, b);
     return hipGetLastError();
 }
