@@ -265,6 +265,19 @@ def test_fused_two_pass_chunk_sampled_rows():
     assert torch.equal(outs[0], outs[1]), "two calls differ"
 
 
+def test_fused_partial_plane_past_2GiB():
+    """A split's plane of packed partials larger than 2^31 bytes (65536 rows x
+    16384 columns x 3 bytes = 3 GiB): the kernel addresses each tile's rows
+    through a buffer resource based at the tile, so no offset passes 2^31;
+    sampled rows, the last row tile's among them, against the oracle."""
+    M, N, O, P = 65536, 64, 448, 16384
+    assert M * P * 3 > (1 << 31)
+    log(f"case fused, 3 GiB partial plane {(M, N, O, P)}")
+    rows = sorted(set(range(0, M, 4099)) | {M - 64, M - 1})
+    got, ref, _ = _run_dense(M, N, O, P, variant=ffn.VARIANT_FUSED, seed=77, rows=rows)
+    compare(got, ref, BF16_TOL, "3 GiB partial plane")
+
+
 @pytest.mark.parametrize("shape", [(100, 256, 256, 520), (70, 64, 136, 64)])
 def test_fused_narrow_hidden(shape):
     """Hidden widths of at most 256 run the 256-wide chunk."""
