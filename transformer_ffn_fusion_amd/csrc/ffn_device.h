@@ -189,6 +189,21 @@ __device__ __forceinline__ void transpose8x8(const uint4 (&rows)[8], uint4 (&col
     for (int j = 0; j < 8; ++j) cols[j] = make_uint4(c[j][0], c[j][1], c[j][2], c[j][3]);
 }
 
+// Column j of transpose8x8 alone (four v_perm_b32).
+__device__ __forceinline__ uint4 transpose8x8_col(const uint4 (&rows)[8], int j) {
+    const uint32_t sel = (j & 1) ? 0x07060302u : 0x05040100u;
+    uint32_t c[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+        const uint4 a = rows[2 * q];
+        const uint4 b = rows[2 * q + 1];
+        const uint32_t av = (j >> 1) == 0 ? a.x : (j >> 1) == 1 ? a.y : (j >> 1) == 2 ? a.z : a.w;
+        const uint32_t bv = (j >> 1) == 0 ? b.x : (j >> 1) == 1 ? b.y : (j >> 1) == 2 ? b.z : b.w;
+        c[q] = __builtin_amdgcn_perm(bv, av, sel);
+    }
+    return make_uint4(c[0], c[1], c[2], c[3]);
+}
+
 // rows[e] holds 4 bf16 (columns 0..3) of row e.  On return cols[j] holds the
 // 8 bf16 of column j, rows 0..7 in order.
 __device__ __forceinline__ void transpose8x4(const uint2 (&rows)[8], uint4 (&cols)[4]) {

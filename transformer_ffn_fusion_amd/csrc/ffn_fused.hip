@@ -96,6 +96,11 @@ struct FusedCfg {
     static constexpr int kLoOff = kKS * kSub;
     static constexpr int kHEnd = kHOff + (kHLo ? 2 : 1) * kKS * kSub;
     static constexpr int kLds = PA::kLds1 > kHEnd ? PA::kLds1 : kHEnd;
+    // dense second product: per-wave staging of packed partials (8 rows x
+    // 384 bytes per wave), below H when H leaves room there, else above it
+    static constexpr int kStgBytes = 8 * 8 * 384;
+    static constexpr int kStgOff = kHOff >= kStgBytes ? 0 : kHEnd;
+    static_assert(kStgOff + kStgBytes <= kLds || kGated || kHLo, "staging fits the LDS");
     static_assert(kHidA % kBK == 0 && kHidB % kBK == 0, "passes cover whole H slabs");
     static_assert(!kGated || (PA::kNB1 % 2 == 0 && (!kTwoPass || PB::kNB1 % 2 == 0)),
                   "gate and up halves are whole 64-column blocks");
@@ -137,6 +142,7 @@ constexpr int64_t kRoundUnits = 256;      // workgroups in one round on MI355X (
 constexpr int kCpolSc1 = 16;   // buffer cache-policy bits: sc1 (device scope)
 constexpr int kCpolNt = 2;     // ... nt (streaming)
 typedef unsigned uint32x3_t __attribute__((ext_vector_type(3)));
+typedef unsigned uint32x4_t __attribute__((ext_vector_type(4)));
 
 // Unit -> (row tile, hidden chunk).  Workgroups are dispatched round-robin
 // over the 8 XCDs (unit u runs on XCD u % 8), and each XCD has its own L2.
@@ -526,8 +532,153 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     }
     __syncthreads();   // H is complete
 
+    auto hrow = [](int ks) {
+        if constexpr (Cfg::kSlabsB == 0) return kBK * ks;
+        else return ks < Cfg::kSlabsB ? Cfg::kHidA + kBK * ks : kBK * (ks - Cfg::kSlabsB);
+    };
+    // Partial stores.  The resource spans this tile's valid rows of the
+    // split's plane, so the stores of rows past them fall outside it and are
+    // dropped by the range check, and lanes whose columns lie past P store at
+    // kOOB; the offsets are relative to the tile, so they stay below 2^31
+    // whatever the plane's size.
+    char* const part_tile = a.part + ((int64_t)s * a.rows_out + row0) * P * kPartBytes;
+    const __amdgpu_buffer_rsrc_t rpart = make_rsrc(part_tile, (int64_t)valid * P * kPartBytes);
+
+    if constexpr (!kGrouped && !kGated) if (P % 128 == 0) {
+        // ================ GEMM2, dense form: Y_part = H W2_chunk ================
+        // All eight waves, for output widths that are a multiple of 128.
+        // Wave m owns columns 128m .. 128m+127 of every 1024-column pass and
+        // streams its W2 columns straight into registers with 16-byte loads:
+        // lane (i, g) loads, for each k-row 8g + e of a stage, the eight
+        // columns 8i .. 8i+7 (the 16 lanes of a k-group read 256 contiguous
+        // bytes of a row).  Column q of that 8 x 8 block, transposed out of the
+        // registers (four v_perm) just before its MFMAs, is a k-contiguous
+        // operand whose index i stands for column 8i + q.  H is the first MFMA
+        // operand, so lane (i, g) ends up with rows 16 fm + 4g + r and, over q,
+        // the eight consecutive columns 8i .. 8i+7 (24 bytes of packed
+        // partials per row), which reach the partial plane through the wave's
+        // LDS staging area in whole 16-byte pieces.  16-byte loads carry twice
+        // the bytes of 8-byte ones per address-unit instruction: the W2
+        // stream alone takes 33 against 52 us per call at the prefill shard,
+        // and this form of the second product ~50 against ~68 us
+        // (per-workgroup timestamps).  Two stages are in flight while one is
+        // multiplied.
+        constexpr int64_t kPW = 1024;   // output columns per pass: eight waves of 128
+        const int64_t npw = (P + kPW - 1) / kPW;
+        const int64_t nsw = npw * Cfg::kKS;
+        // the pass rotation as for the 512-column passes below: every pass
+        // while the chunk's W2 block fits the L2, else a window of 2048 columns
+        const int64_t rspan = (int64_t)Cfg::kHid * P * 2 <= kL2Bytes
+                                  ? npw : (npw < kPassWindow / 2 ? npw : kPassWindow / 2);
+        const int64_t rotw = jx % rspan;
+        const int wm = wave;
+        const __amdgpu_buffer_rsrc_t rw2 = make_rsrc(W2 + o0 * P, oc * P * 2);
+        const uint32_t w2l =
+            (uint32_t)(8 * lg) * (uint32_t)(P * 2) + (uint32_t)(128 * wm + 8 * li) * 2u;
+        auto load16 = [&](int64_t step, uint4 (&R)[8]) {
+            const int64_t pr = step / Cfg::kKS;
+            const int kr = (int)(step - pr * Cfg::kKS);
+            const int64_t pt = pr + rotw < npw ? pr + rotw : pr + rotw - npw;
+            const int ks = kr + rotk < Cfg::kKS ? kr + rotk : kr + rotk - Cfg::kKS;
+            const uint32_t base = step < nsw
+                ? (uint32_t)(((int64_t)hrow(ks) * P + pt * kPW) * 2) + w2l : kOOB;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) R[e] = bload16(rw2, base + (uint32_t)(e * P * 2));
+        };
+        floatx4_t acc[8][4];   // [operand q][row fragment fm]
+#pragma unroll
+        for (int q = 0; q < 8; ++q)
+#pragma unroll
+            for (int fm = 0; fm < 4; ++fm) acc[q][fm] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        // one stage: each operand column is transposed out of R just before its
+        // MFMAs (four v_perm), so only one operand is live besides R; R is
+        // refilled with stage st + 2 once the stage's MFMAs are issued
+        auto mma = [&](int64_t st, uint4 (&R)[8]) {
+            const int64_t pr = st / Cfg::kKS;
+            const int kr = (int)(st - pr * Cfg::kKS);
+            const int ks = kr + rotk < Cfg::kKS ? kr + rotk : kr + rotk - Cfg::kKS;
+            const char* hs = hreg + ks * kSub;
+            uint4 bh[4];
+#pragma unroll
+            for (int fm = 0; fm < 4; ++fm) bh[fm] = ld16(hs + frag_off(16 * fm + li, lg));
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const uint4 wq = transpose8x8_col(R, q);
+#pragma unroll
+                for (int fm = 0; fm < 4; ++fm) acc[q][fm] = mfma16x16x32(bh[fm], wq, acc[q][fm]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            load16(st + 2, R);
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        uint4 RA[8], RB[8];
+        // all of RA's loads before RB's, as in every later iteration: the
+        // compiler's waits at the loop head take the strictest of the paths
+        // into it, so a prologue with the two sets interleaved would make
+        // every iteration wait for both
+        load16(0, RA);
+        __builtin_amdgcn_sched_barrier(0);
+        load16(1, RB);   // the stage count is even
+        __builtin_amdgcn_sched_barrier(0);
+        for (int64_t st = 0; st < nsw; st += 2) {
+            mma(st, RA);
+            mma(st + 1, RB);
+            if ((st + 2) % Cfg::kKS != 0) continue;
+            const int64_t pr = st / Cfg::kKS;
+            // pass pr complete: lane (i, g) holds rows 16 fm + 4 g + r, columns
+            // c0w + 8 i + q of the wave's segment.  Its 24 bytes of packed
+            // partials per row go through the wave's LDS staging area (8 rows at
+            // a time), which is read back in 16-byte pieces that follow the rows
+            // of the partial plane, so every store writes whole, adjacent pieces.
+            const int64_t pt = pr + rotw < npw ? pr + rotw : pr + rotw - npw;
+            const int64_t c0w = pt * kPW + 128 * wm;   // P % 128 == 0: all 128 in or all out
+            // the row stride passes through an empty asm statement so that the
+            // row offsets are formed here, not held across the loop
+            uint32_t rowb = (uint32_t)(P * kPartBytes);
+            asm volatile("" : "+s"(rowb));
+            const uint32_t vo = c0w < P ? (uint32_t)(c0w * kPartBytes) : kOOB;
+            char* const stg = smem + Cfg::kStgOff + wm * 3072;
+#pragma unroll
+            for (int fm = 0; fm < 4; ++fm)
+#pragma unroll
+                for (int t = 0; t < 2; ++t) {
+#pragma unroll
+                    for (int rr = 0; rr < 2; ++rr) {
+                        const int r = 2 * t + rr;
+                        uint32_t w0[3], w1[3];
+                        pack_f24x4(acc[0][fm][r], acc[1][fm][r], acc[2][fm][r], acc[3][fm][r], w0);
+                        pack_f24x4(acc[4][fm][r], acc[5][fm][r], acc[6][fm][r], acc[7][fm][r], w1);
+                        char* dst = stg + (2 * lg + rr) * 384 + 24 * li;
+                        *reinterpret_cast<uint2*>(dst) = make_uint2(w0[0], w0[1]);
+                        *reinterpret_cast<uint2*>(dst + 8) = make_uint2(w0[2], w1[0]);
+                        *reinterpret_cast<uint2*>(dst + 16) = make_uint2(w1[1], w1[2]);
+                    }
+#pragma unroll
+                    for (int k = 0; k < 3; ++k) {
+                        const int cidx = lane + 64 * k;   // 16-byte piece 0..191 of the 8 rows
+                        const int ri = cidx / 24, pos = cidx - 24 * (cidx / 24);
+                        const uint4 v = *reinterpret_cast<const uint4*>(stg + ri * 384 + pos * 16);
+                        const int row = 16 * fm + 4 * (ri >> 1) + 2 * t + (ri & 1);
+                        const uint32_t o = vo + (uint32_t)row * rowb + (uint32_t)(pos * 16);
+                        if (a.part_wt)   // written through to the MALL
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                __builtin_bit_cast(uint32x4_t, v), rpart, o, 0, kCpolSc1);
+                        else             // streamed: read once, by the reduction
+                            __builtin_amdgcn_raw_buffer_store_b128(
+                                __builtin_bit_cast(uint32x4_t, v), rpart, o, 0, kCpolNt);
+                    }
+                }
+#pragma unroll
+            for (int q = 0; q < 8; ++q)
+#pragma unroll
+                for (int fm = 0; fm < 4; ++fm) acc[q][fm] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+        }
+        return;
+    }
+
     // ======================= GEMM2: Y_part = H W2_chunk =====================
-    // All eight waves.  Wave w owns columns 64w .. 64w+63 of every 512-column
+    // (Grouped and gated forms, and output widths that are not a multiple of
+    // 128.)  All eight waves.  Wave w owns columns 64w .. 64w+63 of every 512-column
     // pass and streams its own W2 columns straight into registers -- no LDS
     // staging and no barriers.  Lane (i, g) loads, for each k-row 8g..8g+7 of
     // a stage, the four columns 4i..4i+3 (8 bytes: the 16 lanes of a k-group
@@ -540,10 +691,6 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     const int wc = wave;
     const __amdgpu_buffer_rsrc_t rw2 = make_rsrc(W2 + o0 * P, oc * P * 2);
     const uint32_t w2_lane = (uint32_t)(8 * lg) * (uint32_t)(P * 2) + (uint32_t)(64 * wc + 4 * li) * 2u;
-    auto hrow = [](int ks) {
-        if constexpr (Cfg::kSlabsB == 0) return kBK * ks;
-        else return ks < Cfg::kSlabsB ? Cfg::kHidA + kBK * ks : kBK * (ks - Cfg::kSlabsB);
-    };
     // loads of stage `step` into R; a step past the end reads zeros (out of
     // range), so that every stage refills its registers unconditionally
     auto load2 = [&](int64_t step, uint2 (&R)[8]) {
@@ -593,13 +740,6 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
         }
     };
 
-    // Partial stores.  The resource spans this tile's valid rows of the
-    // split's plane, so the stores of rows past them fall outside it and are
-    // dropped by the range check, and lanes whose columns lie past P store at
-    // kOOB; the offsets are relative to the tile, so they stay below 2^31
-    // whatever the plane's size.
-    char* const part_tile = a.part + ((int64_t)s * a.rows_out + row0) * P * kPartBytes;
-    const __amdgpu_buffer_rsrc_t rpart = make_rsrc(part_tile, (int64_t)valid * P * kPartBytes);
     const uint32_t part_lane = (uint32_t)(((4 * lg) * P + 64 * wc + 4 * li) * kPartBytes);
     uint2 RA[8], RB[8];
     load2(0, RA);
