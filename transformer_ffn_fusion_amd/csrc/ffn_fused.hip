@@ -96,11 +96,13 @@ struct FusedCfg {
     static constexpr int kLoOff = kKS * kSub;
     static constexpr int kHEnd = kHOff + (kHLo ? 2 : 1) * kKS * kSub;
     static constexpr int kLds = PA::kLds1 > kHEnd ? PA::kLds1 : kHEnd;
-    // dense second product: per-wave staging of packed partials (8 rows x
-    // 384 bytes per wave), below H when H leaves room there, else above it
+    // second product (dense and gated forms): per-wave staging of packed
+    // partials (8 rows x 384 bytes per wave), below H when H leaves room
+    // there, else above it
     static constexpr int kStgBytes = 8 * 8 * 384;
     static constexpr int kStgOff = kHOff >= kStgBytes ? 0 : kHEnd;
-    static_assert(kStgOff + kStgBytes <= kLds || kGated || kHLo, "staging fits the LDS");
+    static_assert(kHLo || (kStgOff == 0 ? kStgBytes <= kHOff : kStgOff + kStgBytes <= kLds),
+                  "the staging area fits the LDS beside H");
     static_assert(kHidA % kBK == 0 && kHidB % kBK == 0, "passes cover whole H slabs");
     static_assert(!kGated || (PA::kNB1 % 2 == 0 && (!kTwoPass || PB::kNB1 % 2 == 0)),
                   "gate and up halves are whole 64-column blocks");
@@ -544,8 +546,8 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     char* const part_tile = a.part + ((int64_t)s * a.rows_out + row0) * P * kPartBytes;
     const __amdgpu_buffer_rsrc_t rpart = make_rsrc(part_tile, (int64_t)valid * P * kPartBytes);
 
-    if constexpr (!kGrouped && !kGated) if (P % 128 == 0) {
-        // ================ GEMM2, dense form: Y_part = H W2_chunk ================
+    if constexpr (!kGrouped) if (P % 128 == 0) {
+        // ============ GEMM2, dense and gated forms: Y_part = H W2_chunk ============
         // All eight waves, for output widths that are a multiple of 128.
         // Wave m owns columns 128m .. 128m+127 of every 1024-column pass and
         // streams its W2 columns straight into registers with 16-byte loads:
@@ -677,8 +679,8 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     }
 
     // ======================= GEMM2: Y_part = H W2_chunk =====================
-    // (Grouped and gated forms, and output widths that are not a multiple of
-    // 128.)  All eight waves.  Wave w owns columns 64w .. 64w+63 of every 512-column
+    // (Grouped form, and output widths that are not a multiple of 128.)  All
+    // eight waves.  Wave w owns columns 64w .. 64w+63 of every 512-column
     // pass and streams its own W2 columns straight into registers -- no LDS
     // staging and no barriers.  Lane (i, g) loads, for each k-row 8g..8g+7 of
     // a stage, the four columns 4i..4i+3 (8 bytes: the 16 lanes of a k-group
