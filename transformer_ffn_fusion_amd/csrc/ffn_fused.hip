@@ -96,13 +96,14 @@ struct FusedCfg {
     static constexpr int kLoOff = kKS * kSub;
     static constexpr int kHEnd = kHOff + (kHLo ? 2 : 1) * kKS * kSub;
     static constexpr int kLds = PA::kLds1 > kHEnd ? PA::kLds1 : kHEnd;
-    // second product (dense and gated forms): per-wave staging of packed
+    // second product (P a multiple of 128): per-wave staging of packed
     // partials (8 rows x 384 bytes per wave), below H when H leaves room
     // there, else above it
     static constexpr int kStgBytes = 8 * 8 * 384;
     static constexpr int kStgOff = kHOff >= kStgBytes ? 0 : kHEnd;
-    static_assert(kHLo || (kStgOff == 0 ? kStgBytes <= kHOff : kStgOff + kStgBytes <= kLds),
-                  "the staging area fits the LDS beside H");
+    static constexpr int kLdsAll = kStgOff + kStgBytes > kLds ? kStgOff + kStgBytes : kLds;
+    static_assert(kStgOff == 0 ? kStgBytes <= kHOff : true, "the staging area fits below H");
+    static_assert(kLdsAll <= 160 * 1024, "LDS budget with the staging area");
     static_assert(kHidA % kBK == 0 && kHidB % kBK == 0, "passes cover whole H slabs");
     static_assert(!kGated || (PA::kNB1 % 2 == 0 && (!kTwoPass || PB::kNB1 % 2 == 0)),
                   "gate and up halves are whole 64-column blocks");
@@ -380,7 +381,10 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     const int li = lane & 15;   // fragment index
     const int lg = lane >> 4;   // fragment k-group
 
-    const int64_t np = (a.P + kBN2 - 1) / kBN2;   // 512-column passes of GEMM2
+    // GEMM2 passes: 1024 output columns where P is a multiple of 128 (the
+    // 16-byte form of the second product), else 512
+    const int64_t pass_cols = a.P % 128 == 0 ? 1024 : kBN2;
+    const int64_t np = (a.P + pass_cols - 1) / pass_cols;
     int64_t rb;
     int s;
     int64_t pass0 = 0, npl = np;   // GEMM2 passes of this workgroup: pass0 .. pass0 + npl - 1
@@ -504,8 +508,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     // or 1 passes 172-176 us against 155 for the full rotation).
     const int64_t jx = blockIdx.x >> 3;
     c.rot1 = jx % c.nk;
+    const int64_t pass_window = kPassWindow * kBN2 / pass_cols;   // 2048 columns
     const int64_t rot_span =
-        (int64_t)Cfg::kHid * P * 2 <= kL2Bytes ? npl : (npl < kPassWindow ? npl : kPassWindow);
+        (int64_t)Cfg::kHid * P * 2 <= kL2Bytes ? npl : (npl < pass_window ? npl : pass_window);
     const int64_t rotp = kGrouped ? 0 : jx % rot_span;
     const int rotk = (int)(jx % Cfg::kKS);
     char* const hreg = smem + Cfg::kHOff;
@@ -546,8 +551,8 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     char* const part_tile = a.part + ((int64_t)s * a.rows_out + row0) * P * kPartBytes;
     const __amdgpu_buffer_rsrc_t rpart = make_rsrc(part_tile, (int64_t)valid * P * kPartBytes);
 
-    if constexpr (!kGrouped) if (P % 128 == 0) {
-        // ============ GEMM2, dense and gated forms: Y_part = H W2_chunk ============
+    if (P % 128 == 0) {
+        // ================== GEMM2, P a multiple of 128: Y_part = H W2_chunk ==================
         // All eight waves, for output widths that are a multiple of 128.
         // Wave m owns columns 128m .. 128m+127 of every 1024-column pass and
         // streams its W2 columns straight into registers with 16-byte loads:
@@ -566,13 +571,6 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
         // (per-workgroup timestamps).  Two stages are in flight while one is
         // multiplied.
         constexpr int64_t kPW = 1024;   // output columns per pass: eight waves of 128
-        const int64_t npw = (P + kPW - 1) / kPW;
-        const int64_t nsw = npw * Cfg::kKS;
-        // the pass rotation as for the 512-column passes below: every pass
-        // while the chunk's W2 block fits the L2, else a window of 2048 columns
-        const int64_t rspan = (int64_t)Cfg::kHid * P * 2 <= kL2Bytes
-                                  ? npw : (npw < kPassWindow / 2 ? npw : kPassWindow / 2);
-        const int64_t rotw = jx % rspan;
         const int wm = wave;
         const __amdgpu_buffer_rsrc_t rw2 = make_rsrc(W2 + o0 * P, oc * P * 2);
         const uint32_t w2l =
@@ -580,9 +578,9 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
         auto load16 = [&](int64_t step, uint4 (&R)[8]) {
             const int64_t pr = step / Cfg::kKS;
             const int kr = (int)(step - pr * Cfg::kKS);
-            const int64_t pt = pr + rotw < npw ? pr + rotw : pr + rotw - npw;
+            const int64_t pt = pass0 + (pr + rotp < npl ? pr + rotp : pr + rotp - npl);
             const int ks = kr + rotk < Cfg::kKS ? kr + rotk : kr + rotk - Cfg::kKS;
-            const uint32_t base = step < nsw
+            const uint32_t base = step < nsteps
                 ? (uint32_t)(((int64_t)hrow(ks) * P + pt * kPW) * 2) + w2l : kOOB;
 #pragma unroll
             for (int e = 0; e < 8; ++e) R[e] = bload16(rw2, base + (uint32_t)(e * P * 2));
@@ -595,22 +593,34 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
         // one stage: each operand column is transposed out of R just before its
         // MFMAs (four v_perm), so only one operand is live besides R; R is
         // refilled with stage st + 2 once the stage's MFMAs are issued
+        // (compensated H: one register stage, refilled with stage st + 1 -- the
+        // doubled MFMA work of a stage covers the load, and the hi and lo H
+        // fragments leave no room for a second stage)
+        constexpr int kAhead = kHLo ? 1 : 2;
         auto mma = [&](int64_t st, uint4 (&R)[8]) {
             const int64_t pr = st / Cfg::kKS;
             const int kr = (int)(st - pr * Cfg::kKS);
             const int ks = kr + rotk < Cfg::kKS ? kr + rotk : kr + rotk - Cfg::kKS;
             const char* hs = hreg + ks * kSub;
-            uint4 bh[4];
+            uint4 bh[4], bl[4];
 #pragma unroll
             for (int fm = 0; fm < 4; ++fm) bh[fm] = ld16(hs + frag_off(16 * fm + li, lg));
+            if constexpr (kHLo) {
+#pragma unroll
+                for (int fm = 0; fm < 4; ++fm) bl[fm] = ld16(hs + Cfg::kLoOff + frag_off(16 * fm + li, lg));
+            }
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const uint4 wq = transpose8x8_col(R, q);
 #pragma unroll
                 for (int fm = 0; fm < 4; ++fm) acc[q][fm] = mfma16x16x32(bh[fm], wq, acc[q][fm]);
+                if constexpr (kHLo) {
+#pragma unroll
+                    for (int fm = 0; fm < 4; ++fm) acc[q][fm] = mfma16x16x32(bl[fm], wq, acc[q][fm]);
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
-            load16(st + 2, R);
+            load16(st + kAhead, R);
             __builtin_amdgcn_sched_barrier(0);
         };
         uint4 RA[8], RB[8];
@@ -620,11 +630,12 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
         // every iteration wait for both
         load16(0, RA);
         __builtin_amdgcn_sched_barrier(0);
-        load16(1, RB);   // the stage count is even
+        if constexpr (!kHLo) load16(1, RB);   // the stage count is even
         __builtin_amdgcn_sched_barrier(0);
-        for (int64_t st = 0; st < nsw; st += 2) {
+        for (int64_t st = 0; st < nsteps; st += 2) {
             mma(st, RA);
-            mma(st + 1, RB);
+            if constexpr (kHLo) mma(st + 1, RA);
+            else mma(st + 1, RB);
             if ((st + 2) % Cfg::kKS != 0) continue;
             const int64_t pr = st / Cfg::kKS;
             // pass pr complete: lane (i, g) holds rows 16 fm + 4 g + r, columns
@@ -632,7 +643,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
             // partials per row go through the wave's LDS staging area (8 rows at
             // a time), which is read back in 16-byte pieces that follow the rows
             // of the partial plane, so every store writes whole, adjacent pieces.
-            const int64_t pt = pr + rotw < npw ? pr + rotw : pr + rotw - npw;
+            const int64_t pt = pass0 + (pr + rotp < npl ? pr + rotp : pr + rotp - npl);
             const int64_t c0w = pt * kPW + 128 * wm;   // P % 128 == 0: all 128 in or all out
             // the row stride passes through an empty asm statement so that the
             // row offsets are formed here, not held across the loop
@@ -679,8 +690,7 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     }
 
     // ======================= GEMM2: Y_part = H W2_chunk =====================
-    // (Grouped form, and output widths that are not a multiple of 128.)  All
-    // eight waves.  Wave w owns columns 64w .. 64w+63 of every 512-column
+    // (Output widths that are not a multiple of 128.)  All eight waves.  Wave w owns columns 64w .. 64w+63 of every 512-column
     // pass and streams its own W2 columns straight into registers -- no LDS
     // staging and no barriers.  Lane (i, g) loads, for each k-row 8g..8g+7 of
     // a stage, the four columns 4i..4i+3 (8 bytes: the 16 lanes of a k-group
@@ -862,7 +872,7 @@ hipError_t launch_fused_impl(const FusedArgs& a, int64_t units, hipStream_t stre
     using Cfg = FusedCfg<CA, CB, kGated, kHLo>;
     auto kern = fused_ffn_bf16_kernel<CA, CB, G, kGated, kHLo>;
     static std::atomic<bool> lds_set[kMaxDevices] = {};
-    hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), Cfg::kLds, lds_set);
+    hipError_t e = set_dynamic_lds(reinterpret_cast<const void*>(kern), Cfg::kLdsAll, lds_set);
     if (e != hipSuccess) return e;
     // grouped form: workgroups for the pieces of a short last round (at most
     // cus, plus up to 7 x 8 for the XCD-aligned numbering of the pieces)
@@ -870,7 +880,7 @@ hipError_t launch_fused_impl(const FusedArgs& a, int64_t units, hipStream_t stre
     const int64_t plane_bytes = a.rows_out * a.P * kPartBytes;
     FusedArgs b = a;
     b.part_wt = (int64_t)a.splits * plane_bytes <= kMallBytes;
-    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), Cfg::kLds, stream, b);
+    hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), Cfg::kLdsAll, stream, b);
     return hipGetLastError();
 }
 
