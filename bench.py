@@ -24,8 +24,10 @@ dense workloads then run K more plain steps on one input set (region 3, no
 rotation): `warm_ms_per_step`, a warm-cache figure reported beside the
 headline, never as it; then, once the process has made SETTLE_CALLS calls
 (untimed ones make up the difference), K more rotated steps (region 4):
-`settled`, the rate after the GPU's start-up ramp (the first ~140 calls of a
-process run up to ~40 % slower), also beside the headline, never as it.
+`settled`, the rate after the GPU's start-up ramp (from an idle GPU the first
+~140 calls of a process run up to ~40 % slower; after the box-ceiling kernels'
+~120 ms of load, calls 6-25 still run ~7 % slower than settled), also beside
+the headline, never as it.
 
 One JSON line goes to stdout:
   value      whole-path throughput of the headline workload (TFLOP/s at M=4096);
@@ -34,7 +36,10 @@ One JSON line goes to stdout:
              stream around each kernel, against MI355X's published peak;
   cpu_baseline  the fp64 CPU oracle timed on a bounded sample of the same workload;
   box_ceilings  this GPU's own bf16 MFMA and HBM-read ceilings, measured in the same
-             run (roofline also carries the fraction of the measured ceiling);
+             run right before the headline workload's warm-up steps, after ~120 ms
+             of back-to-back launches of both kernels, which also take the GPU out
+             of its idle power state (roofline carries the fraction of the
+             measured ceiling);
   secondary  the decode shape (M=16: us/call, HBM GB/s) and, with --all, the others.
 """
 from __future__ import annotations
@@ -155,7 +160,7 @@ def to_dev(a, torch):
 
 # ---------------------------------------------------------------- dense
 
-def run_dense(cfg, steps, warmup, hip, torch, ffn, synth, workload):
+def run_dense(cfg, steps, warmup, hip, torch, ffn, synth, workload, prelude=None):
     """Dense FFN workloads, and the SwiGLU ones (cfg a workload.Gated: its inputs
     are X, Wg, Wu, Wd and it has no biases)."""
     dt = cfg.dtype
@@ -206,6 +211,8 @@ def run_dense(cfg, steps, warmup, hip, torch, ffn, synth, workload):
         if rc != 0:
             raise RuntimeError(ffn.ffn_last_error())
 
+    if prelude is not None:
+        prelude()
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
@@ -276,7 +283,7 @@ def run_dense(cfg, steps, warmup, hip, torch, ffn, synth, workload):
                 inputs=(X, W1, b1, W2, b2))
 
 
-def run_moe_router(cfg, steps, warmup, hip, torch, ffn, synth, workload):
+def run_moe_router(cfg, steps, warmup, hip, torch, ffn, synth, workload, prelude=None):
     """The MoE layer with the router on the GPU (logits = X Wr + br): region 1 times
     the whole layer, region 2 the router + routing alone."""
     X, Wr, br, W1, b1, W2, b2 = synth.moe_router_inputs(cfg.M, cfg.E, cfg.N, cfg.O, cfg.P, seed=0)
@@ -306,6 +313,8 @@ def run_moe_router(cfg, steps, warmup, hip, torch, ffn, synth, workload):
         if rc != 0:
             raise RuntimeError(ffn.ffn_last_error())
 
+    if prelude is not None:
+        prelude()
     for i in range(warmup):
         layer(i)
     torch.cuda.synchronize()
@@ -327,7 +336,7 @@ def run_moe_router(cfg, steps, warmup, hip, torch, ffn, synth, workload):
                 bytes=set_bytes, rotate=R)
 
 
-def run_moe(cfg, steps, warmup, hip, torch, ffn, synth, workload):
+def run_moe(cfg, steps, warmup, hip, torch, ffn, synth, workload, prelude=None):
     # the workload's gate logits are X Wr + offsets: formed once, before any
     # timing, by the library's router (then an input of every timed call)
     X, Wr, br, W1, b1, W2, b2 = synth.moe_router_inputs(cfg.M, cfg.E, cfg.N, cfg.O, cfg.P, seed=0)
@@ -361,6 +370,8 @@ def run_moe(cfg, steps, warmup, hip, torch, ffn, synth, workload):
         if rc != 0:
             raise RuntimeError(ffn.ffn_last_error())
 
+    if prelude is not None:
+        prelude()
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
@@ -388,7 +399,7 @@ def run_moe(cfg, steps, warmup, hip, torch, ffn, synth, workload):
                 bytes=set_bytes, rotate=R)
 
 
-def run_backward(cfg, steps, warmup, hip, torch, ffn, synth, workload):
+def run_backward(cfg, steps, warmup, hip, torch, ffn, synth, workload, prelude=None):
     """The FFN backward at a dense shape (act2 none): region 1 plain calls, region 2
     the same calls with events between the six steps."""
     X, W1, b1, W2, _ = synth.dense_inputs(cfg.M, cfg.N, cfg.O, cfg.P, seed=0)
@@ -418,6 +429,8 @@ def run_backward(cfg, steps, warmup, hip, torch, ffn, synth, workload):
         if rc != 0:
             raise RuntimeError(ffn.ffn_last_error())
 
+    if prelude is not None:
+        prelude()
     for i in range(warmup):
         call(i)
     torch.cuda.synchronize()
@@ -445,27 +458,39 @@ def run_backward(cfg, steps, warmup, hip, torch, ffn, synth, workload):
 
 # ---------------------------------------------------------------- box ceilings
 
-def box_ceilings(hip, torch, ffn, reps=10):
+def box_ceilings(hip, torch, ffn, reps=10, busy_ms=120.0):
     """This GPU's own ceilings, measured in the same run: a loop of independent
     bf16 MFMAs on register operands, and a streaming read of a 1 GiB buffer
-    (four times the Infinity Cache)."""
+    (four times the Infinity Cache).
+
+    It runs right before the headline workload's warm-up steps: both kernels are
+    first launched back to back for `busy_ms`, then timed.  From idle, the GPU
+    needs some ~100 ms of continuous load to leave its low-power state (measured
+    on MI355X: prefill calls 11-60 of a fresh process took 200-222 us each from
+    idle, 181-192 us after 100 ms of these kernels, and a 1 s idle gap after
+    them undid it), so the ceilings are timed on a busy GPU and the workload
+    that follows starts from the same state whatever its warm-up count."""
     L = ffn.lib()
     sink = torch.zeros(L.ffn_ceiling_sink_bytes() // 4, dtype=torch.float32, device="cuda")
+    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
     stream = torch.cuda.current_stream().cuda_stream
-    flops = ffn.ceiling_mfma(sink, 2048)          # warm-up
     torch.cuda.synchronize()
+    t_busy = time.perf_counter()
+    while (time.perf_counter() - t_busy) * 1e3 < busy_ms:
+        for _ in range(4):
+            ffn.ceiling_mfma(sink, 2048)
+            ffn.ceiling_read(buf, sink)
+        torch.cuda.synchronize()
+    busy = (time.perf_counter() - t_busy) * 1e3
     t0, t1 = hip.event(), hip.event()
     hip.record(t0, stream)
     for _ in range(reps):
-        ffn.ceiling_mfma(sink, 2048)
+        flops = ffn.ceiling_mfma(sink, 2048)
     hip.record(t1, stream)
     mfma_ms = hip.ms(t0, t1) / reps
-    buf = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
-    nbytes = ffn.ceiling_read(buf, sink)          # warm-up
-    torch.cuda.synchronize()
     hip.record(t0, stream)
     for _ in range(reps):
-        ffn.ceiling_read(buf, sink)
+        nbytes = ffn.ceiling_read(buf, sink)
     hip.record(t1, stream)
     read_ms = hip.ms(t0, t1) / reps
     hip.destroy([t0, t1])
@@ -473,7 +498,9 @@ def box_ceilings(hip, torch, ffn, reps=10):
     return {"mfma_bf16_tflops": flops / (mfma_ms * 1e-3) / 1e12,
             "hbm_read_gbs": nbytes / (read_ms * 1e-3) / 1e9,
             "how": "loop of independent v_mfma_f32_16x16x32_bf16 (2048 workgroups x 4 waves); "
-                   "16-byte streaming read of 1 GiB; mean of %d launches each" % reps}
+                   "16-byte streaming read of 1 GiB; both launched back to back for %.0f ms, then "
+                   "the mean of %d launches each; run right before the headline workload's "
+                   "warm-up steps" % (busy, reps)}
 
 
 # ---------------------------------------------------------------- CPU baseline
@@ -541,9 +568,14 @@ def main():
     head = cfgs[args.workload]
     log(f"[bench] device {torch.cuda.get_device_name(0)}; workload {head.name}")
 
+    ceil = {}
+
+    def prelude():
+        ceil.update(box_ceilings(hip, torch, ffn))
+
     secondary = {}
     if args.workload == "backward":
-        r = run_backward(head, args.steps, args.warmup, hip, torch, ffn, synth, workload)
+        r = run_backward(head, args.steps, args.warmup, hip, torch, ffn, synth, workload, prelude)
         r["traced_ms_per_step"] = sum(r["steps_ms"].values())
         value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
         unit = "TFLOP/s"
@@ -557,7 +589,7 @@ def main():
                 "executed_TFLOP_per_s": r["flops_exec"] / (r["ms_per_step"] * 1e-3) / 1e12}
         dense = None
     elif args.workload in ("moe", "moe_shard"):
-        r = run_moe(head, args.steps, args.warmup, hip, torch, ffn, synth, workload)
+        r = run_moe(head, args.steps, args.warmup, hip, torch, ffn, synth, workload, prelude)
         value = r["flops"] / (r["ms_per_step"] * 1e-3) / 1e12
         kern_tflops = r["flops"] / (r["k1_ms"] * 1e-3) / 1e12
         roof = {"bound": "mfma", "kernel": "grouped fused FFN", "achieved": kern_tflops,
@@ -567,7 +599,7 @@ def main():
         unit = "TFLOP/s"
         dense = None
     else:
-        r = run_dense(head, args.steps, args.warmup, hip, torch, ffn, synth, workload)
+        r = run_dense(head, args.steps, args.warmup, hip, torch, ffn, synth, workload, prelude)
         dense = r
         if head.M <= 16 and head.dtype == "bf16":
             value = r["bytes"] / (r["ms_per_step"] * 1e-3) / 1e9
@@ -648,7 +680,6 @@ def main():
             "TFLOP_per_s": m["flops"] / (m["ms_per_step"] * 1e-3) / 1e12,
             "us_per_call": 1e3 * m["ms_per_step"], "router_and_routing_us": 1e3 * m["router_ms"]}
 
-    ceil = box_ceilings(hip, torch, ffn)
     if roof["unit"] == "TFLOP/s" and head.dtype == "bf16":
         roof["measured_peak"] = ceil["mfma_bf16_tflops"]
         roof["frac_of_measured_peak"] = roof["achieved"] / ceil["mfma_bf16_tflops"]
