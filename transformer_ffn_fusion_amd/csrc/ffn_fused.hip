@@ -252,6 +252,63 @@ __device__ __forceinline__ void gemm1_loads(const G1Ctx& c, int32x4_t rw1, int32
     __syncthreads();   // the multipliers are done with the ring
 }
 
+// Loader side of one pass, register-staged form: each lane loads its 16-byte
+// pieces of a stage (the same pieces, with the same offsets, as the direct
+// loads above) into registers two stages ahead, and writes them into the LDS
+// slot the direct load would fill just before the barrier that publishes the
+// stage.  The same barriers as the direct form, in the same places.
+template <class PC, bool kGated>
+__device__ __forceinline__ void gemm1_loads_reg(const G1Ctx& c, __amdgpu_buffer_rsrc_t rx,
+                                                __amdgpu_buffer_rsrc_t rw1,
+                                                __amdgpu_buffer_rsrc_t rw1u) {
+    auto load = [&](int64_t i, uint4 (&r)[PC::kD1]) {
+        const bool real = i < c.nk;
+        const int64_t kt = !real ? 0 : (i + c.rot1 < c.nk ? i + c.rot1 : i + c.rot1 - c.nk);
+        const int64_t kx = kt * kBK + 8 * c.xc;
+        r[0] = bload16(rx, real && kx < c.N ? c.xrow_off + (uint32_t)(kx * 2) : kOOB);
+#pragma unroll
+        for (int b = 0; b < PC::kNB1; ++b) {
+            const int blk = c.w4 + kMulWaves * b;
+            const int rr = blk / PC::kNB1, cb = blk % PC::kNB1;
+            const bool up = kGated && cb >= PC::kNB1 / 2;
+            const int cc = up ? cb - PC::kNB1 / 2 : cb;
+            const uint32_t base = (uint32_t)(((kt * kBK + 8 * rr) * c.O + 64 * cc) * 2);
+            r[1 + b] = bload16(up ? rw1u : rw1, real ? base + c.w1_lane : kOOB);
+        }
+    };
+    auto store = [&](int64_t i, const uint4 (&r)[PC::kD1]) {
+        char* st = c.smem + (int)(i % PC::kNS1) * PC::kStage1;
+        *reinterpret_cast<uint4*>(st + c.w4 * kFrag + 16 * c.lane) = r[0];
+#pragma unroll
+        for (int b = 0; b < PC::kNB1; ++b) {
+            const int blk = c.w4 + kMulWaves * b;
+            *reinterpret_cast<uint4*>(st + kSub + blk * kFrag + 16 * c.lane) = r[1 + b];
+        }
+    };
+    // Every load is issued, also those of the stages past the end (their
+    // offsets are out of range: they read zeros and touch no memory), so the
+    // load sequence is the same on every iteration and each register set's
+    // wait counts only the loads issued after it.  The stage written after the
+    // last one (index nk2) lands in a buffer the multipliers no longer use.
+    uint4 RA[PC::kD1], RB[PC::kD1];   // stages of even / odd index
+    load(0, RA);
+    load(1, RB);
+    store(0, RA);
+    load(2, RA);
+    __syncthreads();   // barrier -1 publishes stage 0
+    // iteration kt: stage kt + 1 is written and published by barrier kt, then
+    // the registers it used take stage kt + 3
+    for (int64_t kt = 0; kt < c.nk2; kt += 2) {
+        store(kt + 1, RB);
+        __syncthreads();
+        load(kt + 3, RB);
+        store(kt + 2, RA);
+        __syncthreads();
+        load(kt + 4, RA);
+    }
+    __syncthreads();   // the multipliers are done with the ring
+}
+
 // Multiplier side of one pass: A^T = W1_pass^T X^T into acc[fo][fm] (hidden
 // fragment w4 + 4 fo, row fragment fm).
 template <class PC>
@@ -516,13 +573,28 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
     char* const hreg = smem + Cfg::kHOff;
 
     if (loader) {
-        gemm1_loads<PA, kGated>(c, make_srd(W1 + o0, (N * O - o0) * 2),
-                                kGated ? make_srd(a.W1u + o0, (N * O - o0) * 2) : c.rx);
-        if constexpr (Cfg::kTwoPass) {
-            const int64_t ob = o0 + Cfg::kHidA;
-            gemm1_loads<PB, kGated>(c, make_srd(W1 + ob, (N * O - ob) * 2),
-                                    make_srd(a.W1u + ob, (N * O - ob) * 2));
-        }
+        // A pass whose LDS ring is only three stages deep (the second pass of
+        // the dense two-pass chunk) stages its loads through registers: direct
+        // loads into a 3-deep ring have one iteration to land, register-staged
+        // ones about two (large shard, 8192 x 8192 x 3584 x 8192: kernel 1159 ->
+        // 1062 us with every pass register-staged; 4-deep rings measured faster
+        // with direct loads: prefill shard 144 against 152 us, MoE 452 against
+        // 482 us).
+        auto pass_loads = [&](auto pc, int64_t oo) {
+            using PC = decltype(pc);
+            if constexpr (PC::kNS1 == 3) {
+                const __amdgpu_buffer_rsrc_t rx = kGrouped ? make_rsrc(a.X, a.M * N * 2)
+                    : make_rsrc(a.X + row0 * N, (int64_t)valid * N * 2);
+                const __amdgpu_buffer_rsrc_t rw1 = make_rsrc(W1 + oo, (N * O - oo) * 2);
+                gemm1_loads_reg<PC, kGated>(c, rx, rw1,
+                                            kGated ? make_rsrc(a.W1u + oo, (N * O - oo) * 2) : rw1);
+            } else {
+                gemm1_loads<PC, kGated>(c, make_srd(W1 + oo, (N * O - oo) * 2),
+                                        kGated ? make_srd(a.W1u + oo, (N * O - oo) * 2) : c.rx);
+            }
+        };
+        pass_loads(PA{}, o0);
+        if constexpr (Cfg::kTwoPass) pass_loads(PB{}, o0 + Cfg::kHidA);
     } else {
         {
             floatx4_t acc[PA::kFO][4];
