@@ -576,10 +576,11 @@ __global__ __launch_bounds__(kThreads, 1) void fused_ffn_bf16_kernel(FusedArgs a
         // A pass whose LDS ring is only three stages deep (the second pass of
         // the dense two-pass chunk) stages its loads through registers: direct
         // loads into a 3-deep ring have one iteration to land, register-staged
-        // ones about two (large shard, 8192 x 8192 x 3584 x 8192: kernel 1159 ->
-        // 1062 us with every pass register-staged; 4-deep rings measured faster
-        // with direct loads: prefill shard 144 against 152 us, MoE 452 against
-        // 482 us).
+        // ones about two (large shard, 8192 x 8192 x 3584 x 8192: kernel 1152 ->
+        // 1041-1046 us).  4-deep rings keep the direct loads, which measured
+        // faster there (prefill shard 144 against 152 us, MoE 452 against 482
+        // us, and the large shard's first pass: 1062 us with both passes
+        // register-staged).
         auto pass_loads = [&](auto pc, int64_t oo) {
             using PC = decltype(pc);
             if constexpr (PC::kNS1 == 3) {
