@@ -255,7 +255,8 @@ def run_dense(cfg, steps, warmup, hip, torch, ffn, synth, workload, prelude=None
     torch.cuda.synchronize()
     warm_ms = hip.ms(t4, t5)
     # region 4: the same K rotated steps once the GPU has left its start-up
-    # ramp (calls take ~40 % longer over the first ~140 calls of a process):
+    # ramp (from an idle GPU calls take up to ~40 % longer over the first ~140
+    # calls of a process; after the box-ceiling kernels' load, a few per cent):
     # untimed calls up to SETTLE_CALLS in all, then K timed ones ->
     # `settled_ms_per_step`, reported beside the headline, never as it
     done = warmup + 2 * steps + 10 + steps
